@@ -1,0 +1,200 @@
+"""fp64 CPU oracle of the speculative-decoding verify step.
+
+TEST INFRASTRUCTURE ONLY: the slow, obviously correct reference the HIP
+library is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and
+the benchmark's CPU-baseline leg may import it. It shares no code with the HIP
+library and imports nothing of it.
+
+The arithmetic lives in ``sv_oracle.c`` (plain C, fp64, left-to-right loops);
+this module only marshals numpy / CPU-torch arrays into it. Inputs may be
+fp32, fp64 or bf16 (bf16 passed as its raw 16-bit patterns); every value is
+widened exactly to binary64 before any arithmetic.
+
+Every function here has its pins in ``tests/test_oracle_*.py``: worked values
+printed on the pages, closed forms, brute force on tiny inputs, exact
+enumeration of the output law and statistical tests of the acceptance law.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+__all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "icdf", "mass",
+           "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
+           "FLAG_NO_MASS", "library_path", "load_library"]
+
+F32, BF16, F64 = 0, 1, 2
+FLAG_RATIO, FLAG_CDF, FLAG_ZERO_RESIDUAL, FLAG_NO_MASS = 1, 2, 4, 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+_LOCK = threading.Lock()
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "liboracle.so")
+
+
+def load_library(path: str):
+    """Load an oracle build at ``path`` and declare its entry points."""
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.or_warp_row.argtypes = [vp, ctypes.c_int, i64, f64, vp]
+    lib.or_softmax_warp.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, f64, vp]
+    lib.or_argmax_row.argtypes = [vp, ctypes.c_int, i64]
+    lib.or_argmax_row.restype = i64
+    lib.or_verify_greedy.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
+    lib.or_mass.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, i64]
+    lib.or_mass.restype = f64
+    lib.or_icdf.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, i64, f64, f64, ctypes.POINTER(ctypes.c_int32)]
+    lib.or_icdf.restype = i64
+    lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
+    lib.or_overlap.argtypes = [vp, vp, ctypes.c_int, i64]
+    lib.or_overlap.restype = f64
+    assert lib.or_abi_version() == 1
+    return lib
+
+
+def _lib():
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            if not os.path.exists(library_path()):
+                from . import build as _build
+                _build.build()
+            _LIB = load_library(library_path())
+    return _LIB
+
+
+def _array(x):
+    """(contiguous numpy array, dtype code) for a numpy array or CPU torch tensor."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach()
+            if x.device.type != "cpu":
+                raise ValueError("oracle inputs must be host tensors")
+            if x.dtype == torch.bfloat16:
+                return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16)), BF16
+            x = x.contiguous().numpy()
+    except ImportError:
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.float64:
+        return x, F64
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError(f"unsupported oracle input dtype {x.dtype}")
+
+
+def _i32(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def warp_row(z, T: float = 1.0, lib=None) -> np.ndarray:
+    """softmax(z / T) of one row, fp64."""
+    a, dt = _array(z)
+    out = np.empty(a.shape[-1], dtype=np.float64)
+    (lib or _lib()).or_warp_row(_ptr(a), dt, a.shape[-1], float(T), _ptr(out))
+    return out
+
+
+def softmax_warp(logits, lens=None, extra_rows: int = 0, T: float = 1.0, lib=None) -> np.ndarray:
+    """Warp rows r < clamp(lens[b], 0, R - extra_rows) + extra_rows of logits [B, R, V].
+
+    Rows that are not live are left as NaN in the fp64 result.
+    """
+    a, dt = _array(logits)
+    B, R, V = a.shape
+    out = np.full((B, R, V), np.nan, dtype=np.float64)
+    ln = _i32(lens)
+    (lib or _lib()).or_softmax_warp(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), float(T), _ptr(out))
+    return out
+
+
+def argmax_row(row, lib=None) -> int:
+    a, dt = _array(row)
+    return int((lib or _lib()).or_argmax_row(_ptr(a), dt, a.shape[-1]))
+
+
+def verify_greedy(target, tokens, lens=None, lib=None):
+    """Greedy verify of target [B, K+1, V] against tokens [B, K] -> (n_accepted[B], next_token[B])."""
+    a, dt = _array(target)
+    B, K1, V = a.shape
+    t = _i32(tokens).reshape(B, K1 - 1)
+    ln = _i32(lens)
+    n = np.empty(B, dtype=np.int32)
+    nx = np.empty(B, dtype=np.int32)
+    (lib or _lib()).or_verify_greedy(_ptr(a), dt, B, K1 - 1, V, _ptr(t), _ptr(ln), _ptr(n), _ptr(nx))
+    return n, nx
+
+
+def accept(p, q, tokens, uniforms, lens=None, rel_window: float = 1e-5, lib=None):
+    """Speculative-sampling verify -> (n_accepted[B], next_token[B], flags[B]).
+
+    p [B, K+1, V], q [B, K, V] (same dtype), tokens [B, K], uniforms [B, K+1]
+    (fp32 or fp64). ``flags`` marks sequences whose decisions lie within
+    ``rel_window`` (relative) of a ratio or CDF boundary.
+    """
+    pa, dt = _array(p)
+    qa, dq = _array(q)
+    if dq != dt:
+        raise TypeError("p and q must share a dtype")
+    B, K1, V = pa.shape
+    K = K1 - 1
+    if qa.shape != (B, K, V):
+        raise ValueError(f"q shape {qa.shape} != {(B, K, V)}")
+    t = _i32(tokens).reshape(B, K)
+    ua, du = _array(uniforms)
+    if du == BF16 or ua.size != B * K1:
+        raise ValueError("uniforms must be fp32/fp64 [B, K+1]")
+    ln = _i32(lens)
+    n = np.empty(B, dtype=np.int32)
+    nx = np.empty(B, dtype=np.int32)
+    fl = np.empty(B, dtype=np.int32)
+    (lib or _lib()).or_accept(_ptr(pa), _ptr(qa), dt, B, K, V, _ptr(t), _ptr(ln), _ptr(ua), du, float(rel_window), _ptr(n),
+                     _ptr(nx), _ptr(fl))
+    return n, nx, fl
+
+
+def mass(p, q=None, lib=None) -> float:
+    """sum_x max(0, p - q) (q given) or sum_x max(0, p) (q None), fp64."""
+    pa, dt = _array(p)
+    if q is None:
+        return float((lib or _lib()).or_mass(_ptr(pa), None, dt, 1, pa.shape[-1]))
+    qa, _ = _array(q)
+    return float((lib or _lib()).or_mass(_ptr(pa), _ptr(qa), dt, 0, pa.shape[-1]))
+
+
+def icdf(p, u: float, q=None, rel_window: float = 1e-5, lib=None):
+    """Draw from norm(max(0, p - q)) (q given) or norm(max(0, p)) with uniform u -> (id, flag)."""
+    pa, dt = _array(p)
+    qa = None if q is None else _array(q)[0]
+    flag = ctypes.c_int32(0)
+    x = (lib or _lib()).or_icdf(_ptr(pa), _ptr(qa), dt, 0 if q is not None else 1, pa.shape[-1], float(u), float(rel_window),
+                       ctypes.byref(flag))
+    return int(x), int(flag.value)
+
+
+def overlap(p, q, lib=None) -> float:
+    """sum_x min(p(x), q(x)): the per-position acceptance probability."""
+    pa, dt = _array(p)
+    qa, _ = _array(q)
+    return float((lib or _lib()).or_overlap(_ptr(pa), _ptr(qa), dt, pa.shape[-1]))

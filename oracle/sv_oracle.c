@@ -1,0 +1,258 @@
+/*
+ * sv_oracle.c -- plain fp64 CPU oracle of the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously correct
+ * definition the HIP library is checked against. Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it. It shares no code,
+ * header, table or constant with the HIP library, and includes nothing of it.
+ *
+ * Every floating-point step runs in double precision. Inputs given as fp32 or
+ * bf16 are widened exactly (both embed in binary64), so the only rounding is
+ * the oracle's own, in the order written here: left to right over the
+ * vocabulary. Nothing is blocked, fused or reordered.
+ *
+ * Sources (the four web pages on draft-token verification):
+ *  [CARD]   "spec-verify" kernels-hub card: sections "Method", "API",
+ *           "Correctness", "Requirements and limits".
+ *  [BLOG]   llmstudio.ru, "Как работает speculative decoding и MTP при
+ *           инференсе LLM": section 13 (greedy verification), 15 (the
+ *           min(1, p/q) rule), 16 (p > q), 17 (rejection and the residual
+ *           distribution), 22 (what verify needs of the vocabulary),
+ *           38 (temperature and the sampler pipeline), 42 (fixed-seed
+ *           reproducibility), 47-48 (one iteration; left-to-right checking).
+ *  [DSPARK] PocketLLM DSpark notes: the gate's per-position acceptance law
+ *           and the early stop at the first mismatch.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  R1  The final draw (correction or bonus) of sequence b uses uniform
+ *      column K_b; column i < K_b drives the accept test of position i.
+ *  R2  Accept iff u < rho with u in [0,1): accepts with probability min(1,rho).
+ *  R3  rho = p/q; q == 0 < p gives rho = +inf (accept); p == q == 0 gives 0.
+ *  R4  ICDF(w, u) = smallest x with C(x) = sum_{y<=x} w(y) > u * S; zero-mass
+ *      ids are never drawn. If no x qualifies (u >= 1), the last id with
+ *      positive mass; if the row has no positive mass, -1.
+ *  R5  Residual mass S == 0 after a rejection (impossible in exact arithmetic
+ *      for normalised rows): draw from max(0, p) of the same row instead.
+ *  R6  Argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare).
+ *  R7  A draft token outside [0, V) is a greedy miss and a sampled rejection.
+ *      draft_lens[b] is clamped to [0, K]; NULL lens means K for every b.
+ *  R8  Greedy reads its rows as given (logits or probabilities, no warp).
+ *  R9  The bonus and fallback draws weigh ids by max(0, p) (identical to p
+ *      for valid probability rows).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sv_oracle.h"
+
+/* ---- element access: exact widening to binary64 ---------------------- */
+
+static double elem(const void* base, int dtype, int64_t i) {
+    switch (dtype) {
+    case OR_F32:
+        return (double)((const float*)base)[i];
+    case OR_F64:
+        return ((const double*)base)[i];
+    case OR_BF16: {
+        /* a bf16 value is the upper half of the fp32 with the same bits */
+        uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    default:
+        return NAN;
+    }
+}
+
+static size_t dtype_size(int dtype) {
+    return dtype == OR_BF16 ? 2u : dtype == OR_F32 ? 4u : 8u;
+}
+
+static const void* row_ptr(const void* base, int dtype, int64_t row, int64_t V) {
+    return (const char*)base + (size_t)row * (size_t)V * dtype_size(dtype);
+}
+
+static int32_t clamp_len(const int32_t* lens, int64_t b, int64_t K) {
+    if (lens == NULL) return (int32_t)K;
+    int64_t k = lens[b];
+    if (k < 0) k = 0;
+    if (k > K) k = K;
+    return (int32_t)k;
+}
+
+/* ---- warp: p = softmax(z / T) over one row  [BLOG s.38; CARD "Method"] --- */
+
+void or_warp_row(const void* z, int dtype, int64_t V, double T, double* p) {
+    double m = -INFINITY;
+    for (int64_t x = 0; x < V; ++x) {
+        double v = elem(z, dtype, x) / T;
+        if (v > m) m = v;
+    }
+    double s = 0.0;
+    for (int64_t x = 0; x < V; ++x) {
+        double e = exp(elem(z, dtype, x) / T - m);
+        p[x] = e;
+        s += e;
+    }
+    for (int64_t x = 0; x < V; ++x) p[x] /= s;
+}
+
+/* Rows r < min(R, clamp(lens[b], 0, R - extra) + extra) of every sequence b. */
+void or_softmax_warp(const void* logits, int dtype, int64_t B, int64_t R, int64_t V,
+                     const int32_t* lens, int32_t extra_rows, double T, double* probs) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t live = (int64_t)clamp_len(lens, b, R - extra_rows) + extra_rows;
+        if (live > R) live = R;
+        for (int64_t r = 0; r < live; ++r)
+            or_warp_row(row_ptr(logits, dtype, b * R + r, V), dtype, V, T, probs + (size_t)(b * R + r) * V);
+    }
+}
+
+/* ---- argmax with lowest-index ties  [CARD "Method"; reading R6] -------- */
+
+int64_t or_argmax_row(const void* row, int dtype, int64_t V) {
+    int64_t best = 0;
+    double bv = elem(row, dtype, 0);
+    for (int64_t x = 1; x < V; ++x) {
+        double v = elem(row, dtype, x);
+        if (v > bv) { /* strict: an equal later value never displaces */
+            bv = v;
+            best = x;
+        }
+    }
+    return best;
+}
+
+/* ---- greedy verification  [CARD "Method"; BLOG s.13, s.48] -------------
+ * Accept t_i while it equals argmax(target_i); at the first miss emit that
+ * row's argmax; if all K_b match, emit argmax(target_{K_b}). Rows after the
+ * first miss are never examined. */
+void or_verify_greedy(const void* target, int dtype, int64_t B, int64_t K, int64_t V,
+                      const int32_t* tokens, const int32_t* lens, int32_t* n_accepted,
+                      int32_t* next_token) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t kb = clamp_len(lens, b, K);
+        int32_t n = 0;
+        int64_t am = or_argmax_row(row_ptr(target, dtype, b * (K + 1) + 0, V), dtype, V);
+        while (n < kb) {
+            int64_t t = tokens[b * K + n];
+            if (t < 0 || t >= V || t != am) break; /* R7: out-of-range is a miss */
+            ++n;
+            am = or_argmax_row(row_ptr(target, dtype, b * (K + 1) + n, V), dtype, V);
+        }
+        n_accepted[b] = n;
+        next_token[b] = (int32_t)am;
+    }
+}
+
+/* ---- inverse CDF  [CARD "Method"; BLOG s.17; reading R4] ---------------
+ * kind 0: w(x) = max(0, p(x) - q(x))   (residual after a rejection)
+ * kind 1: w(x) = max(0, p(x))          (bonus row, or fallback R5)     */
+
+static double weight(const void* p, const void* q, int dtype, int kind, int64_t x) {
+    double w = kind == 0 ? elem(p, dtype, x) - elem(q, dtype, x) : elem(p, dtype, x);
+    return w > 0.0 ? w : 0.0;
+}
+
+double or_mass(const void* p, const void* q, int dtype, int kind, int64_t V) {
+    double s = 0.0;
+    for (int64_t x = 0; x < V; ++x) s += weight(p, q, dtype, kind, x);
+    return s;
+}
+
+/* Returns the drawn id; *flag gets OR_FLAG_CDF when the threshold u*S lies
+ * within rel_window (relative) of the cumulative mass on either side of the
+ * drawn id, i.e. when a different rounding order could move the draw. */
+int64_t or_icdf(const void* p, const void* q, int dtype, int kind, int64_t V, double u,
+                double rel_window, int32_t* flag) {
+    double S = or_mass(p, q, dtype, kind, V);
+    if (!(S > 0.0)) {
+        *flag |= OR_FLAG_NO_MASS;
+        return -1;
+    }
+    double thr = u * S;
+    double c = 0.0;
+    int64_t last_pos = -1;
+    for (int64_t x = 0; x < V; ++x) {
+        double w = weight(p, q, dtype, kind, x);
+        if (w > 0.0) last_pos = x;
+        double c_prev = c;
+        c += w;
+        if (c > thr) {
+            if (fabs(thr - c_prev) <= rel_window * c_prev || fabs(c - thr) <= rel_window * c)
+                *flag |= OR_FLAG_CDF;
+            return x;
+        }
+    }
+    *flag |= OR_FLAG_CDF; /* u >= 1 or rounding at the top: unreachable for u < 1 */
+    return last_pos;
+}
+
+/* ---- speculative-sampling verification  [CARD "Method"; BLOG s.15-17, s.47] ---
+ * For i < K_b: accept t_i iff u[b,i] < p_i(t_i) / q_i(t_i); stop at the first
+ * rejection n. If n < K_b draw the correction from norm(max(0, p_n - q_n));
+ * else draw the bonus from p_{K_b}. Both draws use u[b, K_b] (R1). */
+void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, int64_t V,
+               const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
+               double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t kb = clamp_len(lens, b, K);
+        int32_t flag = 0;
+        int32_t n = kb;
+        for (int32_t i = 0; i < kb; ++i) {
+            int64_t t = tokens[b * K + i];
+            double ui = elem(uniforms, u_dtype, b * (K + 1) + i);
+            if (t < 0 || t >= V) { /* R7 */
+                n = i;
+                break;
+            }
+            double pt = elem(row_ptr(p, dtype, b * (K + 1) + i, V), dtype, t);
+            double qt = elem(row_ptr(q, dtype, b * K + i, V), dtype, t);
+            double rho;
+            if (qt > 0.0)
+                rho = pt / qt;
+            else
+                rho = pt > 0.0 ? INFINITY : 0.0; /* R3 */
+            if (isfinite(rho) && fabs(ui - rho) <= rel_window * rho) flag |= OR_FLAG_RATIO;
+            if (!(ui < rho)) { /* R2 */
+                n = i;
+                break;
+            }
+        }
+        double uf = elem(uniforms, u_dtype, b * (K + 1) + kb);
+        int64_t next;
+        if (n < kb) {
+            const void* pn = row_ptr(p, dtype, b * (K + 1) + n, V);
+            const void* qn = row_ptr(q, dtype, b * K + n, V);
+            if (or_mass(pn, qn, dtype, 0, V) > 0.0) {
+                next = or_icdf(pn, qn, dtype, 0, V, uf, rel_window, &flag);
+            } else { /* R5 */
+                flag |= OR_FLAG_ZERO_RESIDUAL;
+                next = or_icdf(pn, NULL, dtype, 1, V, uf, rel_window, &flag);
+            }
+        } else {
+            next = or_icdf(row_ptr(p, dtype, b * (K + 1) + kb, V), NULL, dtype, 1, V, uf, rel_window, &flag);
+        }
+        n_accepted[b] = n;
+        next_token[b] = (int32_t)next;
+        if (flags) flags[b] = flag;
+    }
+}
+
+/* ---- per-position acceptance a = sum_x min(p(x), q(x))  [CARD "Measured"] ---
+ * The probability that a token drawn from q passes the min(1, p/q) test. */
+double or_overlap(const void* p, const void* q, int dtype, int64_t V) {
+    double a = 0.0;
+    for (int64_t x = 0; x < V; ++x) {
+        double pv = elem(p, dtype, x), qv = elem(q, dtype, x);
+        a += pv < qv ? pv : qv;
+    }
+    return a;
+}
+
+int or_abi_version(void) { return 1; }

@@ -1,0 +1,190 @@
+"""The oracle's pins have power: each plausible one-place mistake, planted in a
+temporary copy of the oracle's C source and built on the CPU, must fail at
+least one of the checks below, while the committed oracle passes them all.
+
+The checks are condensed versions of the pins in test_oracle_*.py (numpy
+argmax with ties, brute-force greedy, ragged vs dense, exact law of the
+sampled verify against its closed forms, torch softmax in fp64, ICDF edges).
+"""
+import functools
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.exact_law import emitted_marginal, enumerate_law, prob_n_at_least
+
+SRC_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+def check_argmax(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        row = rng.integers(-3, 3, size=257).astype(np.float32)
+        assert oracle.argmax_row(row, lib=lib) == int(np.argmax(row))
+
+
+def check_greedy(lib):
+    import itertools
+    rng = np.random.default_rng(1)
+    V, K = 3, 3
+    target = rng.permutation(np.arange((K + 1) * V)).reshape(1, K + 1, V).astype(np.float64)
+    chain = [int(np.argmax(target[0, i])) for i in range(K + 1)]
+    drafts = np.array(list(itertools.product(range(V), repeat=K)), dtype=np.int32)
+    n, nx = oracle.verify_greedy(np.repeat(target, len(drafts), axis=0), drafts, lib=lib)
+    for d, nn, xx in zip(drafts, n, nx):
+        m = 0
+        while m < K and d[m] == chain[m]:
+            m += 1
+        assert nn == m and xx == chain[m]
+    # lens and out-of-range tokens
+    B, K, V = 12, 5, 30
+    tgt = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    ch = tgt.argmax(-1).astype(np.int32)
+    lens = rng.integers(-1, K + 2, size=B).astype(np.int32)
+    n, nx = oracle.verify_greedy(tgt, ch[:, :K], lens, lib=lib)
+    kb = np.clip(lens, 0, K)
+    assert (n == kb).all() and (nx == ch[np.arange(B), kb]).all()
+    bad = ch[:, :K].copy()
+    bad[:, 1] = V
+    n, _ = oracle.verify_greedy(tgt, bad, lib=lib)
+    assert (n == 1).all()
+
+
+def rows(rng, r, V, conc=1.0):
+    x = rng.gamma(conc, size=(r, V))
+    return x / x.sum(-1, keepdims=True)
+
+
+def check_sampled_law(lib):
+    rng = np.random.default_rng(2)
+    K, V = 2, 6
+    p = rows(rng, K + 1, V)
+    q = rows(rng, K, V, 0.5)
+
+    def run(P, Q, T, U):
+        n, nx, _ = oracle.accept(P, Q, T, U, lib=lib)
+        return n, nx
+
+    law, bad = enumerate_law(p, q, run)
+    a = np.minimum(p[:K], q).sum(-1)
+    for i in range(K + 1):
+        assert prob_n_at_least(law, i) == pytest.approx(np.prod(a[:i]), abs=1e-12)
+        np.testing.assert_allclose(emitted_marginal(law, i, V), np.prod(a[:i]) * p[i], atol=1e-12)
+    assert bad == 0
+
+
+def check_ragged(lib):
+    rng = np.random.default_rng(3)
+    B, K, V = 30, 5, 12
+    p = rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    q = rows(rng, B * K, V).reshape(B, K, V)
+    t = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    u = rng.random((B, K + 1))
+    lens = rng.integers(0, K + 1, size=B).astype(np.int32)
+    n, nx, _ = oracle.accept(p, q, t, u, lens, lib=lib)
+    for b in range(B):
+        kb = lens[b]
+        n1, nx1, _ = oracle.accept(p[b:b + 1, :kb + 1], q[b:b + 1, :kb], t[b:b + 1, :kb], u[b:b + 1, :kb + 1],
+                                   lib=lib)
+        assert n1[0] == n[b] and nx1[0] == nx[b]
+    # p(t) == 0 is rejected even at u == 0
+    pp = np.array([[[0.5, 0.5, 0.0], [0.2, 0.3, 0.5]]])
+    qq = np.array([[[0.0, 0.5, 0.5]]])
+    n, nx, _ = oracle.accept(pp, qq, np.array([[2]]), np.array([[0.0, 0.0]]), lib=lib)
+    assert n[0] == 0 and nx[0] == 0
+
+
+def check_warp(lib):
+    g = torch.Generator().manual_seed(4)
+    z = (3 * torch.randn(3, 777, generator=g)).float()
+    ref = torch.softmax(z.double() / 0.8, -1).numpy()
+    for r in range(3):
+        np.testing.assert_allclose(oracle.warp_row(z[r], 0.8, lib=lib), ref[r], atol=1e-15, rtol=1e-12)
+    lens = np.array([0, 2, 5], dtype=np.int32)
+    zz = z.reshape(3, 1, 777).repeat(1, 4, 1).numpy()
+    out = oracle.softmax_warp(zz, lens, extra_rows=1, T=0.8, lib=lib)
+    for b in range(3):
+        live = min(3, lens[b]) + 1
+        assert np.isfinite(out[b, :live]).all() and np.isnan(out[b, live:]).all()
+
+
+def check_icdf(lib):
+    w = np.array([0.0, 0.0, 2.0, 0.0, 1.0, 0.0])
+    assert oracle.icdf(w, 0.0, lib=lib)[0] == 2
+    assert oracle.icdf(w, 0.66, lib=lib)[0] == 2
+    assert oracle.icdf(w, 0.67, lib=lib)[0] == 4
+    assert oracle.icdf(np.zeros(4), 0.5, lib=lib)[0] == -1
+
+
+ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf]
+
+# (what goes wrong, exact source text, planted replacement)
+MUTANTS = [
+    ("argmax ties go to the highest index", "if (v > bv) {", "if (v >= bv) {"),
+    ("greedy reads target rows with the draft's stride",
+     "am = or_argmax_row(row_ptr(target, dtype, b * (K + 1) + n, V), dtype, V);",
+     "am = or_argmax_row(row_ptr(target, dtype, b * K + n, V), dtype, V);"),
+    ("greedy ignores the token comparison", "t != am) break;", "t == am + V) break;"),
+    ("greedy ignores draft_lens", "int32_t kb = clamp_len(lens, b, K);\n        int32_t n = 0;",
+     "int32_t kb = (int32_t)K;\n        int32_t n = 0;"),
+    ("ratio inverted", "rho = pt / qt;", "rho = qt / pt;"),
+    ("accept test not strict", "if (!(ui < rho)) { /* R2 */", "if (!(ui <= rho)) { /* R2 */"),
+    ("draft rows indexed with the target's stride", "row_ptr(q, dtype, b * K + i, V)",
+     "row_ptr(q, dtype, b * (K + 1) + i, V)"),
+    ("residual sign flipped", "elem(p, dtype, x) - elem(q, dtype, x)", "elem(q, dtype, x) - elem(p, dtype, x)"),
+    ("residual without the max(0, .)", "return w > 0.0 ? w : 0.0;", "return kind == 0 ? w : (w > 0.0 ? w : 0.0);"),
+    ("final draw reuses the rejected position's uniform", "double uf = elem(uniforms, u_dtype, b * (K + 1) + kb);",
+     "double uf = elem(uniforms, u_dtype, b * (K + 1) + n);"),
+    ("bonus drawn from row K instead of K_b",
+     "next = or_icdf(row_ptr(p, dtype, b * (K + 1) + kb, V), NULL",
+     "next = or_icdf(row_ptr(p, dtype, b * (K + 1) + K, V), NULL"),
+    ("correction drawn from p instead of the residual", "next = or_icdf(pn, qn, dtype, 0, V, uf, rel_window, &flag);",
+     "next = or_icdf(pn, qn, dtype, 1, V, uf, rel_window, &flag);"),
+    ("ICDF threshold not strict", "if (c > thr) {", "if (c >= thr) {"),
+    ("warp ignores the temperature", "double e = exp(elem(z, dtype, x) / T - m);", "double e = exp(elem(z, dtype, x) - m);"),
+    ("warp not normalised", "for (int64_t x = 0; x < V; ++x) p[x] /= s;", "(void)s;"),
+    ("ragged warp writes one row too few", "if (live > R) live = R;", "if (live > R) live = R;\n        live -= 1;"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _source():
+    with open(os.path.join(SRC_DIR, "sv_oracle.c")) as f:
+        return f.read()
+
+
+def build_variant(tmp_path, text):
+    d = tmp_path
+    shutil.copy(os.path.join(SRC_DIR, "sv_oracle.h"), d / "sv_oracle.h")
+    (d / "sv_oracle.c").write_text(text)
+    out = d / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(out), str(d / "sv_oracle.c"),
+                    "-lm"], check=True, capture_output=True)
+    return oracle.load_library(str(out))
+
+
+def run_checks(lib):
+    failed = []
+    for chk in ALL_CHECKS:
+        try:
+            chk(lib)
+        except AssertionError:
+            failed.append(chk.__name__)
+    return failed
+
+
+def test_committed_oracle_passes_every_check():
+    assert run_checks(None) == []
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, what, old, new):
+    src = _source()
+    assert src.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+    lib = build_variant(tmp_path, src.replace(old, new))
+    assert run_checks(lib), f"no check caught: {what}"
