@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one verify round over the whole batch, through every kernel of the
+hot path, on inputs already resident in HBM:
+  sv_softmax_warp(target logits) + sv_softmax_warp(draft logits)
+  + sv_accept(p, q, tokens, uniforms) + sv_verify_greedy(target logits).
+Default workload: B = 512 sequences, K = 16 draft tokens, V = 256000, bf16
+logits (target ~ N(0, 5^2) with a Zipf(1.1) rank bias, draft = target +
+N(0, 1)), seeded synthetic data.
+
+Prints ONE JSON line. ``value`` is verify rounds/s; ``roofline`` reports the
+dominant kernel (the warp) against MI355X's 8 TB/s HBM peak on algorithmic
+bytes, timed with HIP events on the stream the kernels run on;
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload on the host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="logits-bf16-b512-k16-v256000-zipf")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                      "warp_traffic.json"),
+                    help="measured HBM bytes per warp launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(sequences shard across GPUs with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_token_verification_amd as sv
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    batch = synth.generate(args.workload, dev)
+    B, K, V = batch.B, batch.K, batch.V
+    T = batch.temperature
+    elem = 2 if batch.dtype == "bf16" else 4
+    lens = batch.lens
+
+    if batch.kind == "logits":
+        p = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
+        q = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    n_gr = torch.empty(B, dtype=torch.int32, device=dev)
+    nx_gr = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        if batch.kind == "logits":
+            sv.sv_softmax_warp(batch.target, T, lens, 1, out=p)
+            if ev:
+                ev[1].record(stream)
+            sv.sv_softmax_warp(batch.draft, T, lens, 0, out=q)
+            pp, qq = p, q
+        else:
+            if ev:
+                ev[1].record(stream)
+            pp, qq = batch.target, batch.draft
+        if ev:
+            ev[2].record(stream)
+        sv.sv_accept(pp, qq, batch.tokens, batch.uniforms, lens, out=(n_acc, nxt))
+        if ev:
+            ev[3].record(stream)
+        sv.sv_verify_greedy(batch.target, batch.tokens, lens, out=(n_gr, nx_gr))
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: K back-to-back steps between two events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel timing: the same steps with events between the launches
+    per = np.zeros(4)
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(ev)
+        torch.cuda.synchronize()
+        per += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    per /= args.steps
+    warp_t_ms, warp_d_ms, accept_ms, greedy_ms = per
+
+    # algorithmic bytes of each kernel (what the method must move)
+    kb = lens.cpu().numpy() if lens is not None else np.full(B, K)
+    n_s = n_acc.cpu().numpy().astype(np.int64)
+    n_g = n_gr.cpu().numpy().astype(np.int64)
+    rows_t = int((kb + 1).sum())
+    rows_d = int(kb.sum())
+    warp_bytes_t = rows_t * V * (elem + 4)
+    warp_bytes_d = rows_d * V * (elem + 4)
+    greedy_bytes = int(((n_g + 1) * V * elem).sum()) + 4 * B * K + 8 * B
+    accept_bytes = int((8 * np.minimum(n_s + 1, kb) + np.where(n_s < kb, 2 * V * 4, V * 4)).sum()) + 4 * B * (K + 1) \
+        + 8 * B
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9 if ms > 0 else None
+
+    out = {
+        "metric": "verify rounds/s and achieved HBM GB/s (% of peak) for [B,K+1,V] verify",
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "K": K, "V": V, "input_dtype": batch.dtype,
+                   "temperature": T, "step": "warp(target)+warp(draft)+accept+greedy"},
+    }
+    if batch.kind == "logits":
+        warp_ms = warp_t_ms + warp_d_ms
+        warp_bytes = warp_bytes_t + warp_bytes_d
+        achieved = gbs(warp_bytes, warp_ms)
+        traffic = None
+        if os.path.exists(args.traffic):
+            with open(args.traffic) as f:
+                tr = json.load(f)
+            if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_source_sha():
+                traffic = tr.get("bytes_per_launch")
+        out["roofline"] = {"bound": "hbm", "kernel": "warp_kernel", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": traffic,
+                           "algorithmic_bytes_per_launch": (warp_bytes_t + warp_bytes_d) // 2,
+                           "avg_launch_ms": round(warp_ms / 2, 4)}
+    out["kernels"] = {
+        "warp_target_ms": round(warp_t_ms, 4), "warp_draft_ms": round(warp_d_ms, 4),
+        "accept_ms": round(accept_ms, 4), "greedy_ms": round(greedy_ms, 4),
+        "warp_GBps": round(gbs(warp_bytes_t + warp_bytes_d, warp_t_ms + warp_d_ms), 1) if batch.kind == "logits"
+        else None,
+        "accept_GBps_needed": round(gbs(accept_bytes, accept_ms), 1),
+        "greedy_GBps_needed": round(gbs(greedy_bytes, greedy_ms), 1),
+        "greedy_full_read_GBps_equiv": round(gbs(B * (K + 1) * V * elem, greedy_ms), 1),
+        "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def kernel_source_sha():
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "draft_token_verification_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(batch, seconds):
+    """The fp64 CPU oracle, as it stands, on a bounded sample of sequences of the
+    same workload: warp of the live target and draft rows, sampled verify on the
+    oracle's own fp64 probabilities, greedy verify on the logits. The sample is
+    repeated until about ``seconds`` of work, then scaled to rounds/s of the
+    full batch."""
+    import numpy as np
+    import oracle
+
+    B, K, V = batch.B, batch.K, batch.V
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity)))
+    # keep the sample's fp64 probability arrays under ~4 GB
+    cap = max(1, int(4e9 // ((2 * K + 1) * V * 8)))
+    n = min(B, cap, max(threads, 1) * 4)
+    sel = np.random.default_rng(0).permutation(B)[:n].tolist()
+    tgt = batch.target[sel].cpu()
+    drf = batch.draft[sel].cpu()
+    tok = batch.tokens[sel].cpu()
+    uni = batch.uniforms[sel].cpu()
+    ln = None if batch.lens is None else batch.lens[sel].cpu()
+
+    def run():
+        t0 = time.perf_counter()
+        if batch.kind == "logits":
+            p = np.nan_to_num(oracle.softmax_warp(tgt, ln, 1, batch.temperature))
+            q = np.nan_to_num(oracle.softmax_warp(drf, ln, 0, batch.temperature))
+        else:
+            p, q = tgt, drf
+        oracle.accept(p, q, tok, uni, ln)
+        oracle.verify_greedy(tgt, tok, ln)
+        return time.perf_counter() - t0
+
+    total, reps = 0.0, 0
+    while total < seconds or reps < 1:
+        total += run()
+        reps += 1
+    per_round = total / reps * B / n
+    return {"value": round(1.0 / per_round, 6), "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {B} sequences x {reps} repeats ({total:.1f} s): warp of the live rows, sampled "
+                      f"verify on the oracle's fp64 probs, greedy on the logits; scaled by B/{n}"}
+
+
+if __name__ == "__main__":
+    main()

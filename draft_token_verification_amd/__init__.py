@@ -1,0 +1,244 @@
+"""Python binding of libspecverify, the speculative-decoding verify step on
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the verify runs in the library's HIP
+kernels. Tensors are taken as device-memory handles; the call is enqueued on
+the tensor device's current torch stream. The functions carry the C ABI's
+names (``sv_softmax_warp``, ``sv_verify_greedy``, ``sv_accept``; see
+``include/specverify.h``). ``verify_greedy`` and ``accept`` add the
+single-sequence forms of the spec-verify card's API ("API" section):
+``(n_accepted, next_token)`` for one ``[K+1, V]`` target.
+
+There is no fallback: if the library is not built, importing this package
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loads the HIP runtime first, so the library binds to the same one
+
+__all__ = ["sv_softmax_warp", "sv_verify_greedy", "sv_accept", "verify_greedy", "accept", "library_path",
+           "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
+
+SV_F32, SV_BF16 = 0, 1
+SV_MAX_K = 64
+_STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libspecverify.so")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load():
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libspecverify is not built ({path} missing); run __graft_entry__.build() or "
+                          f"python draft_token_verification_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+    lib.sv_abi_version.restype = c_int
+    lib.sv_status_string.argtypes = [c_int]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_last_error.restype = ctypes.c_char_p
+    lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp]
+    lib.sv_softmax_warp.restype = c_int
+    lib.sv_verify_greedy.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.sv_verify_greedy.restype = c_int
+    lib.sv_accept.argtypes = [vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.sv_accept.restype = c_int
+    if lib.sv_abi_version() != 1:
+        raise ImportError("libspecverify ABI version mismatch")
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return int(_lib.sv_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SpecVerifyError(fn, status, _lib.sv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _int32(t: Optional[torch.Tensor], what: str, device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    _dev(t, what)
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if t.dtype == torch.int32:
+        return t
+    if t.dtype == torch.int64:
+        return t.to(torch.int32)
+    raise TypeError(f"{what} must be int32 (or int64), got {t.dtype}")
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _out(shape, device, out: Optional[torch.Tensor], dtype, what) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(out, what)
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape) or out.device != device:
+        raise ValueError(f"{what} must be {dtype} of shape {tuple(shape)} on {device}")
+    return out
+
+
+def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: Optional[torch.Tensor] = None,
+                    extra_rows: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """probs[b, r] = softmax(logits[b, r] / T) for the live rows of logits [B, R, V].
+
+    Live rows are r < clamp(draft_lens[b], 0, R - extra_rows) + extra_rows
+    (all rows if draft_lens is None). Returns fp32 [B, R, V]; rows that are not
+    live are left as they were in ``out`` (uninitialised if ``out`` is None).
+    """
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dev = logits.device
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    probs = _out((B, R, V), dev, out, torch.float32, "out")
+    with torch.cuda.device(dev):
+        st = _lib.sv_softmax_warp(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens), int(extra_rows),
+                                  float(temperature), _ptr(probs), _stream(dev))
+    _check("sv_softmax_warp", st)
+    return probs
+
+
+def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
+                     draft_lens: Optional[torch.Tensor] = None,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Greedy verify of target [B, K+1, V] (fp32/bf16 logits or probs) -> (n_accepted[B], next_token[B])."""
+    _dev(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    toks = _int32(draft_tokens, "draft_tokens", dev)
+    if K > 0 and (toks is None or tuple(toks.shape) != (B, K)):
+        raise ValueError(f"draft_tokens must be [B, K] = {(B, K)}")
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
+    nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
+    with torch.cuda.device(dev):
+        st = _lib.sv_verify_greedy(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
+                                   _ptr(n), _ptr(nx), _stream(dev))
+    _check("sv_verify_greedy", st)
+    return n, nx
+
+
+def sv_accept(target_probs: torch.Tensor, draft_probs: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+              uniforms: torch.Tensor, draft_lens: Optional[torch.Tensor] = None,
+              out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Speculative-sampling verify -> (n_accepted[B], next_token[B]).
+
+    target_probs [B, K+1, V] fp32, draft_probs [B, K, V] fp32, draft_tokens
+    [B, K], uniforms [B, K+1] fp32 in [0, 1).
+    """
+    _dev(target_probs, "target_probs")
+    if target_probs.dim() != 3 or target_probs.dtype != torch.float32:
+        raise ValueError("target_probs must be fp32 [B, K+1, V]")
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = target_probs.device
+    if K > 0:
+        _dev(draft_probs, "draft_probs")
+        if draft_probs.dtype != torch.float32 or tuple(draft_probs.shape) != (B, K, V) or draft_probs.device != dev:
+            raise ValueError(f"draft_probs must be fp32 {(B, K, V)} on {dev}")
+    toks = _int32(draft_tokens, "draft_tokens", dev)
+    if K > 0 and (toks is None or tuple(toks.shape) != (B, K)):
+        raise ValueError(f"draft_tokens must be [B, K] = {(B, K)}")
+    _dev(uniforms, "uniforms")
+    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K1) or uniforms.device != dev:
+        raise ValueError(f"uniforms must be fp32 {(B, K1)} on {dev}")
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
+    nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
+    with torch.cuda.device(dev):
+        st = _lib.sv_accept(_ptr(target_probs), _ptr(draft_probs if K > 0 else None), B, K, V, _ptr(toks), _ptr(lens),
+                            _ptr(uniforms), _ptr(n), _ptr(nx), _stream(dev))
+    _check("sv_accept", st)
+    return n, nx
+
+
+def _batched(x: torch.Tensor, dims: int) -> Tuple[torch.Tensor, bool]:
+    if x.dim() == dims - 1:
+        return x.unsqueeze(0).contiguous(), True
+    return x.contiguous(), False
+
+
+def verify_greedy(target_probs: torch.Tensor, draft_tokens: torch.Tensor):
+    """The spec-verify card's greedy op: target_probs [K+1, V], draft_tokens [K] -> (n_accepted, next_token).
+
+    Batched inputs ([B, K+1, V], [B, K]) return device tensors instead of ints.
+    """
+    t, single = _batched(target_probs, 3)
+    d, _ = _batched(draft_tokens, 2)
+    n, nx = sv_verify_greedy(t, d)
+    if single:
+        return int(n[0]), int(nx[0])
+    return n, nx
+
+
+def accept(target_probs: torch.Tensor, draft_probs: torch.Tensor, draft_tokens: torch.Tensor,
+           generator: Optional[torch.Generator] = None):
+    """The spec-verify card's sampled op: uniforms come from ``generator``.
+
+    Draws uniforms [B, K+1] with ``torch.rand`` on the inputs' device, so a
+    fixed generator gives a fixed result, then calls ``sv_accept``.
+    """
+    p, single = _batched(target_probs, 3)
+    q, _ = _batched(draft_probs, 3)
+    d, _ = _batched(draft_tokens, 2)
+    B, K1, _V = p.shape
+    u = torch.rand((B, K1), generator=generator, device=p.device, dtype=torch.float32)
+    n, nx = sv_accept(p, q, d, u)
+    if single:
+        return int(n[0]), int(nx[0])
+    return n, nx

@@ -1,0 +1,147 @@
+// api.hip -- the C ABI of libspecverify (declared in include/specverify.h):
+// argument validation, device check, kernel dispatch and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+#include "specverify.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sv_status fail(sv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sv_status ok() {
+    g_last_error[0] = '\0';
+    return SV_OK;
+}
+
+// The kernels are built for gfx950 only; refuse any other device up front.
+constexpr int kMaxDevices = 64;
+std::once_flag g_arch_once[kMaxDevices];
+bool g_arch_ok[kMaxDevices];
+
+sv_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SV_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::call_once(g_arch_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        g_arch_ok[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                         std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    });
+    if (!g_arch_ok[dev]) return fail(SV_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return SV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t dtype_bytes(int dtype) { return dtype == SV_BF16 ? 2 : 4; }
+
+sv_status check_dtype(int dtype) {
+    if (dtype != SV_F32 && dtype != SV_BF16) return fail(SV_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    return SV_OK;
+}
+
+sv_status check_sizes(const char* fn, int32_t B, int32_t K, int64_t V) {
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (K < 0 || K > SV_MAX_K) return fail(SV_ERR_INVALID_ARG, "%s: K = %d not in [0, %d]", fn, K, SV_MAX_K);
+    if (V < 1 || V > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: V = %lld not in [1, 2^31-1]", fn, (long long)V);
+    return SV_OK;
+}
+
+sv_status launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_string(int status) {
+    switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID_ARG: return "SV_ERR_INVALID_ARG: an argument is out of range, null or misaligned";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: the current device is not gfx950";
+    case SV_ERR_HIP: return "SV_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown sv_status";
+    }
+}
+
+const char* sv_last_error(void) { return g_last_error; }
+
+sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V, const int32_t* draft_lens,
+                          int32_t extra_rows, float temperature, float* probs, void* stream) {
+    const char* fn = "sv_softmax_warp";
+    sv_status st;
+    if ((st = check_dtype(dtype)) != SV_OK) return st;
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (R < 1) return fail(SV_ERR_INVALID_ARG, "%s: R = %d < 1", fn, R);
+    if (extra_rows < 0 || extra_rows > R)
+        return fail(SV_ERR_INVALID_ARG, "%s: extra_rows = %d not in [0, R]", fn, extra_rows);
+    if (V < 1 || V > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: V = %lld not in [1, 2^31-1]", fn, (long long)V);
+    if ((int64_t)B * R > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*R exceeds 2^31-1 rows", fn);
+    if (!(temperature > 0.0f) || !std::isfinite(temperature))
+        return fail(SV_ERR_INVALID_ARG, "%s: temperature %g must be finite and > 0", fn, (double)temperature);
+    if (B == 0) return ok();
+    if (!logits || !probs) return fail(SV_ERR_INVALID_ARG, "%s: null logits or probs", fn);
+    if (!aligned(logits, dtype_bytes(dtype)) || !aligned(probs, 4) || (draft_lens && !aligned(draft_lens, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_warp(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows, temperature,
+                                        probs, (hipStream_t)stream));
+}
+
+sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
+                           const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
+                           int32_t* next_token, void* stream) {
+    const char* fn = "sv_verify_greedy";
+    sv_status st;
+    if ((st = check_dtype(dtype)) != SV_OK) return st;
+    if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
+    if (B == 0) return ok();
+    if (!target || !n_accepted || !next_token || (K > 0 && !draft_tokens))
+        return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(target, dtype_bytes(dtype)) || !aligned(n_accepted, 4) || !aligned(next_token, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || (draft_lens && !aligned(draft_lens, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_greedy(target, dtype == SV_BF16, B, K, (int)V, draft_tokens, draft_lens, n_accepted,
+                                          next_token, (hipStream_t)stream));
+}
+
+sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t B, int32_t K, int64_t V,
+                    const int32_t* draft_tokens, const int32_t* draft_lens, const float* uniforms, int32_t* n_accepted,
+                    int32_t* next_token, void* stream) {
+    const char* fn = "sv_accept";
+    sv_status st;
+    if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
+    if (B == 0) return ok();
+    if (!target_probs || !uniforms || !n_accepted || !next_token || (K > 0 && (!draft_probs || !draft_tokens)))
+        return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(target_probs, 4) || (draft_probs && !aligned(draft_probs, 4)) || !aligned(uniforms, 4) ||
+        !aligned(n_accepted, 4) || !aligned(next_token, 4) || (draft_tokens && !aligned(draft_tokens, 4)) ||
+        (draft_lens && !aligned(draft_lens, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_accept(target_probs, draft_probs, B, K, (int)V, draft_tokens, draft_lens, uniforms,
+                                          n_accepted, next_token, (hipStream_t)stream));
+}
+
+}  // extern "C"

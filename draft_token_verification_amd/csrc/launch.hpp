@@ -1,0 +1,20 @@
+// launch.hpp -- host-side launchers of the libspecverify kernels. Internal:
+// the C ABI in api.hip validates arguments and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
+                         const int32_t* lens, int32_t* n_accepted, int32_t* next_token, hipStream_t stream);
+
+hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, const int32_t* tokens,
+                         const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
+                         hipStream_t stream);
+
+hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
+                       float temperature, float* probs, hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,158 @@
+/*
+ * specverify.h -- C ABI of libspecverify: the verify step of speculative
+ * decoding on AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * Over a batch of B sequences a target model scored K+1 positions and a draft
+ * model proposed K tokens. The calls below decide, per sequence, how many
+ * draft tokens are kept (n_accepted) and which token follows them
+ * (next_token). The caller keeps draft_tokens[b, :n_accepted[b]] and appends
+ * next_token[b] (spec-verify card, "Usage" and "API").
+ *
+ * Layouts (row-major, vocabulary fastest, no padding between rows):
+ *   target        [B, K+1, V]   row i scores position i; row K_b is the bonus row
+ *   draft         [B, K,   V]   row i is the draft distribution of token i
+ *   draft_tokens  [B, K]        int32
+ *   draft_lens    [B]           int32 per-sequence draft length K_b, clamped to
+ *                               [0, K]; NULL means K_b = K for every sequence
+ *   uniforms      [B, K+1]      fp32 in [0, 1); column i < K_b drives the accept
+ *                               test of position i, column K_b the final draw
+ *   n_accepted, next_token  [B] int32 outputs
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device memory owned by the caller. The library never
+ *    allocates, frees or retains them, and needs no workspace.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return. Outputs are valid once the stream reaches them.
+ *    Calls keep no state between them; concurrent calls on different streams
+ *    are safe.
+ *  - Results are bitwise deterministic run to run: every reduction has a fixed
+ *    order.
+ *  - Host-side argument checks return an error before anything is enqueued;
+ *    sv_last_error() then describes it. A launch failure returns SV_ERR_HIP.
+ *  - Data-dependent conditions are defined behaviour, not errors: a draft
+ *    token outside [0, V) is a greedy miss and a sampled rejection and is
+ *    never dereferenced; draft_lens are clamped. Rows, tokens and uniforms a
+ *    sequence does not use are never read. NaN inputs are outside the contract.
+ *  - B == 0 is a valid empty call and enqueues nothing.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+#define SV_MAX_K 64 /* draft lengths up to 64, one wavefront lane per position */
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer, bad dtype */
+    SV_ERR_UNSUPPORTED = 2, /* the current device is not gfx950 */
+    SV_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} sv_status;
+
+typedef enum {
+    SV_F32 = 0,  /* IEEE binary32 */
+    SV_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} sv_dtype;
+
+/* Version of this ABI (SV_ABI_VERSION of the build). */
+int sv_abi_version(void);
+
+/* Static description of a status code. */
+const char* sv_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* sv_last_error(void);
+
+/*
+ * sv_softmax_warp -- temperature warp: probs[r, x] = softmax(logits[r, :] / T)[x].
+ *
+ * The sampled verify works on the distributions the sampler would draw from,
+ * after the temperature step, with target and draft warped identically
+ * (llmstudio blog "Как работает speculative decoding и MTP при инференсе
+ * LLM", sections 21-22 and 38; spec-verify card, "Method" and "Requirements
+ * and limits").
+ *
+ * logits       [B, R, V] of `dtype` (SV_F32 or SV_BF16), element-aligned.
+ * draft_lens   [B] or NULL. Sequence b has live rows r < clamp(draft_lens[b],
+ *              0, R - extra_rows) + extra_rows; NULL makes all R rows live.
+ *              Use extra_rows = 1 with R = K+1 for target rows and
+ *              extra_rows = 0 with R = K for draft rows.
+ * temperature  finite, > 0.
+ * probs        [B, R, V] fp32 output, 4-byte aligned; only live rows are
+ *              written, the others are left untouched.
+ * Accuracy: |probs - exact| <= 1e-5 absolute per element (fp32 arithmetic,
+ * exp2 with a folded log2(e)/T scale, fixed-order sums).
+ * Errors: SV_ERR_INVALID_ARG for a null logits/probs, B < 0, R < 1,
+ * extra_rows not in [0, R], V < 1 or V > INT32_MAX, B*R > INT32_MAX, a bad
+ * dtype or temperature, or misaligned pointers.
+ */
+sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
+                          const int32_t* draft_lens, int32_t extra_rows, float temperature,
+                          float* probs, void* stream);
+
+/*
+ * sv_verify_greedy -- temperature-0 verification.
+ *
+ * Accept draft token t_i while it equals argmax(target row i); at the first
+ * miss emit that row's argmax and stop; if all K_b match emit
+ * argmax(target row K_b) (spec-verify card, "Method"; llmstudio blog,
+ * sections 13 and 48). Rows after a sequence's first miss are never read.
+ * The argmax takes the lowest index among equal maxima; -0.0 equals +0.0.
+ * The rows are read as given: logits or probabilities, no warp.
+ *
+ * target       [B, K+1, V] of `dtype` (SV_F32 or SV_BF16), element-aligned.
+ * draft_tokens [B, K] int32 (may be NULL when K == 0).
+ * draft_lens   [B] int32 or NULL.
+ * Result: n_accepted[b] in [0, K_b], next_token[b] in [0, V); bit-exact.
+ * Errors: SV_ERR_INVALID_ARG for null required pointers, B < 0, K < 0,
+ * K > SV_MAX_K, V < 1 or V > INT32_MAX, a bad dtype, misaligned pointers.
+ */
+sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
+                           const int32_t* draft_tokens, const int32_t* draft_lens,
+                           int32_t* n_accepted, int32_t* next_token, void* stream);
+
+/*
+ * sv_accept -- speculative-sampling verification.
+ *
+ * For i < K_b accept t_i iff u[b, i] < p_i(t_i) / q_i(t_i), i.e. with
+ * probability min(1, p/q); stop at the first rejection n. If n < K_b draw
+ * the correction from norm(max(0, p_n - q_n)); otherwise draw the bonus token
+ * from p_{K_b} (spec-verify card, "Method"; llmstudio blog, sections 15-17
+ * and 47). Both draws are inverse-CDF lookups with uniform u[b, K_b]: the
+ * smallest x whose cumulative weight exceeds u * (total weight).
+ *   - q_i(t_i) == 0 < p_i(t_i) accepts; p_i(t_i) == 0 rejects (even at u = 0).
+ *   - The accept test is exact: it compares u * q < p in binary64.
+ *   - Draw weights are summed in binary64, so rows need not be normalised
+ *     (spec-verify card, "Correctness"); the accept ratio uses p and q as
+ *     given, so distribution preservation assumes normalised rows warped
+ *     identically (card, "Requirements and limits").
+ *   - A residual with no positive mass (p_n == q_n) draws from max(0, p_n).
+ *   - A final-draw row with no positive mass gives next_token = -1.
+ * Only the gathered p_i(t_i), q_i(t_i) for i <= n and the one row (pair)
+ * the final draw needs are read.
+ *
+ * target_probs [B, K+1, V] fp32, draft_probs [B, K, V] fp32, 4-byte aligned.
+ * draft_tokens [B, K] int32 (may be NULL when K == 0), draft_lens [B] or NULL,
+ * uniforms [B, K+1] fp32.
+ * Result: ids and decisions agree exactly with an exact-arithmetic
+ * evaluation except where u lies within ~1e-15 (relative) of a ratio or
+ * cumulative-weight boundary.
+ * Errors: SV_ERR_INVALID_ARG for null required pointers, B < 0, K < 0,
+ * K > SV_MAX_K, V < 1 or V > INT32_MAX, misaligned pointers.
+ */
+sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t B, int32_t K,
+                    int64_t V, const int32_t* draft_tokens, const int32_t* draft_lens,
+                    const float* uniforms, int32_t* n_accepted, int32_t* next_token,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+- libspecverify.so loads and exports every function include/specverify.h
+  declares, with C linkage;
+- the constants the binding uses match the header;
+- each entry point rejects bad arguments with SV_ERR_INVALID_ARG before it
+  looks for a device (so these calls are safe on a host without one).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import draft_token_verification_amd as sv
+    return sv
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_last_error", "sv_softmax_warp",
+                                    "sv_status_string", "sv_verify_greedy"]
+
+
+def test_library_exports_every_declared_symbol(sv):
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for fn in declared_functions():
+        assert fn in exported, fn
+    lib = ctypes.CDLL(sv.library_path())
+    for fn in declared_functions():
+        assert hasattr(lib, fn)
+
+
+def test_constants_match_header(sv):
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 1
+    assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
+    assert re.search(r"SV_F32 = 0", text) and re.search(r"SV_BF16 = 1", text)
+    for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARG"), (2, "SV_ERR_UNSUPPORTED"), (3, "SV_ERR_HIP")]:
+        assert re.search(rf"{name} = {code}", text)
+        assert sv._lib.sv_status_string(code).decode().startswith(name)
+
+
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x1002)        # 2-byte aligned only
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, 0, -1, 4, 100, None, None, FAKE, FAKE, None), "B = -1"),
+    ((FAKE, 0, 2, -1, 100, FAKE, None, FAKE, FAKE, None), "K = -1"),
+    ((FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, None), "K = 65"),
+    ((FAKE, 0, 2, 4, 0, FAKE, None, FAKE, FAKE, None), "V = 0"),
+    ((FAKE, 0, 2, 4, 1 << 31, FAKE, None, FAKE, FAKE, None), "V = 2147483648"),
+    ((FAKE, 7, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "unknown dtype"),
+    ((None, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "null"),
+    ((FAKE, 0, 2, 4, 100, None, None, FAKE, FAKE, None), "null"),
+    ((FAKE, 0, 2, 4, 100, FAKE, None, None, FAKE, None), "null"),
+    ((ODD, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "misaligned"),
+])
+def test_verify_greedy_rejects_bad_arguments(sv, args, fragment):
+    st = sv._lib.sv_verify_greedy(*args)
+    assert st == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, FAKE, -3, 4, 100, FAKE, None, FAKE, FAKE, FAKE, None), "B = -3"),
+    ((FAKE, FAKE, 2, 70, 100, FAKE, None, FAKE, FAKE, FAKE, None), "K = 70"),
+    ((FAKE, None, 2, 4, 100, FAKE, None, FAKE, FAKE, FAKE, None), "null"),
+    ((FAKE, FAKE, 2, 4, 100, FAKE, None, None, FAKE, FAKE, None), "null"),
+    ((FAKE, FAKE, 2, 4, 100, ODD, None, FAKE, FAKE, FAKE, None), "misaligned"),
+])
+def test_accept_rejects_bad_arguments(sv, args, fragment):
+    st = sv._lib.sv_accept(*args)
+    assert st == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, 0, 2, 0, 100, None, 0, 1.0, FAKE, None), "R = 0"),
+    ((FAKE, 0, 2, 3, 100, None, 4, 1.0, FAKE, None), "extra_rows"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 0.0, FAKE, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, float("inf"), FAKE, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, float("nan"), FAKE, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, -1.0, FAKE, None), "temperature"),
+    ((FAKE, 3, 2, 3, 100, None, 1, 1.0, FAKE, None), "unknown dtype"),
+    ((FAKE, 0, 1 << 30, 8, 100, None, 1, 1.0, FAKE, None), "B*R"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, None, None), "null"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, ODD, None), "misaligned"),
+])
+def test_softmax_warp_rejects_bad_arguments(sv, args, fragment):
+    st = sv._lib.sv_softmax_warp(*args)
+    assert st == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op(sv):
+    # B == 0 returns before any pointer is looked at or any device is queried
+    assert sv._lib.sv_verify_greedy(None, 0, 0, 4, 100, None, None, None, None, None) == 0
+    assert sv._lib.sv_accept(None, None, 0, 4, 100, None, None, None, None, None, None) == 0
+    assert sv._lib.sv_softmax_warp(None, 1, 0, 3, 100, None, 1, 1.0, None, None) == 0
+    assert sv._lib.sv_last_error().decode() == ""
+
+
+def test_binding_validates_tensors_on_host(sv):
+    import torch
+    with pytest.raises(ValueError, match="device tensor"):
+        sv.sv_verify_greedy(torch.zeros(2, 3, 5), torch.zeros(2, 2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):
+        sv.sv_softmax_warp(torch.zeros(2, 3, 5), 1.0)
