@@ -22,6 +22,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 31  # read and written once by the calibration copy
 
 
 def parse():
@@ -32,6 +33,11 @@ def parse():
     ap.add_argument("--workload", default="logits-bf16-b512-k16-v256000-zipf")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a plain fp32 device copy of COPY_BYTES (counter calibration under rocprofv3)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --copy-calibrate run "
+                         "into the traffic file, then exit")
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                       "warp_traffic.json"),
                     help="measured HBM bytes per warp launch (from rocprofv3 counters), if present")
@@ -40,6 +46,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload, args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(sequences shard across GPUs with no exchange, see the design notes)", file=sys.stderr)
@@ -172,9 +181,61 @@ def main():
         "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
     }
 
+    if args.copy_calibrate:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = COPY_BYTES
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
+    """HBM bytes per warp launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by what it reads for the calibration copy of
+    COPY_BYTES (read once, written once) in the same run: on gfx950
+    FETCH_SIZE reports about half the bytes a copy reads, WRITE_SIZE all of
+    them. The warp's two launches per step (target rows, draft rows) are
+    averaged, like the roofline's ``achieved``.
+    """
+    import csv
+
+    def load(path, counter):
+        warp, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if "warp_kernel" in r["Kernel_Name"]:
+                warp.append((int(r["Grid_Size"]), v))
+            elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
+                copy.append(v)
+        big = [v for v in copy if v > 0.25 * COPY_BYTES]  # the calibration copies, not small transfers
+        if not warp or not big:
+            raise SystemExit(f"{path}: no warp_kernel or calibration-copy dispatches with {counter}")
+        factor = COPY_BYTES / (sum(big) / len(big))
+        by_grid = {}
+        for g, v in warp:
+            by_grid.setdefault(g, []).append(v)
+        per_launch = sum(sum(v) / len(v) for v in by_grid.values()) / len(by_grid)
+        return factor, per_launch * factor, {g: sum(v) / len(v) * factor for g, v in by_grid.items()}
+
+    ff, fetch, fetch_by = load(fetch_csv, "FETCH_SIZE")
+    wf, write, write_by = load(write_csv, "WRITE_SIZE")
+    rec = {"workload": workload, "kernel": "warp_kernel", "kernel_source_sha": kernel_source_sha(),
+           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
+           "bytes_per_launch": int(fetch + write),
+           "per_grid": {str(g): {"fetch": int(fetch_by[g]), "write": int(write_by.get(g, 0))} for g in fetch_by},
+           "source": [os.path.basename(fetch_csv), os.path.basename(write_csv)]}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def kernel_source_sha():

@@ -8,13 +8,16 @@
 // Mapping: one workgroup (1024 lanes) per live row; rows past a sequence's
 // live count exit at once. Work in the log2 domain: y = z * (log2(e) / T),
 // p = 2^(y - M) / S with M = max y and S = sum 2^(y - M).
-//   pass 1: 16-byte non-temporal loads, per-lane online (max, sum) with a
+//   pass 1: plain (cacheable) loads, per-lane online (max, sum) with a
 //           rescale only when a lane's running max grows; (max, sum) pairs
 //           merge across the wavefront with DPP and a ds_swizzle, then across
 //           wavefronts through LDS;
-//   pass 2: the row is read again (recently touched, so mostly served by the
-//           caches in front of HBM) and 2^(y - M) * (1/S) is written as fp32
-//           with 16-byte non-temporal stores.
+//   pass 2: the row is read again -- pass 1 left it in the caches in front of
+//           HBM -- with non-temporal loads, and 2^(y - M) * (1/S) is written
+//           as fp32 with non-temporal 16-byte stores.
+// Every lane handles 4 consecutive elements per step (an 8-byte bf16 or
+// 16-byte fp32 load), so each 16-byte store instruction covers a contiguous
+// kilobyte across the wavefront: whole cache lines, no partial-line writes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,33 +26,36 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 2;
+constexpr int kUnroll = 8;
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// bf16 vectors carry 8 elements, fp32 vectors 4.
+// Four consecutive elements per lane: 8 bytes of bf16 or 16 bytes of fp32.
 template <bool BF16>
-struct Vec8;
+struct Quad;
 
 template <>
-struct Vec8<true> {
-    static constexpr int kN = 8;
-    using Raw = u32x4;
-    __device__ static void unpack(const Raw& r, float z[8]) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            z[2 * k] = bf16_lo(r[k]);
-            z[2 * k + 1] = bf16_hi(r[k]);
-        }
+struct Quad<true> {
+    using Raw = u32x2;
+    __device__ static Raw load(const Raw* p) { return *p; }
+    __device__ static Raw load_last(const Raw* p) { return __builtin_nontemporal_load(p); }
+    __device__ static void unpack(const Raw& r, float z[4]) {
+        z[0] = bf16_lo(r[0]);
+        z[1] = bf16_hi(r[0]);
+        z[2] = bf16_lo(r[1]);
+        z[3] = bf16_hi(r[1]);
     }
     __device__ static float at(const void* row, int64_t i) { return bf16_at((const uint16_t*)row, i); }
 };
 
 template <>
-struct Vec8<false> {
-    static constexpr int kN = 4;
+struct Quad<false> {
     using Raw = f32x4;
+    __device__ static Raw load(const Raw* p) { return *p; }
+    __device__ static Raw load_last(const Raw* p) { return load_nt(p); }
     __device__ static void unpack(const Raw& r, float z[4]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) z[k] = r[k];
@@ -71,14 +77,20 @@ __device__ __forceinline__ void online_add(const float z[N], float scale, float&
     for (int k = 0; k < N; ++k) s += ex2(fmaf(z[k], scale, -m));
 }
 
-// Vector path: the row and output start on 16-byte boundaries and V is a
-// multiple of the vector width (checked by the launcher).
+__device__ __forceinline__ f32x4 normalised(const float z[4], float scale, float m, float inv) {
+    f32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = ex2(fmaf(z[k], scale, -m)) * inv;
+    return o;
+}
+
+// VEC: V is a multiple of 4 and rows start on load/store boundaries
+// (checked by the launcher); otherwise one element per lane per step.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void warp_kernel(const void* __restrict__ logits, int R, int V,
                                                         const int32_t* __restrict__ lens, int extra_rows,
                                                         float scale, float* __restrict__ probs) {
-    using W = Vec8<BF16>;
-    constexpr int E = W::kN;
+    using Q = Quad<BF16>;
     __shared__ float lds_m[kWaves], lds_s[kWaves];
     const int row = blockIdx.x;
     const int b = row / R, r = row - b * R;
@@ -87,32 +99,32 @@ __global__ __launch_bounds__(kThreads) void warp_kernel(const void* __restrict__
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const char* zrow = (const char*)logits + (size_t)row * (size_t)V * (BF16 ? 2 : 4);
     float* prow = probs + (size_t)row * (size_t)V;
+    const typename Q::Raw* vz = (const typename Q::Raw*)zrow;
+    const int nq = V / 4;
 
     // pass 1: online max / sum
     float m = -INFINITY, s = 0.0f;
     if (VEC) {
-        const typename W::Raw* vz = (const typename W::Raw*)zrow;
-        const int nvec = V / E;
         int j = tid;
-        for (; j + (kUnroll - 1) * kThreads < nvec; j += kUnroll * kThreads) {
-            typename W::Raw raw[kUnroll];
+        for (; j + (kUnroll - 1) * kThreads < nq; j += kUnroll * kThreads) {
+            typename Q::Raw raw[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) raw[u] = load_nt(vz + j + u * kThreads);
+            for (int u = 0; u < kUnroll; ++u) raw[u] = Q::load(vz + j + u * kThreads);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                float z[E];
-                W::unpack(raw[u], z);
-                online_add<E>(z, scale, m, s);
+                float z[4];
+                Q::unpack(raw[u], z);
+                online_add<4>(z, scale, m, s);
             }
         }
-        for (; j < nvec; j += kThreads) {
-            float z[E];
-            W::unpack(load_nt(vz + j), z);
-            online_add<E>(z, scale, m, s);
+        for (; j < nq; j += kThreads) {
+            float z[4];
+            Q::unpack(Q::load(vz + j), z);
+            online_add<4>(z, scale, m, s);
         }
     } else {
         for (int x = tid; x < V; x += kThreads) {
-            float z[1] = {W::at(zrow, x)};
+            float z[1] = {Q::at(zrow, x)};
             online_add<1>(z, scale, m, s);
         }
     }
@@ -129,22 +141,26 @@ __global__ __launch_bounds__(kThreads) void warp_kernel(const void* __restrict__
 
     // pass 2: normalised probabilities
     if (VEC) {
-        const typename W::Raw* vz = (const typename W::Raw*)zrow;
         f32x4* vp = (f32x4*)prow;
-        const int nvec = V / E;
-        for (int j = tid; j < nvec; j += kThreads) {
-            float z[E];
-            W::unpack(load_nt(vz + j), z);
+        int j = tid;
+        for (; j + (kUnroll - 1) * kThreads < nq; j += kUnroll * kThreads) {
+            typename Q::Raw raw[kUnroll];
 #pragma unroll
-            for (int h = 0; h < E / 4; ++h) {
-                f32x4 o;
+            for (int u = 0; u < kUnroll; ++u) raw[u] = Q::load_last(vz + j + u * kThreads);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = ex2(fmaf(z[4 * h + k], scale, -m)) * inv;
-                store_nt(vp + (int64_t)j * (E / 4) + h, o);
+            for (int u = 0; u < kUnroll; ++u) {
+                float z[4];
+                Q::unpack(raw[u], z);
+                store_nt(vp + j + u * kThreads, normalised(z, scale, m, inv));
             }
         }
+        for (; j < nq; j += kThreads) {
+            float z[4];
+            Q::unpack(Q::load_last(vz + j), z);
+            store_nt(vp + j, normalised(z, scale, m, inv));
+        }
     } else {
-        for (int x = tid; x < V; x += kThreads) prow[x] = ex2(fmaf(W::at(zrow, x), scale, -m)) * inv;
+        for (int x = tid; x < V; x += kThreads) prow[x] = ex2(fmaf(Q::at(zrow, x), scale, -m)) * inv;
     }
 }
 
@@ -153,8 +169,7 @@ __global__ __launch_bounds__(kThreads) void warp_kernel(const void* __restrict__
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
                        float temperature, float* probs, hipStream_t stream) {
     const float scale = kLog2e / temperature;
-    const int width = bf16 ? 8 : 4;
-    const bool vec = (V % width == 0) && ((uintptr_t)logits % 16 == 0) && ((uintptr_t)probs % 16 == 0);
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % (bf16 ? 8 : 16) == 0) && ((uintptr_t)probs % 16 == 0);
     const dim3 grid((unsigned)B * (unsigned)R);
     if (bf16) {
         if (vec)
