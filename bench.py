@@ -165,7 +165,7 @@ def main():
                 tr = json.load(f)
             if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_source_sha():
                 traffic = tr.get("bytes_per_launch")
-        out["roofline"] = {"bound": "hbm", "kernel": "warp_kernel", "achieved": round(achieved, 1),
+        out["roofline"] = {"bound": "hbm", "kernel": "warp_coop_kernel", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": traffic,
                            "algorithmic_bytes_per_launch": (warp_bytes_t + warp_bytes_d) // 2,
@@ -204,6 +204,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
     averaged, like the roofline's ``achieved``.
     """
     import csv
+    import re
 
     def load(path, counter):
         warp, copy = [], []
@@ -211,13 +212,13 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
-            if "warp_kernel" in r["Kernel_Name"]:
+            if re.search(r"\bwarp_\w*kernel\b", r["Kernel_Name"]):
                 warp.append((int(r["Grid_Size"]), v))
             elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
                 copy.append(v)
         big = [v for v in copy if v > 0.25 * COPY_BYTES]  # the calibration copies, not small transfers
         if not warp or not big:
-            raise SystemExit(f"{path}: no warp_kernel or calibration-copy dispatches with {counter}")
+            raise SystemExit(f"{path}: no warp kernel or calibration-copy dispatches with {counter}")
         factor = COPY_BYTES / (sum(big) / len(big))
         by_grid = {}
         for g, v in warp:
@@ -227,7 +228,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
 
     ff, fetch, fetch_by = load(fetch_csv, "FETCH_SIZE")
     wf, write, write_by = load(write_csv, "WRITE_SIZE")
-    rec = {"workload": workload, "kernel": "warp_kernel", "kernel_source_sha": kernel_source_sha(),
+    rec = {"workload": workload, "kernel": "warp_coop_kernel", "kernel_source_sha": kernel_source_sha(),
            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
            "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
            "bytes_per_launch": int(fetch + write),

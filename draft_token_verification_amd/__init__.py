@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
-__all__ = ["sv_softmax_warp", "sv_verify_greedy", "sv_accept", "verify_greedy", "accept", "library_path",
+__all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
+           "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
 SV_F32, SV_BF16 = 0, 1
@@ -51,7 +52,11 @@ def _load():
     lib.sv_status_string.argtypes = [c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.restype = ctypes.c_char_p
-    lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp]
+    lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.sv_softmax_warp_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
+    lib.sv_set_wait_limit.argtypes = [i32]
+    lib.sv_set_wait_limit.restype = c_int
     lib.sv_softmax_warp.restype = c_int
     lib.sv_verify_greedy.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp]
     lib.sv_verify_greedy.restype = c_int
@@ -122,13 +127,42 @@ def _out(shape, device, out: Optional[torch.Tensor], dtype, what) -> torch.Tenso
     return out
 
 
+_WORKSPACES = {}
+
+
+def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
+    """A workspace of at least nbytes, kept per (device, stream) so that calls
+    on one stream reuse it and calls on different streams never share one."""
+    if nbytes == 0:
+        return None
+    key = (device.index, stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def sv_softmax_warp_workspace_bytes(B: int, R: int, V: int) -> int:
+    return int(_lib.sv_softmax_warp_workspace_bytes(B, R, V))
+
+
+def sv_set_wait_limit(polls: int, device=None) -> None:
+    """Diagnostic: polls before a warp workgroup computes its row's statistics alone (0 forces it)."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check("sv_set_wait_limit", _lib.sv_set_wait_limit(int(polls)))
+
+
 def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: Optional[torch.Tensor] = None,
-                    extra_rows: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    extra_rows: int = 0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """probs[b, r] = softmax(logits[b, r] / T) for the live rows of logits [B, R, V].
 
     Live rows are r < clamp(draft_lens[b], 0, R - extra_rows) + extra_rows
     (all rows if draft_lens is None). Returns fp32 [B, R, V]; rows that are not
     live are left as they were in ``out`` (uninitialised if ``out`` is None).
+    ``workspace`` (a uint8 device tensor) defaults to one kept per device and
+    stream, sized by sv_softmax_warp_workspace_bytes.
     """
     _dev(logits, "logits")
     if logits.dim() != 3:
@@ -140,8 +174,14 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
         raise ValueError("draft_lens must be [B]")
     probs = _out((B, R, V), dev, out, torch.float32, "out")
     with torch.cuda.device(dev):
+        stream = _stream(dev)
+        if workspace is None:
+            workspace = _workspace(sv_softmax_warp_workspace_bytes(B, R, V) if B > 0 else 0, dev, stream.value)
+        elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the logits' device")
+        ws_bytes = 0 if workspace is None else workspace.numel()
         st = _lib.sv_softmax_warp(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens), int(extra_rows),
-                                  float(temperature), _ptr(probs), _stream(dev))
+                                  float(temperature), _ptr(probs), _ptr(workspace), ws_bytes, stream)
     _check("sv_softmax_warp", st)
     return probs
 

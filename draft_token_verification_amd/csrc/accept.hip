@@ -30,32 +30,38 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
 constexpr int kSub = 4 * kWave;     // elements per sub-block: 4 per lane
 constexpr int kMaxSeg = 7936;       // segment totals kept in LDS (62 KiB)
 
-// Weights of the 4 elements x .. x+3 (zero past V). q == nullptr: w = max(0, p)
-// (bonus row); otherwise w = max(0, p - q) (residual). Inputs widen exactly.
+// The 4 elements x .. x+3 of p (and q): raw values, zero past V.
+struct Raw4 {
+    f32x4 p, q;
+};
+
 template <bool VEC>
-__device__ __forceinline__ void weights4(const float* p, const float* q, int64_t x, int V, double w[4]) {
-    float pv[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ Raw4 load4(const float* p, const float* q, int64_t x, int V) {
+    Raw4 r;
+    r.q = f32x4{0.f, 0.f, 0.f, 0.f};
     if (VEC && x < V) {
-        f32x4 a = load_nt((const f32x4*)(p + x));
-        pv[0] = a[0]; pv[1] = a[1]; pv[2] = a[2]; pv[3] = a[3];
-        if (q) {
-            f32x4 c = load_nt((const f32x4*)(q + x));
-            qv[0] = c[0]; qv[1] = c[1]; qv[2] = c[2]; qv[3] = c[3];
-        }
+        r.p = load_nt((const f32x4*)(p + x));
+        if (q) r.q = load_nt((const f32x4*)(q + x));
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            pv[j] = (x + j < V) ? p[x + j] : 0.f;
-            if (q) qv[j] = (x + j < V) ? q[x + j] : 0.f;
+            r.p[j] = (x + j < V) ? p[x + j] : 0.f;
+            if (q) r.q[j] = (x + j < V) ? q[x + j] : 0.f;
         }
     }
+    return r;
+}
+
+// Weights of those elements, in binary64 (inputs widen exactly):
+// q == nullptr: w = max(0, p) (bonus row); otherwise w = max(0, p - q) (residual).
+__device__ __forceinline__ void weights4(const Raw4& r, bool resid, double w[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        double d = q ? (double)pv[j] - (double)qv[j] : (double)pv[j];
+        double d = resid ? (double)r.p[j] - (double)r.q[j] : (double)r.p[j];
         w[j] = d > 0.0 ? d : 0.0;
     }
 }
@@ -72,14 +78,18 @@ __device__ double segment_totals(const float* p, const float* q, int V, int m, i
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
         for (int k = 0; k < m; ++k) {
-            double w[kUnroll][4];
+            Raw4 raw[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t x = (int64_t)(s0 + u * kWaves) * L + (int64_t)k * kSub + 4 * lane;
-                weights4<VEC>(p, q, x, V, w[u]);
+                raw[u] = load4<VEC>(p, q, x, V);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[u] += ((w[u][0] + w[u][1]) + w[u][2]) + w[u][3];
+            for (int u = 0; u < kUnroll; ++u) {
+                double w[4];
+                weights4(raw[u], q != nullptr, w);
+                acc[u] += ((w[0] + w[1]) + w[2]) + w[3];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -132,7 +142,7 @@ __device__ int locate(const float* p, const float* q, int V, int m, int nseg, co
     for (int k = 0; k < m; ++k) {
         const int64_t x0 = (int64_t)sstar * L + (int64_t)k * kSub + 4 * lane;
         double w[4];
-        weights4<VEC>(p, q, x0, V, w);
+        weights4(load4<VEC>(p, q, x0, V), q != nullptr, w);
         const double p1 = w[0] + w[1], p2 = p1 + w[2], p3 = p2 + w[3];
         const double incl = wave_incl_scan_d(p3, lane);
         double excl = __shfl_up(incl, 1, kWave);

@@ -86,8 +86,20 @@ const char* sv_status_string(int status) {
 
 const char* sv_last_error(void) { return g_last_error; }
 
+size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V) {
+    if (B < 1 || R < 1 || V < 1 || V > INT32_MAX || (int64_t)B * R > INT32_MAX) return 0;
+    return sv::warp_workspace_bytes(B, R, (int)V);
+}
+
+sv_status sv_set_wait_limit(int32_t polls) {
+    if (polls < 0) return fail(SV_ERR_INVALID_ARG, "sv_set_wait_limit: polls = %d < 0", polls);
+    sv::set_wait_limit(polls);
+    return ok();
+}
+
 sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V, const int32_t* draft_lens,
-                          int32_t extra_rows, float temperature, float* probs, void* stream) {
+                          int32_t extra_rows, float temperature, float* probs, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     const char* fn = "sv_softmax_warp";
     sv_status st;
     if ((st = check_dtype(dtype)) != SV_OK) return st;
@@ -105,7 +117,7 @@ sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, i
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_warp(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows, temperature,
-                                        probs, (hipStream_t)stream));
+                                        probs, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,

@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 template <bool BF16>
 struct RowReader;
@@ -129,7 +129,7 @@ __device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int 
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void greedy_kernel(const void* __restrict__ target, int K, int V,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_kernel(const void* __restrict__ target, int K, int V,
                                                           const int32_t* __restrict__ tokens,
                                                           const int32_t* __restrict__ lens,
                                                           int32_t* __restrict__ n_accepted,

@@ -15,6 +15,13 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
                          hipStream_t stream);
 
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
-                       float temperature, float* probs, hipStream_t stream);
+                       float temperature, float* probs, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+// Workspace the cooperative warp path needs (0: that path does not apply to V).
+size_t warp_workspace_bytes(int B, int R, int V);
+
+// Polls a cooperative warp workgroup makes before it recomputes its row alone
+// (applies to launches made after the call, on every device).
+void set_wait_limit(int tries);
 
 }  // namespace sv

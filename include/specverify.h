@@ -20,7 +20,8 @@
  *
  * Conventions for every entry point:
  *  - Pointers are device memory owned by the caller. The library never
- *    allocates, frees or retains them, and needs no workspace.
+ *    allocates, frees or retains them; the one scratch buffer it uses (the
+ *    warp's workspace) is passed in by the caller too.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
  *    stream) and return. Outputs are valid once the stream reaches them.
  *    Calls keep no state between them; concurrent calls on different streams
@@ -86,15 +87,34 @@ const char* sv_last_error(void);
  * temperature  finite, > 0.
  * probs        [B, R, V] fp32 output, 4-byte aligned; only live rows are
  *              written, the others are left untouched.
+ * workspace    device memory of at least sv_softmax_warp_workspace_bytes(B,
+ *              R, V) bytes, 8-byte aligned, owned by the caller, contents
+ *              irrelevant (the call initialises it on `stream`); it holds the
+ *              per-row partial statistics the workgroups of a row exchange.
+ *              NULL (or too small) selects a slower path that needs none.
+ *              Calls that overlap in time must not share a workspace.
  * Accuracy: |probs - exact| <= 1e-5 absolute per element (fp32 arithmetic,
- * exp2 with a folded log2(e)/T scale, fixed-order sums).
+ * exp2 with a folded log2(e)/T scale, fixed-order sums); results are bitwise
+ * identical run to run and independent of the workspace path's internal
+ * timing.
  * Errors: SV_ERR_INVALID_ARG for a null logits/probs, B < 0, R < 1,
  * extra_rows not in [0, R], V < 1 or V > INT32_MAX, B*R > INT32_MAX, a bad
  * dtype or temperature, or misaligned pointers.
  */
 sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
                           const int32_t* draft_lens, int32_t extra_rows, float temperature,
-                          float* probs, void* stream);
+                          float* probs, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sv_softmax_warp uses for these sizes (0 when its fast path
+ * does not apply: V not a multiple of 4, or V above about 2 million). */
+size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
+
+/* Diagnostic control, process-wide: how many times a workgroup of
+ * sv_softmax_warp's fast path polls for the partial statistics of its row
+ * before computing them all itself (default 16384), for calls made after
+ * this one. Any value gives the same results; 0 forces the
+ * self-computation. */
+sv_status sv_set_wait_limit(int32_t polls);
 
 /*
  * sv_verify_greedy -- temperature-0 verification.

@@ -30,8 +30,9 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_last_error", "sv_softmax_warp",
-                                    "sv_status_string", "sv_verify_greedy"]
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_last_error", "sv_set_wait_limit",
+                                    "sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_status_string",
+                                    "sv_verify_greedy"]
 
 
 def test_library_exports_every_declared_symbol(sv):
@@ -91,16 +92,16 @@ def test_accept_rejects_bad_arguments(sv, args, fragment):
 
 
 @pytest.mark.parametrize("args,fragment", [
-    ((FAKE, 0, 2, 0, 100, None, 0, 1.0, FAKE, None), "R = 0"),
-    ((FAKE, 0, 2, 3, 100, None, 4, 1.0, FAKE, None), "extra_rows"),
-    ((FAKE, 0, 2, 3, 100, None, 1, 0.0, FAKE, None), "temperature"),
-    ((FAKE, 0, 2, 3, 100, None, 1, float("inf"), FAKE, None), "temperature"),
-    ((FAKE, 0, 2, 3, 100, None, 1, float("nan"), FAKE, None), "temperature"),
-    ((FAKE, 0, 2, 3, 100, None, 1, -1.0, FAKE, None), "temperature"),
-    ((FAKE, 3, 2, 3, 100, None, 1, 1.0, FAKE, None), "unknown dtype"),
-    ((FAKE, 0, 1 << 30, 8, 100, None, 1, 1.0, FAKE, None), "B*R"),
-    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, None, None), "null"),
-    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, ODD, None), "misaligned"),
+    ((FAKE, 0, 2, 0, 100, None, 0, 1.0, FAKE, None, 0, None), "R = 0"),
+    ((FAKE, 0, 2, 3, 100, None, 4, 1.0, FAKE, None, 0, None), "extra_rows"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 0.0, FAKE, None, 0, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, float("inf"), FAKE, None, 0, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, float("nan"), FAKE, None, 0, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, -1.0, FAKE, None, 0, None), "temperature"),
+    ((FAKE, 3, 2, 3, 100, None, 1, 1.0, FAKE, None, 0, None), "unknown dtype"),
+    ((FAKE, 0, 1 << 30, 8, 100, None, 1, 1.0, FAKE, None, 0, None), "B*R"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, None, None, 0, None), "null"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, ODD, None, 0, None), "misaligned"),
 ])
 def test_softmax_warp_rejects_bad_arguments(sv, args, fragment):
     st = sv._lib.sv_softmax_warp(*args)
@@ -112,7 +113,7 @@ def test_empty_batch_is_a_no_op(sv):
     # B == 0 returns before any pointer is looked at or any device is queried
     assert sv._lib.sv_verify_greedy(None, 0, 0, 4, 100, None, None, None, None, None) == 0
     assert sv._lib.sv_accept(None, None, 0, 4, 100, None, None, None, None, None, None) == 0
-    assert sv._lib.sv_softmax_warp(None, 1, 0, 3, 100, None, 1, 1.0, None, None) == 0
+    assert sv._lib.sv_softmax_warp(None, 1, 0, 3, 100, None, 1, 1.0, None, None, 0, None) == 0
     assert sv._lib.sv_last_error().decode() == ""
 
 
@@ -122,3 +123,16 @@ def test_binding_validates_tensors_on_host(sv):
         sv.sv_verify_greedy(torch.zeros(2, 3, 5), torch.zeros(2, 2, dtype=torch.int32))
     with pytest.raises(ValueError, match="device tensor"):
         sv.sv_softmax_warp(torch.zeros(2, 3, 5), 1.0)
+
+
+def test_warp_workspace_size(sv):
+    # one 8-byte slot per (row, 32768-element slice); 0 where the fast path does not apply
+    assert sv.sv_softmax_warp_workspace_bytes(512, 17, 256000) == 512 * 17 * 8 * 8
+    assert sv.sv_softmax_warp_workspace_bytes(2, 3, 32000) == 2 * 3 * 1 * 8
+    assert sv.sv_softmax_warp_workspace_bytes(2, 3, 32003) == 0
+    assert sv.sv_softmax_warp_workspace_bytes(2, 3, 64 * 32768 + 4) == 0
+    assert sv.sv_softmax_warp_workspace_bytes(0, 3, 32000) == 0
+
+
+def test_wait_limit_rejects_negative(sv):
+    assert sv._lib.sv_set_wait_limit(-1) == 1

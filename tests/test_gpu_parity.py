@@ -360,3 +360,55 @@ def test_card_single_sequence_api(sv):
     g.manual_seed(11)
     r2 = sv.accept(b.target[0], b.draft[0], b.tokens[0].long(), generator=g)
     assert r1 == r2 and 0 <= r1[0] <= 4 and 0 <= r1[1] < b.V
+
+
+@pytest.mark.parametrize("case", [("logits-bf16-b512-k16-v256000-zipf", {"B": 5}),
+                                  ("logits-f32-b1024-ragged7-v152064", {"B": 24}),
+                                  ("logits-bf16-b256-k5-v128256", {"B": 9, "V": 32000})],
+                         ids=["bf16-v256000", "f32-ragged-v152064", "bf16-v32000"])
+def test_warp_cooperative_and_row_paths(sv, case):
+    """The cooperative warp (row split over workgroups that exchange partial
+    statistics) and the one-row-per-workgroup path agree with the oracle; with
+    the wait limit at 0 every cooperative workgroup recomputes its row's
+    partials itself, and the result must be bitwise the same."""
+    name, ov = case
+    batch = synth.generate(name, "cuda", poison=True, **ov)
+    T, lens = batch.temperature, batch.lens
+    B, R, V = batch.target.shape
+    assert sv.sv_softmax_warp_workspace_bytes(B, R, V) > 0
+    sentinel = -1.0
+    outs = {}
+    for mode in ("coop", "rows", "forced"):
+        out = torch.full((B, R, V), sentinel, dtype=torch.float32, device="cuda")
+        if mode == "rows":
+            ws = torch.empty(0, dtype=torch.uint8, device="cuda")
+        else:
+            ws = torch.empty(sv.sv_softmax_warp_workspace_bytes(B, R, V), dtype=torch.uint8, device="cuda")
+            ws.fill_(0x5A)  # garbage: the call must initialise it
+        if mode == "forced":
+            sv.sv_set_wait_limit(0)
+        try:
+            sv.sv_softmax_warp(batch.target, T, lens, 1, out=out, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            if mode == "forced":
+                sv.sv_set_wait_limit(1 << 14)
+        outs[mode] = out
+    assert torch.equal(outs["coop"].view(torch.int32), outs["forced"].view(torch.int32))
+    kb = host(lens).numpy() if lens is not None else np.full(B, R - 1)
+    g = np.random.default_rng(2)
+    for b in range(B):
+        live = min(R - 1, max(0, int(kb[b]))) + 1
+        for r in range(R):
+            if r >= live:
+                for mode in outs:
+                    assert (outs[mode][b, r] == sentinel).all(), (mode, b, r)
+                continue
+            if g.random() > 0.35:
+                continue
+            ref = oracle.warp_row(host(batch.target[b, r]), T)
+            for mode in ("coop", "rows"):
+                err = float(np.abs(host(outs[mode][b, r]).numpy() - ref).max())
+                assert err <= WARP_TOL, (mode, b, r, err)
+    print(f"[{name}] coop vs rows max |diff| = "
+          f"{float((outs['coop'] - outs['rows']).abs().nan_to_num(0).max()):.3g}", flush=True)
