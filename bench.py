@@ -126,6 +126,25 @@ def main():
     per /= args.steps
     warp_t_ms, warp_d_ms, accept_ms, greedy_ms = per
 
+    # the fused sampled path: the accept test and the draw straight from logits
+    fused_ms = None
+    if batch.kind == "logits":
+        n_fu = torch.empty(B, dtype=torch.int32, device=dev)
+        nx_fu = torch.empty(B, dtype=torch.int32, device=dev)
+        fused = lambda: sv.sv_accept_logits(batch.target, batch.draft, batch.tokens, batch.uniforms, T, lens,
+                                            out=(n_fu, nx_fu))
+        for _ in range(args.warmup):
+            fused()
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for _ in range(args.steps):
+            fused()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = f0.elapsed_time(f1) / args.steps
+
     # algorithmic bytes of each kernel (what the method must move)
     kb = lens.cpu().numpy() if lens is not None else np.full(B, K)
     n_s = n_acc.cpu().numpy().astype(np.int64)
@@ -138,6 +157,10 @@ def main():
     accept_bytes = int((8 * np.minimum(n_s + 1, kb) + np.where(n_s < kb, 2 * V * 4, V * 4)).sum()) + 4 * B * (K + 1) \
         + 8 * B
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9 if ms > 0 else None
+    if fused_ms is not None:
+        n_f = n_fu.cpu().numpy().astype(np.int64)
+        # target rows 0..n and draft rows 0..min(n, kb-1), each read once
+        fused_bytes = int(((n_f + 1 + np.minimum(n_f + 1, kb)) * V * elem).sum()) + 4 * B * (2 * K + 1) + 8 * B
 
     out = {
         "metric": "verify rounds/s and achieved HBM GB/s (% of peak) for [B,K+1,V] verify",
@@ -180,6 +203,13 @@ def main():
         "greedy_full_read_GBps_equiv": round(gbs(B * (K + 1) * V * elem, greedy_ms), 1),
         "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
     }
+    if fused_ms is not None:
+        out["kernels"].update({
+            "accept_logits_ms": round(fused_ms, 4),
+            "accept_logits_GBps_needed": round(gbs(fused_bytes, fused_ms), 1),
+            "mean_n_accept_logits": round(float(n_f.mean()), 4),
+            "fused_sampled_rounds_per_s": round(1000.0 / (fused_ms + greedy_ms), 3),
+        })
 
     if args.copy_calibrate:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -240,10 +270,11 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
 
 
 def kernel_source_sha():
+    """Hash of the warp kernel's sources: measured traffic is void once they change."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "draft_token_verification_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in ("common.hpp", "warp.hip"):
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

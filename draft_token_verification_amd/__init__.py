@@ -21,6 +21,7 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
+           "sv_accept_logits",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
@@ -62,6 +63,8 @@ def _load():
     lib.sv_verify_greedy.restype = c_int
     lib.sv_accept.argtypes = [vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.sv_accept.restype = c_int
+    lib.sv_accept_logits.argtypes = [vp, vp, c_int, i32, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp]
+    lib.sv_accept_logits.restype = c_int
     if lib.sv_abi_version() != 1:
         raise ImportError("libspecverify ABI version mismatch")
     return lib
@@ -244,6 +247,46 @@ def sv_accept(target_probs: torch.Tensor, draft_probs: Optional[torch.Tensor], d
         st = _lib.sv_accept(_ptr(target_probs), _ptr(draft_probs if K > 0 else None), B, K, V, _ptr(toks), _ptr(lens),
                             _ptr(uniforms), _ptr(n), _ptr(nx), _stream(dev))
     _check("sv_accept", st)
+    return n, nx
+
+
+def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                     draft_tokens: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: float = 1.0,
+                     draft_lens: Optional[torch.Tensor] = None,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Speculative-sampling verify from logits (fp32 or bf16) -> (n_accepted[B], next_token[B]).
+
+    target_logits [B, K+1, V], draft_logits [B, K, V] (same dtype), draft_tokens [B, K],
+    uniforms [B, K+1] fp32; the rows are warped with temperature T on the fly.
+    """
+    _dev(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, K+1, V]")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits, "target_logits")
+    if K > 0:
+        _dev(draft_logits, "draft_logits")
+        if draft_logits.dtype != target_logits.dtype or tuple(draft_logits.shape) != (B, K, V) \
+                or draft_logits.device != dev:
+            raise ValueError(f"draft_logits must be {target_logits.dtype} {(B, K, V)} on {dev}")
+    toks = _int32(draft_tokens, "draft_tokens", dev)
+    if K > 0 and (toks is None or tuple(toks.shape) != (B, K)):
+        raise ValueError(f"draft_tokens must be [B, K] = {(B, K)}")
+    _dev(uniforms, "uniforms")
+    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K1) or uniforms.device != dev:
+        raise ValueError(f"uniforms must be fp32 {(B, K1)} on {dev}")
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
+    nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
+    with torch.cuda.device(dev):
+        st = _lib.sv_accept_logits(_ptr(target_logits), _ptr(draft_logits if K > 0 else None), code, B, K, V,
+                                   float(temperature), _ptr(toks), _ptr(lens), _ptr(uniforms), _ptr(n), _ptr(nx),
+                                   _stream(dev))
+    _check("sv_accept_logits", st)
     return n, nx
 
 

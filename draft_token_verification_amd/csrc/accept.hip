@@ -8,20 +8,30 @@
 // the inverse CDF at u[b, K_b]: the smallest x whose cumulative weight
 // exceeds u * S, S the total weight.
 //
-// Mapping: one workgroup (1024 lanes) per sequence.
+// Two kernels, one workgroup (1024 lanes) per sequence, sharing the draw:
+//
+// accept_kernel -- p and q given as fp32 probability rows.
 //  1. Gather and decide (wavefront 0): lane i < K_b loads t_i, p_i(t_i),
 //     q_i(t_i), u[b,i] and tests u*q < p in binary64 -- exact, since the
 //     product of two binary32 values fits in binary64 -- so the ratio is never
 //     rounded. A ballot over the lanes gives the first rejection n.
-//  2. Segment sums (all 16 wavefronts): the one row pair the draw needs is
-//     streamed once with 16-byte non-temporal loads; weights are formed and
-//     summed in binary64 per 256*m-element segment (fixed DPP butterfly), and
-//     the segment totals go to LDS.
+//
+// accept_logits_kernel -- p and q given as logits, warped on the fly: no
+// probability row is ever written (the sampled verify needs the target
+// distribution only at the positions it examines; blog, section 22).
+//  1. For i = 0, 1, ... in order, one pass over target row i and draft row i
+//     gives each row's log2-domain (max, sum) (online, per lane, merged with
+//     DPP and LDS); p_i(t_i) and q_i(t_i) follow from the two logits at t_i,
+//     and the test u*q < p runs in binary64. The loop stops at the first
+//     rejection, so rows after it are never read.
+//
+// The draw (both kernels):
+//  2. Segment sums (all 16 wavefronts): the one row (pair) the draw needs is
+//     streamed once; weights are formed and summed in binary64 per
+//     256*m-element segment (fixed DPP butterfly) into an LDS table.
 //  3. Locate (wavefront 0): a carry-chained wave scan over the segment totals
 //     finds the segment holding u*S; that single segment is re-read and
 //     scanned in x order to find the id.
-// Only the draw's row (pair) is read in full; gathers touch one value per
-// tested position.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,43 +44,147 @@ constexpr int kUnroll = 2;
 constexpr int kSub = 4 * kWave;     // elements per sub-block: 4 per lane
 constexpr int kMaxSeg = 7936;       // segment totals kept in LDS (62 KiB)
 
-// The 4 elements x .. x+3 of p (and q): raw values, zero past V.
-struct Raw4 {
-    f32x4 p, q;
-};
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- weight sources: 4 consecutive elements x .. x+3 per lane ------------
+// load() issues the loads (zero / -inf past V, selected rather than branched
+// on, so several loads stay in flight); weights() turns them into binary64
+// draw weights.
+
+// fp32 probability rows: w = max(0, p - q) (residual) or max(0, p) (q null).
 template <bool VEC>
-__device__ __forceinline__ Raw4 load4(const float* p, const float* q, int64_t x, int V) {
-    Raw4 r;
-    r.q = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (VEC && x < V) {
-        r.p = load_nt((const f32x4*)(p + x));
-        if (q) r.q = load_nt((const f32x4*)(q + x));
-    } else {
+struct ProbSource {
+    const float* p;
+    const float* q;
+    int V;
+    struct Raw {
+        f32x4 p, q;
+    };
+    __device__ Raw load(int64_t x) const {
+        Raw r;
+        r.q = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (VEC) {
+            const bool in = x < V;
+            r.p = in ? load_nt((const f32x4*)(p + x)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (q) r.q = in ? load_nt((const f32x4*)(q + x)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                r.p[j] = (x + j < V) ? p[x + j] : 0.f;
+                if (q) r.q[j] = (x + j < V) ? q[x + j] : 0.f;
+            }
+        }
+        return r;
+    }
+    __device__ void weights(const Raw& r, double w[4]) const {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            r.p[j] = (x + j < V) ? p[x + j] : 0.f;
-            if (q) r.q[j] = (x + j < V) ? q[x + j] : 0.f;
+            double d = q ? (double)r.p[j] - (double)r.q[j] : (double)r.p[j];
+            w[j] = d > 0.0 ? d : 0.0;
         }
     }
-    return r;
-}
+};
 
-// Weights of those elements, in binary64 (inputs widen exactly):
-// q == nullptr: w = max(0, p) (bonus row); otherwise w = max(0, p - q) (residual).
-__device__ __forceinline__ void weights4(const Raw4& r, bool resid, double w[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        double d = resid ? (double)r.p[j] - (double)r.q[j] : (double)r.p[j];
-        w[j] = d > 0.0 ? d : 0.0;
+// Four consecutive logits: an 8-byte bf16 load or a 16-byte fp32 load.
+template <bool BF16>
+struct Logit4;
+
+template <>
+struct Logit4<true> {
+    using Raw = u32x2;
+    __device__ static Raw load(const void* row, int64_t x) { return *(const Raw*)((const uint16_t*)row + x); }
+    __device__ static Raw neg_inf() { return Raw{0xFF80FF80u, 0xFF80FF80u}; }
+    __device__ static void unpack(const Raw& r, float z[4]) {
+        z[0] = bf16_lo(r[0]);
+        z[1] = bf16_hi(r[0]);
+        z[2] = bf16_lo(r[1]);
+        z[3] = bf16_hi(r[1]);
     }
+    __device__ static Raw pack(const float a[4]) {
+        return Raw{(__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xFFFF0000u),
+                   (__float_as_uint(a[2]) >> 16) | (__float_as_uint(a[3]) & 0xFFFF0000u)};
+    }
+    __device__ static float at(const void* row, int64_t i) { return bf16_at((const uint16_t*)row, i); }
+};
+
+template <>
+struct Logit4<false> {
+    using Raw = f32x4;
+    __device__ static Raw load(const void* row, int64_t x) { return *(const Raw*)((const float*)row + x); }
+    __device__ static Raw neg_inf() { return Raw{-INFINITY, -INFINITY, -INFINITY, -INFINITY}; }
+    __device__ static void unpack(const Raw& r, float z[4]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) z[k] = r[k];
+    }
+    __device__ static Raw pack(const float a[4]) { return Raw{a[0], a[1], a[2], a[3]}; }
+    __device__ static float at(const void* row, int64_t i) { return ((const float*)row)[i]; }
+};
+
+// Row statistics in the log2 domain: p(x) = 2^(z(x)*c - m) * inv, c = log2(e)/T.
+struct RowStats {
+    float m;
+    double inv;
+};
+
+__device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) {
+    return (double)ex2(fmaf(z, c, -st.m)) * st.inv;
 }
 
-// Pass 2 of the draw: all wavefronts write seg[s] = sum of the weights of
-// segment s (L = m * kSub elements). Returns the row's total weight S,
-// identical in every lane (each wavefront sums seg[] in the same order).
-template <bool VEC>
-__device__ double segment_totals(const float* p, const float* q, int V, int m, int nseg, double* seg) {
+// Logits rows with their statistics: w = max(0, p - q) (residual) or max(0, p).
+template <bool BF16, bool VEC>
+struct LogitSource {
+    const void* zt;
+    const void* zd;  // null: bonus row
+    int V;
+    float c;
+    RowStats st, sd;
+    using L = Logit4<BF16>;
+    struct Raw {
+        typename L::Raw t, d;
+    };
+    __device__ Raw load(int64_t x) const {
+        Raw r;
+        if (VEC) {
+            const bool in = x < V;
+            r.t = in ? L::load(zt, x) : L::neg_inf();
+            r.d = (zd && in) ? L::load(zd, x) : L::neg_inf();
+        } else {
+            float a[4], d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = (x + j < V) ? L::at(zt, x + j) : -INFINITY;
+                d[j] = (zd && x + j < V) ? L::at(zd, x + j) : -INFINITY;
+            }
+            r.t = L::pack(a);
+            r.d = L::pack(d);
+        }
+        return r;
+    }
+    __device__ void weights(const Raw& r, double w[4]) const {
+        // No contraction: p - q must be exactly 0 where the two rows agree;
+        // fma(e_t, inv_t, -(e_d * inv_d)) would leave a product's rounding error.
+#pragma clang fp contract(off)
+        float a[4], d[4];
+        L::unpack(r.t, a);
+        L::unpack(r.d, d);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double p = prob_of(a[j], c, st);
+            const double v = zd ? p - prob_of(d[j], c, sd) : p;
+            w[j] = v > 0.0 ? v : 0.0;
+        }
+    }
+};
+
+// ---- the draw ---------------------------------------------------------------
+
+// All wavefronts write seg[s] = sum of the weights of segment s
+// (L = m * kSub elements). Returns the row's total weight S, identical in
+// every lane (each wavefront sums seg[] in the same order).
+template <class Src>
+__device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t L = (int64_t)m * kSub;
     for (int s0 = wave; s0 < nseg; s0 += kWaves * kUnroll) {
@@ -78,16 +192,16 @@ __device__ double segment_totals(const float* p, const float* q, int V, int m, i
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
         for (int k = 0; k < m; ++k) {
-            Raw4 raw[kUnroll];
+            typename Src::Raw raw[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t x = (int64_t)(s0 + u * kWaves) * L + (int64_t)k * kSub + 4 * lane;
-                raw[u] = load4<VEC>(p, q, x, V);
+                raw[u] = src.load(x);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 double w[4];
-                weights4(raw[u], q != nullptr, w);
+                src.weights(raw[u], w);
                 acc[u] += ((w[0] + w[1]) + w[2]) + w[3];
             }
         }
@@ -107,8 +221,8 @@ __device__ double segment_totals(const float* p, const float* q, int V, int m, i
 // Smallest x with positive weight whose cumulative weight exceeds thr
 // (wavefront 0 only). If rounding leaves no such x in the chosen segment,
 // or u*S reaches S, the last positive-weight id is returned.
-template <bool VEC>
-__device__ int locate(const float* p, const float* q, int V, int m, int nseg, const double* seg, double thr) {
+template <class Src>
+__device__ int locate(const Src& src, int m, int nseg, const double* seg, double thr) {
     const int lane = threadIdx.x & (kWave - 1);
     // segment level: first s with seg[s] > 0 and P(s) > thr
     double carry = 0.0, pexcl = 0.0;
@@ -142,7 +256,7 @@ __device__ int locate(const float* p, const float* q, int V, int m, int nseg, co
     for (int k = 0; k < m; ++k) {
         const int64_t x0 = (int64_t)sstar * L + (int64_t)k * kSub + 4 * lane;
         double w[4];
-        weights4(load4<VEC>(p, q, x0, V), q != nullptr, w);
+        src.weights(src.load(x0), w);
         const double p1 = w[0] + w[1], p2 = p1 + w[2], p3 = p2 + w[3];
         const double incl = wave_incl_scan_d(p3, lane);
         double excl = __shfl_up(incl, 1, kWave);
@@ -163,6 +277,17 @@ __device__ int locate(const float* p, const float* q, int V, int m, int nseg, co
     }
     return last_pos;
 }
+
+// After segment_totals: wavefront 0 locates the draw at u*S (-1 when the row
+// has no positive weight). Only lane 0 of wavefront 0 may use the result.
+template <class Src>
+__device__ int draw(const Src& src, int m, int nseg, const double* seg, float u, double S) {
+    if (threadIdx.x >= kWave) return -2;
+    if (!(S > 0.0)) return -1;
+    return locate(src, m, nseg, seg, (double)u * S);
+}
+
+// ---- accept_kernel: probability rows ----------------------------------------
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void accept_kernel(const float* __restrict__ p, const float* __restrict__ q,
@@ -199,35 +324,221 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(const float* __restric
     __syncthreads();
     const int n = s_n;
 
-    // 2. the row (pair) of the final draw
-    const float* prow;
-    const float* qrow;
+    // 2-3. the draw from the row (pair) it needs
+    ProbSource<VEC> src;
+    src.V = V;
     if (n < kb) {
-        prow = p + ((int64_t)b * (K + 1) + n) * Vl;
-        qrow = q + ((int64_t)b * K + n) * Vl;
+        src.p = p + ((int64_t)b * (K + 1) + n) * Vl;
+        src.q = q + ((int64_t)b * K + n) * Vl;
     } else {
-        prow = p + ((int64_t)b * (K + 1) + kb) * Vl;
-        qrow = nullptr;
+        src.p = p + ((int64_t)b * (K + 1) + kb) * Vl;
+        src.q = nullptr;
     }
-    double S = segment_totals<VEC>(prow, qrow, V, m, nseg, seg);
-    if (!(S > 0.0) && qrow != nullptr) {
+    double S = segment_totals(src, m, nseg, seg);
+    if (!(S > 0.0) && src.q != nullptr) {
         // p_n == q_n leaves no residual mass: draw from max(0, p_n) instead
         __syncthreads();
-        qrow = nullptr;
-        S = segment_totals<VEC>(prow, qrow, V, m, nseg, seg);
+        src.q = nullptr;
+        S = segment_totals(src, m, nseg, seg);
     }
-    if (wave != 0) return;
-
-    // 3. inverse CDF at u[b, K_b]
-    int next = -1;
-    if (S > 0.0) {
-        const double thr = (double)uniforms[(int64_t)b * (K + 1) + kb] * S;
-        next = locate<VEC>(prow, qrow, V, m, nseg, seg, thr);
-    }
-    if (lane == 0) {
+    const int next = draw(src, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb], S);
+    if (threadIdx.x == 0) {
         n_accepted[b] = n;
         next_token[b] = next;
     }
+}
+
+// ---- accept_logits_kernel: logits rows, warped on the fly -------------------
+
+// Online (max, sum) of y = z*c: `s` accumulates 4-element fp32 partials in
+// binary64, rescaled when the running max grows.
+struct Online {
+    float m;
+    double s;
+};
+
+__device__ __forceinline__ void online_add4(const float z[4], float c, Online& o) {
+    const float zm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    const float ym = zm * c;
+    if (ym > o.m) {
+        o.s = (o.m == -INFINITY) ? 0.0 : o.s * (double)ex2(o.m - ym);
+        o.m = ym;
+    }
+    if (o.m == -INFINITY) return;  // all -inf so far: nothing to add (and no -inf - -inf)
+    const float part = (ex2(fmaf(z[0], c, -o.m)) + ex2(fmaf(z[1], c, -o.m))) +
+                       (ex2(fmaf(z[2], c, -o.m)) + ex2(fmaf(z[3], c, -o.m)));
+    o.s += (double)part;
+}
+
+__device__ __forceinline__ void online_merge(Online& a, float m2, double s2) {
+    const float mm = fmaxf(a.m, m2);
+    const double x = (a.m == -INFINITY) ? 0.0 : a.s * (double)ex2(a.m - mm);
+    const double y = (m2 == -INFINITY) ? 0.0 : s2 * (double)ex2(m2 - mm);
+    a.m = mm;
+    a.s = x + y;
+}
+
+// Wave-wide merge (same butterfly as the other reductions); result uniform.
+__device__ __forceinline__ void wave_online(Online& o) {
+    online_merge(o, dpp_f<kDppQuadXor1>(o.m), dpp_d<kDppQuadXor1>(o.s));
+    online_merge(o, dpp_f<kDppQuadXor2>(o.m), dpp_d<kDppQuadXor2>(o.s));
+    online_merge(o, dpp_f<kDppRowHalfMirror>(o.m), dpp_d<kDppRowHalfMirror>(o.s));
+    online_merge(o, dpp_f<kDppRowMirror>(o.m), dpp_d<kDppRowMirror>(o.s));
+    online_merge(o, swz16_f(o.m), swz16_d(o.s));
+    Online r{readlane_f(o.m, 0), readlane_d(o.s, 0)};
+    online_merge(r, readlane_f(o.m, 32), readlane_d(o.s, 32));
+    o = r;
+}
+
+struct StatsLds {
+    float m[2][kWaves];
+    double s[2][kWaves];
+};
+
+// Statistics of target row zt and (unless zd is null) draft row zd in one
+// pass, merged over the workgroup; every lane gets them. Contains barriers.
+template <bool BF16, bool VEC>
+__device__ void row_stats(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
+                          RowStats& sd) {
+    using L = Logit4<BF16>;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    Online ot{-INFINITY, 0.0}, od{-INFINITY, 0.0};
+    if (VEC) {
+        constexpr int U = 4;
+        const int nq = V / 4;
+        int j = tid;
+        for (; j + (U - 1) * kThreads < nq; j += U * kThreads) {
+            typename L::Raw rt[U], rd[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                rt[u] = L::load(zt, 4 * (int64_t)(j + u * kThreads));
+                rd[u] = zd ? L::load(zd, 4 * (int64_t)(j + u * kThreads)) : L::neg_inf();
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float a[4];
+                L::unpack(rt[u], a);
+                online_add4(a, c, ot);
+                if (zd) {
+                    L::unpack(rd[u], a);
+                    online_add4(a, c, od);
+                }
+            }
+        }
+        for (; j < nq; j += kThreads) {
+            float a[4];
+            L::unpack(L::load(zt, 4 * (int64_t)j), a);
+            online_add4(a, c, ot);
+            if (zd) {
+                L::unpack(L::load(zd, 4 * (int64_t)j), a);
+                online_add4(a, c, od);
+            }
+        }
+    } else {
+        for (int x = tid; x < V; x += kThreads) {
+            const float a[4] = {L::at(zt, x), -INFINITY, -INFINITY, -INFINITY};
+            online_add4(a, c, ot);
+            if (zd) {
+                const float d[4] = {L::at(zd, x), -INFINITY, -INFINITY, -INFINITY};
+                online_add4(d, c, od);
+            }
+        }
+    }
+    wave_online(ot);
+    if (zd) wave_online(od);
+    __syncthreads();  // the LDS slots may still be read from the previous call
+    if (lane == 0) {
+        lds->m[0][wave] = ot.m;
+        lds->s[0][wave] = ot.s;
+        lds->m[1][wave] = od.m;
+        lds->s[1][wave] = od.s;
+    }
+    __syncthreads();
+    Online rt{lane < kWaves ? lds->m[0][lane] : -INFINITY, lane < kWaves ? lds->s[0][lane] : 0.0};
+    wave_online(rt);
+    st = RowStats{rt.m, 1.0 / rt.s};
+    if (zd) {
+        Online rd{lane < kWaves ? lds->m[1][lane] : -INFINITY, lane < kWaves ? lds->s[1][lane] : 0.0};
+        wave_online(rd);
+        sd = RowStats{rd.m, 1.0 / rd.s};
+    }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __restrict__ zt,
+                                                                 const void* __restrict__ zd, int K, int V, int m,
+                                                                 int nseg, float c, const int32_t* __restrict__ tokens,
+                                                                 const int32_t* __restrict__ lens,
+                                                                 const float* __restrict__ uniforms,
+                                                                 int32_t* __restrict__ n_accepted,
+                                                                 int32_t* __restrict__ next_token) {
+    extern __shared__ double seg[];
+    __shared__ StatsLds lds;
+    using L = Logit4<BF16>;
+    const int b = blockIdx.x;
+    const int kb = clamp_len(lens, b, K);
+    const size_t row_bytes = (size_t)V * (BF16 ? 2 : 4);
+    const char* tbase = (const char*)zt + (size_t)b * (size_t)(K + 1) * row_bytes;
+    const char* dbase = (const char*)zd + (size_t)b * (size_t)K * row_bytes;
+
+    // 1. positions in order; stop at the first rejection
+    int n = kb;
+    bool have = false;  // statistics of row pair n are in st, sd
+    RowStats st{0.f, 0.0}, sd{0.f, 0.0};
+    for (int i = 0; i < kb; ++i) {
+        const int t = tokens[(int64_t)b * K + i];
+        if (t < 0 || t >= V) {  // out-of-range draft token: rejected, never dereferenced
+            n = i;
+            break;
+        }
+        const void* tr = tbase + (size_t)i * row_bytes;
+        const void* dr = dbase + (size_t)i * row_bytes;
+        row_stats<BF16, VEC>(tr, dr, V, c, &lds, st, sd);
+        const double pt = prob_of(L::at(tr, t), c, st);
+        const double qt = prob_of(L::at(dr, t), c, sd);
+        const double u = uniforms[(int64_t)b * (K + 1) + i];
+        if (!(u * qt < pt)) {
+            n = i;
+            have = true;
+            break;
+        }
+    }
+
+    // 2-3. the draw
+    LogitSource<BF16, VEC> src;
+    src.V = V;
+    src.c = c;
+    if (n < kb) {
+        src.zt = tbase + (size_t)n * row_bytes;
+        src.zd = dbase + (size_t)n * row_bytes;
+        if (!have) row_stats<BF16, VEC>(src.zt, src.zd, V, c, &lds, st, sd);
+    } else {
+        src.zt = tbase + (size_t)kb * row_bytes;
+        src.zd = nullptr;
+        row_stats<BF16, VEC>(src.zt, nullptr, V, c, &lds, st, sd);
+    }
+    src.st = st;
+    src.sd = sd;
+    double S = segment_totals(src, m, nseg, seg);
+    if (!(S > 0.0) && src.zd != nullptr) {
+        // p_n == q_n leaves no residual mass: draw from max(0, p_n) instead
+        __syncthreads();
+        src.zd = nullptr;
+        S = segment_totals(src, m, nseg, seg);
+    }
+    const int next = draw(src, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb], S);
+    if (threadIdx.x == 0) {
+        n_accepted[b] = n;
+        next_token[b] = next;
+    }
+}
+
+// m sub-blocks per segment keep the segment count within the LDS table
+void segment_shape(int V, int& m, int& nseg) {
+    const int64_t per_seg_min = ((int64_t)V + kMaxSeg - 1) / kMaxSeg;
+    m = (int)((per_seg_min + kSub - 1) / kSub);  // >= 1 since V >= 1
+    const int64_t L = (int64_t)m * kSub;
+    nseg = (int)(((int64_t)V + L - 1) / L);
 }
 
 }  // namespace
@@ -235,11 +546,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(const float* __restric
 hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
                          hipStream_t stream) {
-    // m sub-blocks per segment keep the segment count within the LDS table
-    const int64_t per_seg_min = ((int64_t)V + kMaxSeg - 1) / kMaxSeg;
-    const int m = (int)((per_seg_min + kSub - 1) / kSub);  // >= 1 since V >= 1
-    const int64_t L = (int64_t)m * kSub;
-    const int nseg = (int)(((int64_t)V + L - 1) / L);
+    int m, nseg;
+    segment_shape(V, m, nseg);
     const size_t lds = (size_t)nseg * sizeof(double);
     const bool vec = (V % 4 == 0) && ((uintptr_t)p % 16 == 0) && ((uintptr_t)q % 16 == 0);
     if (vec)
@@ -248,6 +556,33 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
     else
         hipLaunchKernelGGL(accept_kernel<false>, dim3(B), dim3(kThreads), lds, stream, p, q, K, V, m, nseg, tokens,
                            lens, uniforms, n_accepted, next_token);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
+                                const int32_t* tokens, const int32_t* lens, const float* uniforms,
+                                int32_t* n_accepted, int32_t* next_token, hipStream_t stream) {
+    int m, nseg;
+    segment_shape(V, m, nseg);
+    const size_t lds = (size_t)nseg * sizeof(double);
+    const float c = 1.4426950408889634f / temperature;
+    const uintptr_t al = bf16 ? 8 : 16;
+    const bool vec = (V % 4 == 0) && ((uintptr_t)zt % al == 0) && ((uintptr_t)zd % al == 0);
+    if (bf16) {
+        if (vec)
+            hipLaunchKernelGGL((accept_logits_kernel<true, true>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K, V,
+                               m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
+        else
+            hipLaunchKernelGGL((accept_logits_kernel<true, false>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
+                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((accept_logits_kernel<false, true>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
+                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
+        else
+            hipLaunchKernelGGL((accept_logits_kernel<false, false>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
+                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
+    }
     return hipGetLastError();
 }
 

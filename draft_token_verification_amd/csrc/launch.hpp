@@ -14,6 +14,10 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
                          const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
                          hipStream_t stream);
 
+hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
+                                const int32_t* tokens, const int32_t* lens, const float* uniforms,
+                                int32_t* n_accepted, int32_t* next_token, hipStream_t stream);
+
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
                        float temperature, float* probs, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

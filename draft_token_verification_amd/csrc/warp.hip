@@ -86,6 +86,7 @@ __device__ __forceinline__ void online_add(const float z[N], float scale, float&
         s = (m == -INFINITY) ? 0.0f : s * ex2(m - ym);
         m = ym;
     }
+    if (m == -INFINITY) return;  // all -inf so far: nothing to add (and no -inf - -inf)
 #pragma unroll
     for (int k = 0; k < N; ++k) s += ex2(fmaf(z[k], scale, -m));
 }

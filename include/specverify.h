@@ -171,6 +171,32 @@ sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t
                     const float* uniforms, int32_t* n_accepted, int32_t* next_token,
                     void* stream);
 
+/*
+ * sv_accept_logits -- speculative-sampling verification straight from logits.
+ *
+ * The result sv_accept gives on p = softmax(target_logits / T) and
+ * q = softmax(draft_logits / T) (the verify compares the distributions after
+ * the sampler's temperature step: llmstudio blog, sections 21-22 and 38;
+ * spec-verify card, "Method"), without writing any probability row: each
+ * position's target and draft rows are reduced to their softmax statistics
+ * in one pass, p_i(t_i) and q_i(t_i) follow from the two logits at t_i, and
+ * the correction or bonus row is re-derived from its logits for the draw.
+ * Rows after a sequence's first rejection are never read, so a round reads
+ * about (n_b + 2) row pairs per sequence instead of all of them twice.
+ *
+ * target_logits [B, K+1, V], draft_logits [B, K, V] of `dtype` (SV_F32 or
+ * SV_BF16), element-aligned; draft_tokens, draft_lens, uniforms, outputs as
+ * for sv_accept; temperature finite, > 0.
+ * Accuracy: p and q are evaluated in fp32 (absolute error well below 1e-6 per
+ * element) and the test and draw weights in binary64, so decisions and ids
+ * agree with an exact evaluation except where u lies within about 1e-6 of a
+ * ratio or cumulative-weight boundary.
+ * Errors: as sv_accept, plus SV_ERR_INVALID_ARG for a bad dtype or temperature.
+ */
+sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
+                           int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
+                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

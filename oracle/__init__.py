@@ -22,7 +22,7 @@ import threading
 
 import numpy as np
 
-__all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "icdf", "mass",
+__all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "accept_logits", "icdf", "mass",
            "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
            "FLAG_NO_MASS", "library_path", "load_library"]
 
@@ -52,6 +52,8 @@ def load_library(path: str):
     lib.or_icdf.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, i64, f64, f64, ctypes.POINTER(ctypes.c_int32)]
     lib.or_icdf.restype = i64
     lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
+    lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, f64, vp,
+                                     vp, vp]
     lib.or_overlap.argtypes = [vp, vp, ctypes.c_int, i64]
     lib.or_overlap.restype = f64
     assert lib.or_abi_version() == 1
@@ -171,6 +173,36 @@ def accept(p, q, tokens, uniforms, lens=None, rel_window: float = 1e-5, lib=None
     fl = np.empty(B, dtype=np.int32)
     (lib or _lib()).or_accept(_ptr(pa), _ptr(qa), dt, B, K, V, _ptr(t), _ptr(ln), _ptr(ua), du, float(rel_window), _ptr(n),
                      _ptr(nx), _ptr(fl))
+    return n, nx, fl
+
+
+def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_window: float = 1e-5,
+                  abs_window: float = 0.0, lib=None):
+    """Sampled verify from logits: or_accept on softmax(z / T) of the examined rows, in fp64.
+
+    zt [B, K+1, V], zd [B, K, V] logits (same dtype). Returns (n_accepted, next_token, flags).
+    ``abs_window`` adds an absolute floor to the CDF boundary flag.
+    """
+    ta, dt = _array(zt)
+    B, K1, V = ta.shape
+    K = K1 - 1
+    if zd is None and K == 0:
+        zd = np.empty((B, 0, V), dtype=ta.dtype)
+    da, dd = _array(zd)
+    if dd != dt:
+        raise TypeError("target and draft logits must share a dtype")
+    if da.shape != (B, K, V):
+        raise ValueError(f"draft shape {da.shape} != {(B, K, V)}")
+    t = np.zeros((B, 0), dtype=np.int32) if tokens is None and K == 0 else _i32(tokens).reshape(B, K)
+    ua, du = _array(uniforms)
+    if du == BF16 or ua.size != B * K1:
+        raise ValueError("uniforms must be fp32/fp64 [B, K+1]")
+    ln = _i32(lens)
+    n = np.empty(B, dtype=np.int32)
+    nx = np.empty(B, dtype=np.int32)
+    fl = np.empty(B, dtype=np.int32)
+    (lib or _lib()).or_accept_logits(_ptr(ta), _ptr(da), dt, B, K, V, float(T), _ptr(t), _ptr(ln), _ptr(ua), du,
+                                     float(rel_window), float(abs_window), _ptr(n), _ptr(nx), _ptr(fl))
     return n, nx, fl
 
 

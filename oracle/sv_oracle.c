@@ -42,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "sv_oracle.h"
@@ -241,6 +242,81 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
         n_accepted[b] = n;
         next_token[b] = (int32_t)next;
         if (flags) flags[b] = flag;
+    }
+}
+
+/* ---- sampled verification from logits  [BLOG s.21-22, s.38; CARD "Method"] ---
+ * The same procedure as or_accept on p = softmax(z_target / T) and
+ * q = softmax(z_draft / T) of each examined row, warped in fp64 with
+ * or_warp_row; only the rows the procedure examines are warped. Flags use
+ * the relative window plus an absolute floor `abs_window` on the CDF check
+ * (the warp's own tolerance), since a kernel that warps in fp32 carries that
+ * much absolute error in every p and q. */
+void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                      const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
+                      double rel_window, double abs_window, int32_t* n_accepted, int32_t* next_token,
+                      int32_t* flags) {
+#pragma omp parallel
+    {
+        double* p = (double*)malloc((size_t)V * sizeof(double));
+        double* q = (double*)malloc((size_t)V * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t b = 0; b < B; ++b) {
+            int32_t kb = clamp_len(lens, b, K);
+            int32_t flag = 0;
+            int32_t n = kb;
+            for (int32_t i = 0; i < kb; ++i) {
+                int64_t t = tokens[b * K + i];
+                double ui = elem(uniforms, u_dtype, b * (K + 1) + i);
+                if (t < 0 || t >= V) {
+                    n = i;
+                    break;
+                }
+                or_warp_row(row_ptr(zt, dtype, b * (K + 1) + i, V), dtype, V, T, p);
+                or_warp_row(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, q);
+                double rho = q[t] > 0.0 ? p[t] / q[t] : (p[t] > 0.0 ? INFINITY : 0.0);
+                if (isfinite(rho) && fabs(ui - rho) <= rel_window * rho) flag |= OR_FLAG_RATIO;
+                if (!(ui < rho)) {
+                    n = i;
+                    break;
+                }
+            }
+            double u_final = elem(uniforms, u_dtype, b * (K + 1) + kb);
+            int64_t next;
+            int32_t f2 = 0;
+            if (n < kb) {
+                /* p, q hold row n unless the loop stopped on an out-of-range token */
+                or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);
+                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);
+                if (or_mass(p, q, OR_F64, 0, V) > 0.0) {
+                    next = or_icdf(p, q, OR_F64, 0, V, u_final, rel_window, &f2);
+                } else {
+                    flag |= OR_FLAG_ZERO_RESIDUAL;
+                    next = or_icdf(p, NULL, OR_F64, 1, V, u_final, rel_window, &f2);
+                }
+            } else {
+                or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);
+                next = or_icdf(p, NULL, OR_F64, 1, V, u_final, rel_window, &f2);
+            }
+            /* absolute floor on the CDF window: recheck the draw's neighbours */
+            if (abs_window > 0.0 && next >= 0) {
+                int kind = (n < kb && !(flag & OR_FLAG_ZERO_RESIDUAL)) ? 0 : 1;
+                double S = or_mass(p, kind == 0 ? q : NULL, OR_F64, kind, V);
+                double thr = u_final * S, c = 0.0;
+                for (int64_t x = 0; x <= next; ++x) {
+                    double w = kind == 0 ? p[x] - q[x] : p[x];
+                    double c_prev = c;
+                    c += w > 0.0 ? w : 0.0;
+                    if (x == next && (fabs(thr - c_prev) <= abs_window || fabs(c - thr) <= abs_window))
+                        f2 |= OR_FLAG_CDF;
+                }
+            }
+            n_accepted[b] = n;
+            next_token[b] = (int32_t)next;
+            if (flags) flags[b] = flag | f2;
+        }
+        free(p);
+        free(q);
     }
 }
 

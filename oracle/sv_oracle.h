@@ -42,6 +42,11 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
                const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
                double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags);
 
+void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                      const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
+                      double rel_window, double abs_window, int32_t* n_accepted, int32_t* next_token,
+                      int32_t* flags);
+
 double or_overlap(const void* p, const void* q, int dtype, int64_t V);
 
 #ifdef __cplusplus

@@ -30,7 +30,7 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_last_error", "sv_set_wait_limit",
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_last_error", "sv_set_wait_limit",
                                     "sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_status_string",
                                     "sv_verify_greedy"]
 
@@ -136,3 +136,16 @@ def test_warp_workspace_size(sv):
 
 def test_wait_limit_rejects_negative(sv):
     assert sv._lib.sv_set_wait_limit(-1) == 1
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, FAKE, 0, -1, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "B = -1"),
+    ((FAKE, FAKE, 1, 2, 65, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "K = 65"),
+    ((FAKE, FAKE, 9, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "unknown dtype"),
+    ((FAKE, FAKE, 1, 2, 4, 100, 0.0, FAKE, None, FAKE, FAKE, FAKE, None), "temperature"),
+    ((FAKE, None, 1, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "null"),
+    ((ODD, FAKE, 0, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "misaligned"),
+])
+def test_accept_logits_rejects_bad_arguments(sv, args, fragment):
+    assert sv._lib.sv_accept_logits(*args) == 1
+    assert fragment in sv._lib.sv_last_error().decode()

@@ -121,7 +121,23 @@ def check_icdf(lib):
     assert oracle.icdf(np.zeros(4), 0.5, lib=lib)[0] == -1
 
 
-ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf]
+def check_logits(lib):
+    rng = np.random.default_rng(5)
+    B, K, V, T = 40, 4, 60, 0.8
+    zt = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    zd = (zt[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    # against the composition of the separately pinned warp (torch) and verify
+    p_ref = torch.softmax(torch.from_numpy(zt).double() / T, -1).numpy()
+    q_ref = torch.softmax(torch.from_numpy(zd).double() / T, -1).numpy()
+    t = np.array([[rng.choice(V, p=q_ref[b, i]) for i in range(K)] for b in range(B)], dtype=np.int32)
+    u = rng.random((B, K + 1))
+    lens = rng.integers(0, K + 1, size=B).astype(np.int32)
+    n1, x1, _ = oracle.accept(p_ref, q_ref, t, u, lens, lib=lib)
+    n2, x2, _ = oracle.accept_logits(zt, zd, t, u, lens, T, lib=lib)
+    assert (n1 == n2).all() and (x1 == x2).all()
+
+
+ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits]
 
 # (what goes wrong, exact source text, planted replacement)
 MUTANTS = [
@@ -149,6 +165,12 @@ MUTANTS = [
     ("warp ignores the temperature", "double e = exp(elem(z, dtype, x) / T - m);", "double e = exp(elem(z, dtype, x) - m);"),
     ("warp not normalised", "for (int64_t x = 0; x < V; ++x) p[x] /= s;", "(void)s;"),
     ("ragged warp writes one row too few", "if (live > R) live = R;", "if (live > R) live = R;\n        live -= 1;"),
+    ("logits verify warps draft rows with the target's stride",
+     "or_warp_row(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, q);",
+     "or_warp_row(row_ptr(zd, dtype, b * (K + 1) + i, V), dtype, V, T, q);"),
+    ("logits verify draws the correction from the wrong row",
+     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);",
+     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);"),
 ]
 
 
