@@ -24,10 +24,11 @@ import numpy as np
 
 __all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "accept_logits", "icdf", "mass",
            "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
-           "FLAG_NO_MASS", "library_path", "load_library"]
+           "FLAG_NO_MASS", "FLAG_TOPP", "warp_row_filtered", "softmax_warp_filtered", "library_path",
+           "load_library"]
 
 F32, BF16, F64 = 0, 1, 2
-FLAG_RATIO, FLAG_CDF, FLAG_ZERO_RESIDUAL, FLAG_NO_MASS = 1, 2, 4, 8
+FLAG_RATIO, FLAG_CDF, FLAG_ZERO_RESIDUAL, FLAG_NO_MASS, FLAG_TOPP = 1, 2, 4, 8, 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -44,6 +45,8 @@ def load_library(path: str):
     vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
     lib.or_warp_row.argtypes = [vp, ctypes.c_int, i64, f64, vp]
     lib.or_softmax_warp.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, f64, vp]
+    lib.or_warp_row_filtered.argtypes = [vp, ctypes.c_int, i64, f64, i32, f64, f64, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.or_softmax_warp_filtered.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, f64, vp, vp, f64, vp, vp]
     lib.or_argmax_row.argtypes = [vp, ctypes.c_int, i64]
     lib.or_argmax_row.restype = i64
     lib.or_verify_greedy.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
@@ -129,6 +132,33 @@ def softmax_warp(logits, lens=None, extra_rows: int = 0, T: float = 1.0, lib=Non
     ln = _i32(lens)
     (lib or _lib()).or_softmax_warp(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), float(T), _ptr(out))
     return out
+
+
+def warp_row_filtered(z, T: float = 1.0, top_k: int = 0, top_p: float = 1.0, window: float = 1e-5, lib=None):
+    """Temperature, top-k, top-p, renormalise (fp64) -> (probabilities, flag)."""
+    a, dt = _array(z)
+    out = np.empty(a.shape[-1], dtype=np.float64)
+    fl = ctypes.c_int32(0)
+    (lib or _lib()).or_warp_row_filtered(_ptr(a), dt, a.shape[-1], float(T), int(top_k), float(top_p), float(window),
+                                         _ptr(out), ctypes.byref(fl))
+    return out, int(fl.value)
+
+
+def softmax_warp_filtered(logits, lens=None, extra_rows: int = 0, T: float = 1.0, top_k=None, top_p=None,
+                          window: float = 1e-5, lib=None):
+    """Filtered warp of the live rows of logits [B, R, V] with per-sequence top_k [B] and
+    top_p [B] (None: off) -> (probs [B, R, V] fp64 with NaN in dead rows, flags [B, R])."""
+    a, dt = _array(logits)
+    B, R, V = a.shape
+    out = np.full((B, R, V), np.nan, dtype=np.float64)
+    flags = np.zeros((B, R), dtype=np.int32)
+    ln = _i32(lens)
+    tk = _i32(top_k)
+    tp = None if top_p is None else np.ascontiguousarray(np.asarray(
+        top_p.detach().cpu().numpy() if hasattr(top_p, "detach") else top_p, dtype=np.float32))
+    (lib or _lib()).or_softmax_warp_filtered(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), float(T), _ptr(tk),
+                                             _ptr(tp), float(window), _ptr(out), _ptr(flags))
+    return out, flags
 
 
 def argmax_row(row, lib=None) -> int:

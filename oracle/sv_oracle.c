@@ -320,6 +320,98 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
     }
 }
 
+/* ---- filtered warp: temperature, top-k, top-p, normalise [BLOG §38] ---
+ * The sampler pipeline turns logits into the effective distribution in the
+ * order: temperature, top-k, top-p, renormalisation (penalties and other
+ * stateful filters are not part of it here; see BLOG §39). Readings:
+ *  R16 top-k keeps every id whose value is at least the k-th largest value
+ *      (ties at the boundary are all kept); k <= 0 or k >= V keeps all ids.
+ *  R17 top-p acts on the top-k survivors renormalised: an id is kept iff the
+ *      mass of the ids strictly more probable than it is below top_p times
+ *      their total (equal values share one decision); the most probable
+ *      value is always kept; top_p >= 1 (or NaN) keeps all survivors.
+ *  R18 ids outside the kept set get probability exactly 0.
+ * `flag` gets OR_FLAG_TOPP when the top-p decision of a boundary value lies
+ * within `window` (relative to the survivors' mass) of the threshold. */
+typedef struct {
+    double y;
+    int64_t x;
+} vy_t;
+
+static int by_value_desc(const void* a, const void* b) {
+    double ya = ((const vy_t*)a)->y, yb = ((const vy_t*)b)->y;
+    if (ya > yb) return -1;
+    if (ya < yb) return 1;
+    int64_t xa = ((const vy_t*)a)->x, xb = ((const vy_t*)b)->x;
+    return xa < xb ? -1 : (xa > xb);
+}
+
+void or_warp_row_filtered(const void* z, int dtype, int64_t V, double T, int32_t top_k, double top_p,
+                          double window, double* p, int32_t* flag) {
+    int32_t f = 0;
+    vy_t* s = (vy_t*)malloc((size_t)V * sizeof(vy_t));
+    /* temperature */
+    double m = -INFINITY;
+    for (int64_t x = 0; x < V; ++x) {
+        s[x].y = elem(z, dtype, x) / T;
+        s[x].x = x;
+        if (s[x].y > m) m = s[x].y;
+    }
+    /* descending value order (a library sort; ties in index order) */
+    qsort(s, (size_t)V, sizeof(vy_t), by_value_desc);
+    /* top-k: survivors are the first n entries of the sorted order */
+    int64_t n = V;
+    if (top_k > 0 && top_k < V) {
+        double kth = s[top_k - 1].y;
+        n = top_k;
+        while (n < V && s[n].y >= kth) ++n;
+    }
+    for (int64_t x = 0; x < V; ++x) p[x] = 0.0;
+    double S = 0.0;
+    for (int64_t i = 0; i < n; ++i) S += exp(s[i].y - m);
+    /* top-p over the survivors, one decision per group of equal values */
+    int64_t kept = n;
+    if (top_p < 1.0) {
+        double target = top_p * S, above = 0.0;
+        int64_t i = 0;
+        kept = 0;
+        while (i < n) {
+            int64_t j = i;
+            double g = 0.0;
+            while (j < n && s[j].y == s[i].y) g += exp(s[j++].y - m);
+            if (fabs(above - target) <= window * S) f |= OR_FLAG_TOPP;
+            if (i > 0 && !(above < target)) break;
+            kept = j;
+            above += g;
+            i = j;
+        }
+    }
+    double Sk = 0.0;
+    for (int64_t i = 0; i < kept; ++i) Sk += exp(s[i].y - m);
+    for (int64_t i = 0; i < kept; ++i) p[s[i].x] = exp(s[i].y - m) / Sk;
+    free(s);
+    if (flag) *flag = f;
+}
+
+/* Rows r < clamp(lens[b]) + extra_rows of every sequence, with that
+ * sequence's top_k[b] / top_p[b] (NULL: the filter is off); rows past the
+ * live count are left untouched (the caller pre-fills them). */
+void or_softmax_warp_filtered(const void* logits, int dtype, int64_t B, int64_t R, int64_t V,
+                              const int32_t* lens, int32_t extra_rows, double T, const int32_t* top_k,
+                              const float* top_p, double window, double* probs, int32_t* flags) {
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t live = (int64_t)clamp_len(lens, b, R - extra_rows) + extra_rows;
+            if (r >= (live < R ? live : R)) continue;
+            int32_t f = 0;
+            or_warp_row_filtered(row_ptr(logits, dtype, b * R + r, V), dtype, V, T, top_k ? top_k[b] : 0,
+                                 top_p ? (double)top_p[b] : 1.0, window, probs + (size_t)(b * R + r) * V, &f);
+            if (flags) flags[b * R + r] = f;
+        }
+    }
+}
+
 /* ---- per-position acceptance a = sum_x min(p(x), q(x))  [CARD "Measured"] ---
  * The probability that a token drawn from q passes the min(1, p/q) test. */
 double or_overlap(const void* p, const void* q, int dtype, int64_t V) {

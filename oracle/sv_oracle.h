@@ -21,7 +21,8 @@ enum {
     OR_FLAG_RATIO = 1,         /* a tested u lies within the window of its ratio p/q */
     OR_FLAG_CDF = 2,           /* the draw threshold lies within the window of a CDF step */
     OR_FLAG_ZERO_RESIDUAL = 4, /* residual mass was zero; drew from p instead */
-    OR_FLAG_NO_MASS = 8        /* the final-draw row had no positive mass; next = -1 */
+    OR_FLAG_NO_MASS = 8,       /* the final-draw row had no positive mass; next = -1 */
+    OR_FLAG_TOPP = 16          /* a top-p decision lies within the window of its threshold */
 };
 
 int or_abi_version(void);
@@ -29,6 +30,12 @@ int or_abi_version(void);
 void or_warp_row(const void* z, int dtype, int64_t V, double T, double* p);
 void or_softmax_warp(const void* logits, int dtype, int64_t B, int64_t R, int64_t V,
                      const int32_t* lens, int32_t extra_rows, double T, double* probs);
+
+void or_warp_row_filtered(const void* z, int dtype, int64_t V, double T, int32_t top_k, double top_p,
+                          double window, double* p, int32_t* flag);
+void or_softmax_warp_filtered(const void* logits, int dtype, int64_t B, int64_t R, int64_t V,
+                              const int32_t* lens, int32_t extra_rows, double T, const int32_t* top_k,
+                              const float* top_p, double window, double* probs, int32_t* flags);
 
 int64_t or_argmax_row(const void* row, int dtype, int64_t V);
 void or_verify_greedy(const void* target, int dtype, int64_t B, int64_t K, int64_t V,

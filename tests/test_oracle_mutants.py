@@ -137,7 +137,40 @@ def check_logits(lib):
     assert (n1 == n2).all() and (x1 == x2).all()
 
 
-ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits]
+def check_filtered(lib):
+    # tie groups at the top-k boundary and in the nucleus (closed forms)
+    z = np.array([5.0, 4.0, 3.0, 4.0, 4.0, 1.0], dtype=np.float32)
+    got, _ = oracle.warp_row_filtered(z, 1.0, 2, 1.0, lib=lib)
+    w = np.exp(np.array([5.0, 4.0, 0, 4.0, 4.0, 0]) - 5.0) * np.array([1, 1, 0, 1, 1, 0])
+    np.testing.assert_allclose(got, w / w.sum(), rtol=1e-12)
+    z = np.log(np.array([0.4, 0.2, 0.2, 0.1, 0.1]))
+    np.testing.assert_allclose(oracle.warp_row_filtered(z, 1.0, 0, 0.41, lib=lib)[0], [0.5, 0.25, 0.25, 0, 0],
+                               rtol=1e-12)
+    np.testing.assert_allclose(oracle.warp_row_filtered(z, 1.0, 3, 0.55, lib=lib)[0], [0.5, 0.25, 0.25, 0, 0],
+                               rtol=1e-12)
+    # a k-then-p case against torch: sort, cut, renormalise (tie-free row)
+    rng = np.random.default_rng(6)
+    z = rng.permutation(np.linspace(-6.0, 6.0, 400)) + rng.uniform(0, 1e-3, 400)
+    for k, p, T in [(60, 0.8, 0.9), (60, 1.0, 0.9)]:
+        check_filtered_against_torch(z, k, p, T, lib)
+
+
+def check_filtered_against_torch(z, k, p, T, lib):
+    y = torch.as_tensor(z) / T
+    kth = torch.topk(y, k).values[-1]
+    y = torch.where(y >= kth, y, torch.tensor(-np.inf, dtype=y.dtype))
+    pr = torch.softmax(y, -1)
+    srt, idx = torch.sort(pr, descending=True)
+    above = torch.cumsum(srt, 0) - srt
+    keep = torch.zeros_like(pr, dtype=torch.bool)
+    keep[idx[above < p]] = True
+    ref = torch.where(keep, pr, torch.zeros_like(pr))
+    ref = (ref / ref.sum()).numpy()
+    np.testing.assert_allclose(oracle.warp_row_filtered(z, T, k, p, lib=lib)[0], ref, rtol=1e-10, atol=1e-300)
+
+
+ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits,
+              check_filtered]
 
 # (what goes wrong, exact source text, planted replacement)
 MUTANTS = [
@@ -171,6 +204,13 @@ MUTANTS = [
     ("logits verify draws the correction from the wrong row",
      "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);",
      "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);"),
+    ("top-k drops the ties of the k-th value", "while (n < V && s[n].y >= kth) ++n;", "while (n < V && s[n].y > kth) ++n;"),
+    ("top-k keeps one value too many", "double kth = s[top_k - 1].y;", "double kth = s[top_k < V - 1 ? top_k : top_k - 1].y;"),
+    ("top-p measured against the unfiltered mass", "for (int64_t i = 0; i < n; ++i) S += exp(s[i].y - m);",
+     "for (int64_t i = 0; i < V; ++i) S += exp(s[i].y - m);"),
+    ("top-p drops the group that crosses the threshold", "if (i > 0 && !(above < target)) break;",
+     "if (i > 0 && !(above + g < target)) break;"),
+    ("filtered rows not renormalised", "p[s[i].x] = exp(s[i].y - m) / Sk;", "p[s[i].x] = exp(s[i].y - m) / S;"),
 ]
 
 
