@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
-           "sv_accept_logits",
+           "sv_accept_logits", "sv_softmax_warp_filtered",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
@@ -55,6 +55,8 @@ def _load():
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.sv_softmax_warp_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_softmax_warp_filtered.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, vp, vp]
+    lib.sv_softmax_warp_filtered.restype = c_int
     lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_set_wait_limit.argtypes = [i32]
     lib.sv_set_wait_limit.restype = c_int
@@ -186,6 +188,44 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
         st = _lib.sv_softmax_warp(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens), int(extra_rows),
                                   float(temperature), _ptr(probs), _ptr(workspace), ws_bytes, stream)
     _check("sv_softmax_warp", st)
+    return probs
+
+
+def _per_sequence(v, B: int, dtype: torch.dtype, dev: torch.device, name: str) -> Optional[torch.Tensor]:
+    """None stays None; a Python number is broadcast to [B]; a tensor must be [B] (moved and cast)."""
+    if v is None:
+        return None
+    if isinstance(v, torch.Tensor):
+        if tuple(v.shape) != (B,):
+            raise ValueError(f"{name} must be [B] = {(B,)}")
+        return v.to(device=dev, dtype=dtype).contiguous()
+    return torch.full((B,), v, dtype=dtype, device=dev)
+
+
+def sv_softmax_warp_filtered(logits: torch.Tensor, temperature: float = 1.0, draft_lens: Optional[torch.Tensor] = None,
+                             extra_rows: int = 0, top_k=None, top_p=None,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Temperature -> top-k -> top-p -> renormalise for the live rows of logits [B, R, V].
+
+    ``top_k`` / ``top_p``: None (off), a number for every sequence, or a [B] tensor.
+    Filtered-out ids get probability 0. Rows that are not live are left as in ``out``.
+    """
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dev = logits.device
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    tk = _per_sequence(top_k, B, torch.int32, dev, "top_k")
+    tp = _per_sequence(top_p, B, torch.float32, dev, "top_p")
+    probs = _out((B, R, V), dev, out, torch.float32, "out")
+    with torch.cuda.device(dev):
+        st = _lib.sv_softmax_warp_filtered(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens),
+                                           int(extra_rows), float(temperature), _ptr(tk), _ptr(tp), _ptr(probs),
+                                           _stream(dev))
+    _check("sv_softmax_warp_filtered", st)
     return probs
 
 

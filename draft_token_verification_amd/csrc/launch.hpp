@@ -21,6 +21,10 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
                        float temperature, float* probs, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+hipError_t launch_warp_filtered(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens,
+                                int extra_rows, float temperature, const int32_t* top_k, const float* top_p,
+                                float* probs, hipStream_t stream);
+
 // Workspace the cooperative warp path needs (0: that path does not apply to V).
 size_t warp_workspace_bytes(int B, int R, int V);
 

@@ -117,6 +117,35 @@ size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
 sv_status sv_set_wait_limit(int32_t polls);
 
 /*
+ * sv_softmax_warp_filtered -- the sampler pipeline temperature -> top-k ->
+ * top-p -> renormalise (llmstudio blog "Как работает speculative decoding и
+ * MTP при инференсе LLM", section 38: the verify compares the distributions
+ * after the sampler's transforms, target and draft filtered alike).
+ *
+ * Same rows, layouts and live-row rule as sv_softmax_warp, plus per-sequence
+ * filter parameters:
+ * top_k   [B] int32 device array, or NULL (off for every sequence). Sequence
+ *         b keeps every id whose logit is at least its row's top_k[b]-th
+ *         largest logit (ties at the boundary are all kept); top_k[b] <= 0 or
+ *         >= V turns the filter off.
+ * top_p   [B] fp32 device array, or NULL (off). After top-k, with the
+ *         survivors renormalised, an id is kept iff the mass of the ids
+ *         strictly more probable than it is below top_p[b] times the
+ *         survivors' mass; equal logits are kept or dropped together; the
+ *         largest logit is always kept (so top_p[b] <= 0 keeps only it);
+ *         top_p[b] >= 1 or NaN turns the filter off.
+ * probs   live rows get softmax over the kept ids and exactly 0 elsewhere.
+ * Kept sets are decided exactly for top-k; top-p decides with fixed-point
+ * masses (2^-40 or finer per unit) of fp32 exponentials, so a value within
+ * ~1e-5 relative of its threshold may fall either way. Results are bitwise
+ * identical run to run. No workspace; one workgroup per live row.
+ * Errors: as sv_softmax_warp, plus misaligned top_k / top_p.
+ */
+sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
+                                   const int32_t* draft_lens, int32_t extra_rows, float temperature,
+                                   const int32_t* top_k, const float* top_p, float* probs, void* stream);
+
+/*
  * sv_verify_greedy -- temperature-0 verification.
  *
  * Accept draft token t_i while it equals argmax(target row i); at the first

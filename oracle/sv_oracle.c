@@ -379,7 +379,8 @@ void or_warp_row_filtered(const void* z, int dtype, int64_t V, double T, int32_t
             int64_t j = i;
             double g = 0.0;
             while (j < n && s[j].y == s[i].y) g += exp(s[j++].y - m);
-            if (fabs(above - target) <= window * S) f |= OR_FLAG_TOPP;
+            /* the most probable value is kept whatever top_p is: never a close call */
+            if (i > 0 && fabs(above - target) <= window * S) f |= OR_FLAG_TOPP;
             if (i > 0 && !(above < target)) break;
             kept = j;
             above += g;

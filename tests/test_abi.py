@@ -31,8 +31,8 @@ def sv():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_last_error", "sv_set_wait_limit",
-                                    "sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_status_string",
-                                    "sv_verify_greedy"]
+                                    "sv_softmax_warp", "sv_softmax_warp_filtered", "sv_softmax_warp_workspace_bytes",
+                                    "sv_status_string", "sv_verify_greedy"]
 
 
 def test_library_exports_every_declared_symbol(sv):
@@ -149,3 +149,22 @@ def test_wait_limit_rejects_negative(sv):
 def test_accept_logits_rejects_bad_arguments(sv, args, fragment):
     assert sv._lib.sv_accept_logits(*args) == 1
     assert fragment in sv._lib.sv_last_error().decode()
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, 0, 2, 0, 100, None, 0, 1.0, None, None, FAKE, None), "R = 0"),
+    ((FAKE, 0, -1, 3, 100, None, 1, 1.0, None, None, FAKE, None), "B = -1"),
+    ((FAKE, 0, 2, 3, 100, None, 4, 1.0, None, None, FAKE, None), "extra_rows"),
+    ((FAKE, 0, 2, 3, 0, None, 1, 1.0, None, None, FAKE, None), "V = 0"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 0.0, None, None, FAKE, None), "temperature"),
+    ((FAKE, 0, 2, 3, 100, None, 1, float("nan"), None, None, FAKE, None), "temperature"),
+    ((FAKE, 2, 2, 3, 100, None, 1, 1.0, None, None, FAKE, None), "unknown dtype"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, None, None, None, None), "null"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, ODD, None, FAKE, None), "misaligned"),
+    ((FAKE, 0, 2, 3, 100, None, 1, 1.0, None, ODD, FAKE, None), "misaligned"),
+])
+def test_softmax_warp_filtered_rejects_bad_arguments(sv, args, fragment):
+    assert sv._lib.sv_softmax_warp_filtered(*args) == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+    # B == 0 is an empty call
+    assert sv._lib.sv_softmax_warp_filtered(None, 0, 0, 3, 100, None, 1, 1.0, None, None, None, None) == 0

@@ -126,6 +126,10 @@ def test_boundary_flag():
     assert fl & oracle.FLAG_TOPP
     _, fl = oracle.warp_row_filtered(z, 1.0, 0, 0.45, window=1e-5)
     assert fl == 0
+    # the most probable value is kept for any top_p: top_p = 0 or tiny is no close call
+    for p in (0.0, 1e-7):
+        _, fl = oracle.warp_row_filtered(z, 1.0, 0, p, window=1e-5)
+        assert fl == 0
 
 
 def test_invariances():
