@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--workload", default="logits-bf16-b512-k16-v256000-zipf")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--top-k", type=int, default=50, help="top-k of the filtered-warp leg")
+    ap.add_argument("--top-p", type=float, default=0.9, help="top-p of the filtered-warp leg")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain fp32 device copy of COPY_BYTES (counter calibration under rocprofv3)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -145,6 +147,28 @@ def main():
         torch.cuda.synchronize()
         fused_ms = f0.elapsed_time(f1) / args.steps
 
+    # the filtered warp (temperature, top-k, top-p) of target and draft rows
+    filt_ms = None
+    if batch.kind == "logits":
+        tk = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
+        tp = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
+
+        def filtered():
+            sv.sv_softmax_warp_filtered(batch.target, T, lens, 1, tk, tp, out=p)
+            sv.sv_softmax_warp_filtered(batch.draft, T, lens, 0, tk, tp, out=q)
+
+        for _ in range(args.warmup):
+            filtered()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.steps):
+            filtered()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        filt_ms = g0.elapsed_time(g1) / args.steps
+
     # algorithmic bytes of each kernel (what the method must move)
     kb = lens.cpu().numpy() if lens is not None else np.full(B, K)
     n_s = n_acc.cpu().numpy().astype(np.int64)
@@ -203,6 +227,12 @@ def main():
         "greedy_full_read_GBps_equiv": round(gbs(B * (K + 1) * V * elem, greedy_ms), 1),
         "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
     }
+    if filt_ms is not None:
+        out["kernels"].update({
+            "filtered_warp_ms": round(filt_ms, 4),
+            "filtered_warp_GBps": round(gbs(warp_bytes_t + warp_bytes_d, filt_ms), 1),
+            "filtered_warp_top_k": args.top_k, "filtered_warp_top_p": args.top_p,
+        })
     if fused_ms is not None:
         out["kernels"].update({
             "accept_logits_ms": round(fused_ms, 4),
