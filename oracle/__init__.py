@@ -24,7 +24,8 @@ import numpy as np
 
 __all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "accept_logits", "icdf", "mass",
            "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
-           "FLAG_NO_MASS", "FLAG_TOPP", "warp_row_filtered", "softmax_warp_filtered", "library_path",
+           "FLAG_NO_MASS", "FLAG_TOPP", "warp_row_filtered", "softmax_warp_filtered", "top2_margin", "gate_update",
+           "gate_choose", "GATE_DEFAULTS", "library_path",
            "load_library"]
 
 F32, BF16, F64 = 0, 1, 2
@@ -57,6 +58,10 @@ def load_library(path: str):
     lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
     lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, f64, vp,
                                      vp, vp]
+    lib.or_top2_margin.argtypes = [vp, ctypes.c_int, i64]
+    lib.or_top2_margin.restype = f64
+    lib.or_gate_update.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, f64]
+    lib.or_gate_choose.argtypes = [vp, vp, i64, i64, i64, vp, vp, f64, f64, f64, f64, f64, i32, f64, vp]
     lib.or_overlap.argtypes = [vp, vp, ctypes.c_int, i64]
     lib.or_overlap.restype = f64
     assert lib.or_abi_version() == 1
@@ -159,6 +164,44 @@ def softmax_warp_filtered(logits, lens=None, extra_rows: int = 0, T: float = 1.0
     (lib or _lib()).or_softmax_warp_filtered(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), float(T), _ptr(tk),
                                              _ptr(tp), float(window), _ptr(out), _ptr(flags))
     return out, flags
+
+
+def top2_margin(row, lib=None) -> float:
+    """Largest value minus the largest of the others (fp64; +inf for one element)."""
+    a, dt = _array(row)
+    return float((lib or _lib()).or_top2_margin(_ptr(a), dt, a.shape[-1]))
+
+
+# the DSpark notes' default gate parameters (draft, verify base and slope, plain decode in ms)
+GATE_DEFAULTS = dict(draft_ms=196.0, verify_base_ms=300.0, verify_slope_ms=109.0, plain_ms=303.0, margin=1.15,
+                     decay=0.9, min_draft=0, margin_threshold=0.0)
+
+
+def gate_update(hits, trials, K: int, lens, n_accepted, buckets=None, decay: float = 0.9, lib=None):
+    """Record one verify round (draft lens [B] of at most K, n_accepted [B], buckets [B, K] or None
+    for the position) into hits / trials [B, NB] (float64 numpy arrays, updated in place)."""
+    assert hits.dtype == np.float64 and trials.dtype == np.float64 and hits.flags.c_contiguous
+    assert trials.flags.c_contiguous and trials.shape == hits.shape
+    B, NB = hits.shape
+    ln = _i32(lens)
+    na = _i32(n_accepted)
+    bk = _i32(buckets)
+    (lib or _lib()).or_gate_update(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(ln), _ptr(na), _ptr(bk),
+                                   float(decay))
+
+
+def gate_choose(hits, trials, K: int, buckets=None, top2_margin=None, lib=None, **params):
+    """Next draft length [B] (int32) from the gate's counts; params default to GATE_DEFAULTS."""
+    P = dict(GATE_DEFAULTS)
+    P.update(params)
+    B, NB = hits.shape
+    bk = _i32(buckets)
+    tm = None if top2_margin is None else np.ascontiguousarray(np.asarray(top2_margin, dtype=np.float32))
+    out = np.empty(B, dtype=np.int32)
+    (lib or _lib()).or_gate_choose(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(bk), _ptr(tm), P["draft_ms"],
+                                   P["verify_base_ms"], P["verify_slope_ms"], P["plain_ms"], P["margin"],
+                                   int(P["min_draft"]), P["margin_threshold"], _ptr(out))
+    return out
 
 
 def argmax_row(row, lib=None) -> int:

@@ -413,6 +413,91 @@ void or_softmax_warp_filtered(const void* logits, int dtype, int64_t B, int64_t 
     }
 }
 
+/* ---- top1 - top2 margin of a row [DSPARK "pre-draft gating"] -----------
+ * The largest value minus the largest of the others (one occurrence of the
+ * maximum removed, so a tied maximum gives 0); +inf when V == 1. */
+double or_top2_margin(const void* row, int dtype, int64_t V) {
+    int64_t am = or_argmax_row(row, dtype, V);
+    double v1 = elem(row, dtype, am), v2 = -INFINITY;
+    for (int64_t x = 0; x < V; ++x)
+        if (x != am && elem(row, dtype, x) > v2) v2 = elem(row, dtype, x);
+    return v1 - v2;
+}
+
+/* ---- acceptance-driven draft-length gate [DSPARK "gating"] --------------
+ * Per sequence b, per bucket c (a draft position, or a caller's confidence
+ * bucket of it): decayed counts hits[b, c] and trials[b, c].
+ * Update after a verify round in which sequence b drafted kb = lens[b]
+ * tokens and had n = n_accepted[b] accepted:
+ *   if kb > 0: every count of b is multiplied by `decay` (forgetting), then
+ *   positions j = 0 .. min(n, kb - 1) are recorded (trials += 1, hits += 1 if
+ *   j < n). Positions after the first rejection were not observed (censored)
+ *   and are not recorded.
+ * Readings: a round without a draft observes nothing and forgets nothing;
+ * bucket ids outside [0, NB) are clamped into it. */
+static int32_t bucket_of(const int32_t* buckets, int64_t b, int64_t K, int64_t j, int64_t NB) {
+    int64_t c = buckets ? buckets[b * K + j] : j;
+    return (int32_t)(c < 0 ? 0 : (c >= NB ? NB - 1 : c));
+}
+
+void or_gate_update(double* hits, double* trials, int64_t B, int64_t NB, int64_t K, const int32_t* lens,
+                    const int32_t* n_accepted, const int32_t* buckets, double decay) {
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t kb = clamp_len(lens, b, K);
+        if (kb == 0) continue;
+        for (int64_t c = 0; c < NB; ++c) {
+            hits[b * NB + c] *= decay;
+            trials[b * NB + c] *= decay;
+        }
+        int64_t n = n_accepted[b] < 0 ? 0 : (n_accepted[b] > kb ? kb : n_accepted[b]);
+        int64_t last = n < kb ? n : kb - 1;
+        for (int64_t j = 0; j <= last; ++j) {
+            int32_t c = bucket_of(buckets, b, K, j, NB);
+            trials[b * NB + c] += 1.0;
+            if (j < n) hits[b * NB + c] += 1.0;
+        }
+    }
+}
+
+/* Choice of the next draft length of sequence b, in 0 .. K:
+ *   p_j = hits/trials of position j's bucket (1 while the bucket has no
+ *         trials: a cold gate drafts and learns; reading),
+ *   E(n) = 1 + sum_{i<n} prod_{j<=i} p_j,
+ *   cost(0) = plain_ms, cost(n) = draft_ms + verify_base_ms + verify_slope_ms * n,
+ *   n* = argmax_n E(n) / cost(n) (ties: the larger n; reading);
+ *   a truncation n* < K is taken only if E/cost beats the full draft's by the
+ *   factor `margin`; then n >= min_draft; and when margin_threshold > 0 and
+ *   the committed token's top1 - top2 logit margin is below it, 0 (skip the
+ *   draft). */
+void or_gate_choose(const double* hits, const double* trials, int64_t B, int64_t NB, int64_t K,
+                    const int32_t* buckets, const float* top2_margin, double draft_ms, double verify_base_ms,
+                    double verify_slope_ms, double plain_ms, double margin, int32_t min_draft,
+                    double margin_threshold, int32_t* next_lens) {
+    for (int64_t b = 0; b < B; ++b) {
+        double E = 1.0, prod = 1.0;
+        double best = E / plain_ms, full = best;
+        int64_t nstar = 0;
+        for (int64_t n = 1; n <= K; ++n) {
+            int32_t c = bucket_of(buckets, b, K, n - 1, NB);
+            double t = trials[b * NB + c];
+            double p = t > 0.0 ? hits[b * NB + c] / t : 1.0;
+            prod *= p;
+            E += prod;
+            double r = E / (draft_ms + verify_base_ms + verify_slope_ms * (double)n);
+            if (r >= best) {
+                best = r;
+                nstar = n;
+            }
+            if (n == K) full = r;
+        }
+        int64_t len = nstar;
+        if (nstar < K && !(best >= margin * full)) len = K;
+        if (len < min_draft) len = min_draft > K ? K : min_draft;
+        if (margin_threshold > 0.0 && top2_margin && (double)top2_margin[b] < margin_threshold) len = 0;
+        next_lens[b] = (int32_t)len;
+    }
+}
+
 /* ---- per-position acceptance a = sum_x min(p(x), q(x))  [CARD "Measured"] ---
  * The probability that a token drawn from q passes the min(1, p/q) test. */
 double or_overlap(const void* p, const void* q, int dtype, int64_t V) {

@@ -54,6 +54,14 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
                       double rel_window, double abs_window, int32_t* n_accepted, int32_t* next_token,
                       int32_t* flags);
 
+double or_top2_margin(const void* row, int dtype, int64_t V);
+void or_gate_update(double* hits, double* trials, int64_t B, int64_t NB, int64_t K, const int32_t* lens,
+                    const int32_t* n_accepted, const int32_t* buckets, double decay);
+void or_gate_choose(const double* hits, const double* trials, int64_t B, int64_t NB, int64_t K,
+                    const int32_t* buckets, const float* top2_margin, double draft_ms, double verify_base_ms,
+                    double verify_slope_ms, double plain_ms, double margin, int32_t min_draft,
+                    double margin_threshold, int32_t* next_lens);
+
 double or_overlap(const void* p, const void* q, int dtype, int64_t V);
 
 #ifdef __cplusplus

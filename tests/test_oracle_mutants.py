@@ -169,8 +169,36 @@ def check_filtered_against_torch(z, k, p, T, lib):
     np.testing.assert_allclose(oracle.warp_row_filtered(z, T, k, p, lib=lib)[0], ref, rtol=1e-10, atol=1e-300)
 
 
+def check_gate(lib):
+    from tests.test_oracle_gate import brute_choice
+    K = 5
+    h = np.zeros((2, K))
+    t = np.zeros((2, K))
+    oracle.gate_update(h, t, K, lens=[5, 0], n_accepted=[2, 0], decay=1.0, lib=lib)
+    np.testing.assert_array_equal(t[0], [1, 1, 1, 0, 0])
+    np.testing.assert_array_equal(h[0], [1, 1, 0, 0, 0])
+    assert t[1].sum() == 0
+    h = np.zeros((1, 2))
+    t = np.zeros((1, 2))
+    for _ in range(200):
+        oracle.gate_update(h, t, 2, lens=[2], n_accepted=[1], decay=0.9, lib=lib)
+    np.testing.assert_allclose(t[0], [10, 10], rtol=1e-9)
+    np.testing.assert_allclose(h[0], [10, 0], rtol=1e-9, atol=1e-12)
+    for p in ([0.9, 0.9, 0.0, 0.0, 0.0], [0.7, 0.5, 0.9, 0.3, 0.8], [0.3] * 5, [1.0] * 5):
+        hh = np.asarray(p, dtype=np.float64).reshape(1, -1) * 1000
+        tt = np.full((1, 5), 1000.0)
+        assert oracle.gate_choose(hh, tt, 5, lib=lib)[0] == brute_choice(np.asarray(p), 5)
+    # a truncation that wins by less than the margin factor keeps the full draft
+    hh = np.array([[0.95, 0.95, 0, 0, 0, 0]]) * 1000
+    tt = np.full((1, 6), 1000.0)
+    assert oracle.gate_choose(hh, tt, 6, margin=4.0, lib=lib)[0] == 6
+    assert oracle.gate_choose(hh, tt, 6, margin=1.15, lib=lib)[0] == 2
+    assert oracle.top2_margin(np.array([1.0, 3.0, 3.0], np.float32), lib=lib) == 0.0
+    assert oracle.top2_margin(np.array([1.0, 3.0, 2.5], np.float32), lib=lib) == 0.5
+
+
 ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits,
-              check_filtered]
+              check_filtered, check_gate]
 
 # (what goes wrong, exact source text, planted replacement)
 MUTANTS = [
@@ -211,6 +239,15 @@ MUTANTS = [
     ("top-p drops the group that crosses the threshold", "if (i > 0 && !(above < target)) break;",
      "if (i > 0 && !(above + g < target)) break;"),
     ("filtered rows not renormalised", "p[s[i].x] = exp(s[i].y - m) / Sk;", "p[s[i].x] = exp(s[i].y - m) / S;"),
+    ("gate counts censored positions as misses", "int64_t last = n < kb ? n : kb - 1;", "int64_t last = kb - 1;"),
+    ("gate forgets hits but not trials", "trials[b * NB + c] *= decay;", "trials[b * NB + c] *= 1.0;"),
+    ("gate reads the next position's acceptance", "int32_t c = bucket_of(buckets, b, K, n - 1, NB);",
+     "int32_t c = bucket_of(buckets, b, K, n < K ? n : K - 1, NB);"),
+    ("gate truncation margin inverted", "if (nstar < K && !(best >= margin * full)) len = K;",
+     "if (nstar < K && !(best * margin >= full)) len = K;"),
+    ("gate verify cost without the per-token slope", "verify_slope_ms * (double)n);", "verify_slope_ms);"),
+    ("top-2 margin drops every copy of a tied maximum", "if (x != am && elem(row, dtype, x) > v2)",
+     "if (elem(row, dtype, x) < v1 && elem(row, dtype, x) > v2)"),
 ]
 
 
