@@ -21,11 +21,19 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
-           "sv_accept_logits", "sv_softmax_warp_filtered",
+           "sv_accept_logits", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
+           "sv_gate_choose", "GATE_DEFAULTS",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
 SV_F32, SV_BF16 = 0, 1
+
+
+class GateParams(ctypes.Structure):
+    """sv_gate_params of include/specverify.h."""
+    _fields_ = [("draft_ms", ctypes.c_double), ("verify_base_ms", ctypes.c_double),
+                ("verify_slope_ms", ctypes.c_double), ("plain_ms", ctypes.c_double), ("margin", ctypes.c_double),
+                ("min_draft", ctypes.c_int32), ("margin_threshold", ctypes.c_float)]
 SV_MAX_K = 64
 _STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_HIP"}
 
@@ -55,6 +63,12 @@ def _load():
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.sv_softmax_warp_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_verify_greedy_margin.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.sv_verify_greedy_margin.restype = c_int
+    lib.sv_gate_update.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_double, vp]
+    lib.sv_gate_update.restype = c_int
+    lib.sv_gate_choose.argtypes = [vp, vp, i32, i32, i32, vp, vp, ctypes.POINTER(GateParams), vp, vp]
+    lib.sv_gate_choose.restype = c_int
     lib.sv_softmax_warp_filtered.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, vp, vp]
     lib.sv_softmax_warp_filtered.restype = c_int
     lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
@@ -189,6 +203,94 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
                                   float(temperature), _ptr(probs), _ptr(workspace), ws_bytes, stream)
     _check("sv_softmax_warp", st)
     return probs
+
+
+def sv_verify_greedy_margin(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
+                            draft_lens: Optional[torch.Tensor] = None,
+                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Greedy verify plus the top1 - top2 margin of the row next_token comes from
+    -> (n_accepted[B], next_token[B], top2_margin[B] fp32)."""
+    _dev(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    toks = _int32(draft_tokens, "draft_tokens", dev)
+    if K > 0 and (toks is None or tuple(toks.shape) != (B, K)):
+        raise ValueError(f"draft_tokens must be [B, K] = {(B, K)}")
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
+    nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
+    mg = _out((B,), dev, None if out is None else out[2], torch.float32, "top2_margin")
+    with torch.cuda.device(dev):
+        st = _lib.sv_verify_greedy_margin(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
+                                          _ptr(n), _ptr(nx), _ptr(mg), _stream(dev))
+    _check("sv_verify_greedy_margin", st)
+    return n, nx, mg
+
+
+# The DSpark notes' defaults (milliseconds; only their ratios matter).
+GATE_DEFAULTS = dict(draft_ms=196.0, verify_base_ms=300.0, verify_slope_ms=109.0, plain_ms=303.0, margin=1.15,
+                     min_draft=0, margin_threshold=0.0)
+
+
+def _gate_state(hits: torch.Tensor, trials: torch.Tensor):
+    for t, name in ((hits, "hits"), (trials, "trials")):
+        _dev(t, name)
+        if t.dtype != torch.float64 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float64 [B, NB] device tensor")
+    if hits.shape != trials.shape or hits.device != trials.device:
+        raise ValueError("hits and trials must match")
+    return hits.shape
+
+
+def sv_gate_update(hits: torch.Tensor, trials: torch.Tensor, K: int, draft_lens: Optional[torch.Tensor],
+                   n_accepted: torch.Tensor, buckets: Optional[torch.Tensor] = None, decay: float = 0.9) -> None:
+    """Record one verify round into the gate's counts (in place, on the device)."""
+    B, NB = _gate_state(hits, trials)
+    dev = hits.device
+    lens = _int32(draft_lens, "draft_lens", dev)
+    na = _int32(n_accepted, "n_accepted", dev)
+    bk = _int32(buckets, "buckets", dev)
+    if na is None or tuple(na.shape) != (B,) or (lens is not None and tuple(lens.shape) != (B,)):
+        raise ValueError("n_accepted and draft_lens must be [B]")
+    if bk is not None and tuple(bk.shape) != (B, K):
+        raise ValueError(f"buckets must be [B, K] = {(B, K)}")
+    with torch.cuda.device(dev):
+        st = _lib.sv_gate_update(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(lens), _ptr(na), _ptr(bk),
+                                 float(decay), _stream(dev))
+    _check("sv_gate_update", st)
+
+
+def sv_gate_choose(hits: torch.Tensor, trials: torch.Tensor, K: int, buckets: Optional[torch.Tensor] = None,
+                   top2_margin: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   **params) -> torch.Tensor:
+    """Next draft length [B] int32 from the gate's counts; params default to GATE_DEFAULTS."""
+    B, NB = _gate_state(hits, trials)
+    dev = hits.device
+    P = dict(GATE_DEFAULTS)
+    unknown = set(params) - set(P)
+    if unknown:
+        raise ValueError(f"unknown gate parameters {sorted(unknown)}")
+    P.update(params)
+    bk = _int32(buckets, "buckets", dev)
+    if bk is not None and tuple(bk.shape) != (B, K):
+        raise ValueError(f"buckets must be [B, K] = {(B, K)}")
+    if top2_margin is not None:
+        _dev(top2_margin, "top2_margin")
+        if top2_margin.dtype != torch.float32 or tuple(top2_margin.shape) != (B,):
+            raise ValueError("top2_margin must be fp32 [B]")
+    nl = _out((B,), dev, out, torch.int32, "out")
+    gp = GateParams(P["draft_ms"], P["verify_base_ms"], P["verify_slope_ms"], P["plain_ms"], P["margin"],
+                    int(P["min_draft"]), P["margin_threshold"])
+    with torch.cuda.device(dev):
+        st = _lib.sv_gate_choose(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(bk), _ptr(top2_margin),
+                                 ctypes.byref(gp), _ptr(nl), _stream(dev))
+    _check("sv_gate_choose", st)
+    return nl
 
 
 def _per_sequence(v, B: int, dtype: torch.dtype, dev: torch.device, name: str) -> Optional[torch.Tensor]:

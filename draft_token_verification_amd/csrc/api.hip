@@ -68,7 +68,27 @@ sv_status launched(const char* fn, hipError_t e) {
     return ok();
 }
 
+sv_status greedy_common(const char* fn, const void* target, int dtype, int32_t B, int32_t K, int64_t V,
+                        const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
+                        int32_t* next_token, float* top2_margin, bool want_margin, void* stream) {
+    sv_status st;
+    if ((st = check_dtype(dtype)) != SV_OK) return st;
+    if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
+    if (B == 0) return ok();
+    if (!target || !n_accepted || !next_token || (K > 0 && !draft_tokens) || (want_margin && !top2_margin))
+        return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(target, dtype_bytes(dtype)) || !aligned(n_accepted, 4) || !aligned(next_token, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || (draft_lens && !aligned(draft_lens, 4)) ||
+        (top2_margin && !aligned(top2_margin, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_greedy(target, dtype == SV_BF16, B, K, (int)V, draft_tokens, draft_lens, n_accepted,
+                                          next_token, top2_margin, (hipStream_t)stream));
+}
+
 }  // namespace
+
+static_assert(sizeof(sv_gate_params) == 48, "sv_gate_params layout: five doubles, an int32 and a float");
 
 extern "C" {
 
@@ -147,19 +167,67 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
 sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                            const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
                            int32_t* next_token, void* stream) {
-    const char* fn = "sv_verify_greedy";
-    sv_status st;
-    if ((st = check_dtype(dtype)) != SV_OK) return st;
-    if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
+    return greedy_common("sv_verify_greedy", target, dtype, B, K, V, draft_tokens, draft_lens, n_accepted, next_token,
+                         nullptr, false, stream);
+}
+
+sv_status sv_verify_greedy_margin(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
+                                  const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
+                                  int32_t* next_token, float* top2_margin, void* stream) {
+    return greedy_common("sv_verify_greedy_margin", target, dtype, B, K, V, draft_tokens, draft_lens, n_accepted,
+                         next_token, top2_margin, true, stream);
+}
+
+sv_status sv_gate_update(double* hits, double* trials, int32_t B, int32_t NB, int32_t K, const int32_t* draft_lens,
+                         const int32_t* n_accepted, const int32_t* buckets, double decay, void* stream) {
+    const char* fn = "sv_gate_update";
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (NB < 1) return fail(SV_ERR_INVALID_ARG, "%s: NB = %d < 1", fn, NB);
+    if (K < 0 || K > SV_MAX_K) return fail(SV_ERR_INVALID_ARG, "%s: K = %d not in [0, %d]", fn, K, SV_MAX_K);
+    if (!buckets && NB < K) return fail(SV_ERR_INVALID_ARG, "%s: NB = %d < K = %d with position buckets", fn, NB, K);
+    if (!(decay >= 0.0 && decay <= 1.0)) return fail(SV_ERR_INVALID_ARG, "%s: decay %g not in [0, 1]", fn, decay);
+    if ((int64_t)B * NB > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*NB exceeds 2^31-1", fn);
     if (B == 0) return ok();
-    if (!target || !n_accepted || !next_token || (K > 0 && !draft_tokens))
-        return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
-    if (!aligned(target, dtype_bytes(dtype)) || !aligned(n_accepted, 4) || !aligned(next_token, 4) ||
-        (draft_tokens && !aligned(draft_tokens, 4)) || (draft_lens && !aligned(draft_lens, 4)))
+    if (!hits || !trials || !n_accepted) return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(hits, 8) || !aligned(trials, 8) || !aligned(n_accepted, 4) || (draft_lens && !aligned(draft_lens, 4)) ||
+        (buckets && !aligned(buckets, 4)))
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    sv_status st;
     if ((st = check_device()) != SV_OK) return st;
-    return launched(fn, sv::launch_greedy(target, dtype == SV_BF16, B, K, (int)V, draft_tokens, draft_lens, n_accepted,
-                                          next_token, (hipStream_t)stream));
+    return launched(fn, sv::launch_gate_update(hits, trials, B, NB, K, draft_lens, n_accepted, buckets, decay,
+                                               (hipStream_t)stream));
+}
+
+sv_status sv_gate_choose(const double* hits, const double* trials, int32_t B, int32_t NB, int32_t K,
+                         const int32_t* buckets, const float* top2_margin, const sv_gate_params* params,
+                         int32_t* next_lens, void* stream) {
+    const char* fn = "sv_gate_choose";
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (NB < 1) return fail(SV_ERR_INVALID_ARG, "%s: NB = %d < 1", fn, NB);
+    if (K < 0 || K > SV_MAX_K) return fail(SV_ERR_INVALID_ARG, "%s: K = %d not in [0, %d]", fn, K, SV_MAX_K);
+    if (!buckets && NB < K) return fail(SV_ERR_INVALID_ARG, "%s: NB = %d < K = %d with position buckets", fn, NB, K);
+    if (!params) return fail(SV_ERR_INVALID_ARG, "%s: null params", fn);
+    const sv_gate_params& p = *params;
+    if (!(p.draft_ms >= 0.0 && p.verify_base_ms >= 0.0 && p.verify_slope_ms >= 0.0 && p.plain_ms > 0.0) ||
+        !std::isfinite(p.draft_ms) || !std::isfinite(p.verify_base_ms) || !std::isfinite(p.verify_slope_ms) ||
+        !std::isfinite(p.plain_ms) || !(p.draft_ms + p.verify_base_ms + p.verify_slope_ms > 0.0))
+        return fail(SV_ERR_INVALID_ARG, "%s: costs must be finite, >= 0, plain_ms > 0 and a draft round > 0", fn);
+    if (!(p.margin > 0.0) || !std::isfinite(p.margin)) return fail(SV_ERR_INVALID_ARG, "%s: margin %g", fn, p.margin);
+    if (p.min_draft < 0) return fail(SV_ERR_INVALID_ARG, "%s: min_draft = %d < 0", fn, p.min_draft);
+    if (!std::isfinite(p.margin_threshold))
+        return fail(SV_ERR_INVALID_ARG, "%s: margin_threshold must be finite", fn);
+    if ((int64_t)B * NB > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*NB exceeds 2^31-1", fn);
+    if (B == 0) return ok();
+    if (!hits || !trials || !next_lens) return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(hits, 8) || !aligned(trials, 8) || !aligned(next_lens, 4) || (buckets && !aligned(buckets, 4)) ||
+        (top2_margin && !aligned(top2_margin, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    sv_status st;
+    if ((st = check_device()) != SV_OK) return st;
+    const sv::GateCosts g{p.draft_ms, p.verify_base_ms, p.verify_slope_ms, p.plain_ms,
+                          p.margin,   p.min_draft,      (double)p.margin_threshold};
+    return launched(fn, sv::launch_gate_choose(hits, trials, B, NB, K, buckets, top2_margin, g, next_lens,
+                                               (hipStream_t)stream));
 }
 
 sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t B, int32_t K, int64_t V,

@@ -26,6 +26,43 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 8;
 
+// Argmax plus the runner-up value, for top1 - top2 margins: (v, i) merge as in
+// argmax_merge; s is the largest value other than the winner's one
+// occurrence, so a tied maximum leaves s == v (margin 0).
+__device__ __forceinline__ void top2_merge(float& v, int& i, float& s, float w, int j, float t) {
+    const bool take = (w > v) | ((w == v) & (j < i));
+    s = fmaxf(fmaxf(s, t), take ? v : w);
+    v = take ? w : v;
+    i = take ? j : i;
+}
+
+__device__ __forceinline__ void wave_top2(float& v, int& i, float& s) {
+    top2_merge(v, i, s, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(i), dpp_f<kDppQuadXor1>(s));
+    top2_merge(v, i, s, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(i), dpp_f<kDppQuadXor2>(s));
+    top2_merge(v, i, s, dpp_f<kDppRowHalfMirror>(v), dpp_i<kDppRowHalfMirror>(i), dpp_f<kDppRowHalfMirror>(s));
+    top2_merge(v, i, s, dpp_f<kDppRowMirror>(v), dpp_i<kDppRowMirror>(i), dpp_f<kDppRowMirror>(s));
+    top2_merge(v, i, s, swz16_f(v), swz16_i(i), swz16_f(s));
+    float v0 = readlane_f(v, 0), s0 = readlane_f(s, 0);
+    int i0 = readlane_i(i, 0);
+    top2_merge(v0, i0, s0, readlane_f(v, 32), readlane_i(i, 32), readlane_f(s, 32));
+    v = v0;
+    i = i0;
+    s = s0;
+}
+
+// One element in index order: the running (best, bidx) and, with M, the
+// runner-up value `second`.
+template <bool M>
+__device__ __forceinline__ void take(float x, int idx, float& best, int& bidx, float& second) {
+    if (x > best) {
+        if (M) second = best;
+        best = x;
+        bidx = idx;
+    } else if (M) {
+        second = fmaxf(second, x);
+    }
+}
+
 template <bool BF16>
 struct RowReader;
 
@@ -35,22 +72,30 @@ struct RowReader<true> {
     static constexpr int kPerVec = 8;
     using Vec = u32x4;
     __device__ static float at(const void* row, int64_t i) { return bf16_at((const uint16_t*)row, i); }
-    __device__ static void scan(const Vec& w, int base, float& best, int& bidx) {
+    template <bool M>
+    __device__ static void scan(const Vec& w, int base, float& best, int& bidx, float& second) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
-            if (lo > best) { best = lo; bidx = base + 2 * k; }
-            if (hi > best) { best = hi; bidx = base + 2 * k + 1; }
+            take<M>(bf16_lo(w[k]), base + 2 * k, best, bidx, second);
+            take<M>(bf16_hi(w[k]), base + 2 * k + 1, best, bidx, second);
         }
     }
     // First vector of a lane: an element that only ties -inf must still be
     // taken when the lane holds nothing yet.
-    __device__ static void scan_first(const Vec& w, int base, float& best, int& bidx) {
+    template <bool M>
+    __device__ static void scan_first(const Vec& w, int base, float& best, int& bidx, float& second) {
+        const float lo0 = bf16_lo(w[0]);
+        if (bidx == INT32_MAX) {
+            best = lo0;
+            bidx = base;
+        } else {
+            take<M>(lo0, base, best, bidx, second);
+        }
+        take<M>(bf16_hi(w[0]), base + 1, best, bidx, second);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
-            if (lo > best || bidx == INT32_MAX) { best = lo; bidx = base + 2 * k; }
-            if (hi > best) { best = hi; bidx = base + 2 * k + 1; }
+        for (int k = 1; k < 4; ++k) {
+            take<M>(bf16_lo(w[k]), base + 2 * k, best, bidx, second);
+            take<M>(bf16_hi(w[k]), base + 2 * k + 1, best, bidx, second);
         }
     }
 };
@@ -61,24 +106,31 @@ struct RowReader<false> {
     static constexpr int kPerVec = 4;
     using Vec = f32x4;
     __device__ static float at(const void* row, int64_t i) { return ((const float*)row)[i]; }
-    __device__ static void scan(const Vec& w, int base, float& best, int& bidx) {
+    template <bool M>
+    __device__ static void scan(const Vec& w, int base, float& best, int& bidx, float& second) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (w[k] > best) { best = w[k]; bidx = base + k; }
+        for (int k = 0; k < 4; ++k) take<M>(w[k], base + k, best, bidx, second);
     }
-    __device__ static void scan_first(const Vec& w, int base, float& best, int& bidx) {
-        if (w[0] > best || bidx == INT32_MAX) { best = w[0]; bidx = base; }
+    template <bool M>
+    __device__ static void scan_first(const Vec& w, int base, float& best, int& bidx, float& second) {
+        if (bidx == INT32_MAX) {
+            best = w[0];
+            bidx = base;
+        } else {
+            take<M>(w[0], base, best, bidx, second);
+        }
 #pragma unroll
-        for (int k = 1; k < 4; ++k)
-            if (w[k] > best) { best = w[k]; bidx = base + k; }
+        for (int k = 1; k < 4; ++k) take<M>(w[k], base + k, best, bidx, second);
     }
 };
 
-// Argmax of one row of V elements. Returns the wave-uniform index; every lane
-// of the workgroup must call it (it contains one barrier). `slot` alternates
+// Argmax of one row of V elements. Returns the wave-uniform index (and, with
+// M, the row's maximum and runner-up values in vmax / vsecond); every lane of
+// the workgroup must call it (it contains one barrier). `slot` alternates
 // between two LDS buffers so that consecutive rows never race on them.
-template <bool BF16>
-__device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int (*lds_i)[kWaves], int slot) {
+template <bool BF16, bool M>
+__device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int (*lds_i)[kWaves],
+                            float (*lds_s)[kWaves], int slot, float& vmax, float& vsecond) {
     using R = RowReader<BF16>;
     constexpr int E = R::kPerVec;
     const int tid = threadIdx.x;
@@ -91,7 +143,7 @@ __device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int 
     const int nvec = (V - head) / E;
     const int tail0 = head + nvec * E;
 
-    float best = -INFINITY;
+    float best = -INFINITY, second = -INFINITY;
     int bidx = INT32_MAX;
     if (tid < head) {
         best = R::at(row, tid);
@@ -100,7 +152,7 @@ __device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int 
     const typename R::Vec* vrow = (const typename R::Vec*)((const char*)row + head * (BF16 ? 2 : 4));
     int j = tid;
     if (j < nvec) {
-        R::scan_first(load_nt(vrow + j), head + j * E, best, bidx);
+        R::template scan_first<M>(load_nt(vrow + j), head + j * E, best, bidx, second);
         j += kThreads;
     }
     for (; j + (kUnroll - 1) * kThreads < nvec; j += kUnroll * kThreads) {
@@ -108,34 +160,53 @@ __device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) w[u] = load_nt(vrow + j + u * kThreads);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) R::scan(w[u], head + (j + u * kThreads) * E, best, bidx);
+        for (int u = 0; u < kUnroll; ++u) R::template scan<M>(w[u], head + (j + u * kThreads) * E, best, bidx, second);
     }
-    for (; j < nvec; j += kThreads) R::scan(load_nt(vrow + j), head + j * E, best, bidx);
+    for (; j < nvec; j += kThreads) R::template scan<M>(load_nt(vrow + j), head + j * E, best, bidx, second);
     if (tail0 + tid < V) {
-        float v = R::at(row, tail0 + tid);
-        if (v > best || bidx == INT32_MAX) { best = v; bidx = tail0 + tid; }
+        const float v = R::at(row, tail0 + tid);
+        if (bidx == INT32_MAX) {
+            best = v;
+            bidx = tail0 + tid;
+        } else {
+            take<M>(v, tail0 + tid, best, bidx, second);
+        }
     }
 
-    wave_argmax(best, bidx);
+    if (M) {
+        wave_top2(best, bidx, second);
+    } else {
+        wave_argmax(best, bidx);
+    }
     if (lane == 0) {
         lds_v[slot][wave] = best;
         lds_i[slot][wave] = bidx;
+        if (M) lds_s[slot][wave] = second;
     }
     __syncthreads();
     float v = lane < kWaves ? lds_v[slot][lane] : -INFINITY;
     int i = lane < kWaves ? lds_i[slot][lane] : INT32_MAX;
-    wave_argmax(v, i);
+    if (M) {
+        float s = lane < kWaves ? lds_s[slot][lane] : -INFINITY;
+        wave_top2(v, i, s);
+        vmax = v;
+        vsecond = s;
+    } else {
+        wave_argmax(v, i);
+    }
     return i;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_kernel(const void* __restrict__ target, int K, int V,
-                                                          const int32_t* __restrict__ tokens,
-                                                          const int32_t* __restrict__ lens,
-                                                          int32_t* __restrict__ n_accepted,
-                                                          int32_t* __restrict__ next_token) {
+// M: also write top2_margin[b] = max - runner-up of the row next_token comes
+// from (the committed token's row; 0 for a tied maximum, +inf when V == 1).
+template <bool BF16, bool M>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_kernel(
+    const void* __restrict__ target, int K, int V, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ lens, int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token,
+    float* __restrict__ top2_margin) {
     __shared__ float lds_v[2][kWaves];
     __shared__ int lds_i[2][kWaves];
+    __shared__ float lds_s[M ? 2 : 1][kWaves];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int kb = clamp_len(lens, b, K);
@@ -146,12 +217,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 
     int i = 0;
     for (;; ++i) {
-        const int am = block_argmax<BF16>(base + (size_t)i * row_bytes, V, lds_v, lds_i, i & 1);
+        float vmax = 0.0f, vsecond = 0.0f;
+        const int am =
+            block_argmax<BF16, M>(base + (size_t)i * row_bytes, V, lds_v, lds_i, lds_s, i & 1, vmax, vsecond);
         // a token outside [0, V) never equals an argmax: it is a miss
         if (i == kb || readlane_i(my_tok, i) != am) {
             if (threadIdx.x == 0) {
                 n_accepted[b] = i;
                 next_token[b] = am;
+                if (M) top2_margin[b] = vmax - vsecond;
             }
             return;
         }
@@ -161,13 +235,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 }  // namespace
 
 hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
-                         const int32_t* lens, int32_t* n_accepted, int32_t* next_token, hipStream_t stream) {
-    if (bf16)
-        hipLaunchKernelGGL(greedy_kernel<true>, dim3(B), dim3(kThreads), 0, stream, target, K, V, tokens, lens,
-                           n_accepted, next_token);
-    else
-        hipLaunchKernelGGL(greedy_kernel<false>, dim3(B), dim3(kThreads), 0, stream, target, K, V, tokens, lens,
-                           n_accepted, next_token);
+                         const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
+                         hipStream_t stream) {
+    const dim3 grid(B), block(kThreads);
+    if (top2_margin) {
+        if (bf16)
+            hipLaunchKernelGGL((greedy_kernel<true, true>), grid, block, 0, stream, target, K, V, tokens, lens,
+                               n_accepted, next_token, top2_margin);
+        else
+            hipLaunchKernelGGL((greedy_kernel<false, true>), grid, block, 0, stream, target, K, V, tokens, lens,
+                               n_accepted, next_token, top2_margin);
+    } else {
+        if (bf16)
+            hipLaunchKernelGGL((greedy_kernel<true, false>), grid, block, 0, stream, target, K, V, tokens, lens,
+                               n_accepted, next_token, top2_margin);
+        else
+            hipLaunchKernelGGL((greedy_kernel<false, false>), grid, block, 0, stream, target, K, V, tokens, lens,
+                               n_accepted, next_token, top2_margin);
+    }
     return hipGetLastError();
 }
 

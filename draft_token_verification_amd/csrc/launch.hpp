@@ -7,8 +7,10 @@
 
 namespace sv {
 
+// top2_margin may be null (no margin output).
 hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
-                         const int32_t* lens, int32_t* n_accepted, int32_t* next_token, hipStream_t stream);
+                         const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
+                         hipStream_t stream);
 
 hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
@@ -24,6 +26,19 @@ hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const
 hipError_t launch_warp_filtered(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens,
                                 int extra_rows, float temperature, const int32_t* top_k, const float* top_p,
                                 float* probs, hipStream_t stream);
+
+// Draft-length gate parameters as the kernels take them (by value).
+struct GateCosts {
+    double draft_ms, verify_base_ms, verify_slope_ms, plain_ms, margin;
+    int min_draft;
+    double margin_threshold;
+};
+
+hipError_t launch_gate_update(double* hits, double* trials, int B, int NB, int K, const int32_t* lens,
+                              const int32_t* n_accepted, const int32_t* buckets, double decay, hipStream_t stream);
+
+hipError_t launch_gate_choose(const double* hits, const double* trials, int B, int NB, int K, const int32_t* buckets,
+                              const float* top2_margin, const GateCosts& g, int32_t* next_lens, hipStream_t stream);
 
 // Workspace the cooperative warp path needs (0: that path does not apply to V).
 size_t warp_workspace_bytes(int B, int R, int V);

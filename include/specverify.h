@@ -167,6 +167,75 @@ sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, 
                            int32_t* n_accepted, int32_t* next_token, void* stream);
 
 /*
+ * sv_verify_greedy_margin -- sv_verify_greedy plus, per sequence, the top1 -
+ * top2 margin of the row next_token is taken from (target row n_accepted[b]):
+ * its largest value minus the largest of its other values, computed in fp32
+ * (0 for a tied maximum, +inf when V == 1). A serving loop feeds it to the
+ * pre-draft gate, which skips drafting when the target is unsure of the
+ * committed token (PocketLLM DSpark notes, "gating": the top1 - top2 logit
+ * margin of the committed token).
+ * top2_margin  [B] fp32 output, 4-byte aligned, required.
+ * Same arguments, results and errors as sv_verify_greedy otherwise.
+ */
+sv_status sv_verify_greedy_margin(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
+                                  const int32_t* draft_tokens, const int32_t* draft_lens,
+                                  int32_t* n_accepted, int32_t* next_token, float* top2_margin,
+                                  void* stream);
+
+/*
+ * Acceptance-driven draft-length gate (PocketLLM DSpark notes, "gating"), on
+ * the device: the verify's n_accepted never has to reach the host.
+ *
+ * State: hits[B, NB] and trials[B, NB], fp64 device arrays owned by the
+ * caller, zero-filled for a cold gate; bucket c of sequence b counts the
+ * decayed acceptances and observations of the draft positions mapped to c
+ * (the position itself when `buckets` is NULL, which needs NB >= K; or a
+ * caller's confidence bucket, buckets[b, j] for position j, clamped into
+ * [0, NB)).
+ *
+ * sv_gate_update records one verify round: for each sequence with
+ * draft_lens[b] = kb > 0 (clamped to [0, K]; NULL means K), every count of b
+ * is multiplied by `decay` in [0, 1], then positions j = 0 .. min(n, kb - 1)
+ * with n = n_accepted[b] (clamped to [0, kb]) add 1 to trials, and 1 to hits
+ * when j < n. Later positions were not observed (censored) and are not
+ * recorded. A sequence without a draft is left unchanged.
+ *
+ * sv_gate_choose writes next_lens[b] in [0, K]: with p_j = hits / trials of
+ * position j's bucket (1 when it has no trials, so a cold gate drafts and
+ * learns), E(n) = 1 + sum_{i<n} prod_{j<=i} p_j, cost(0) = plain_ms and
+ * cost(n) = draft_ms + verify_base_ms + verify_slope_ms * n, it takes
+ * n* = argmax E(n) / cost(n) (ties to the longer draft); a truncation n* < K
+ * only if it beats the full draft by the factor `margin`; at least
+ * min(min_draft, K); and 0 when margin_threshold > 0, top2_margin is given
+ * and top2_margin[b] < margin_threshold (skip the draft). All arithmetic is
+ * IEEE fp64 in the order written, identical on every run.
+ * params is a host pointer read during the call. The notes' defaults: draft
+ * 196, verify 300 + 109 n, plain 303 (ms), margin 1.15, decay 0.9,
+ * min_draft 0, margin_threshold 0 (off).
+ * Errors: SV_ERR_INVALID_ARG for B < 0, NB < 1, K not in [0, SV_MAX_K],
+ * NB < K without buckets, decay outside [0, 1], negative or non-finite
+ * costs, plain_ms <= 0, margin <= 0, min_draft < 0, a non-finite
+ * margin_threshold, null required pointers, misalignment.
+ */
+typedef struct {
+    double draft_ms;         /* cost of drafting a block */
+    double verify_base_ms;   /* fixed cost of a verify forward */
+    double verify_slope_ms;  /* verify cost per draft token */
+    double plain_ms;         /* cost of a plain single-token decode step */
+    double margin;           /* a truncation must beat the full draft by this factor */
+    int32_t min_draft;       /* never draft fewer than this (0: no floor) */
+    float margin_threshold;  /* skip drafting below this top1 - top2 margin (0: off) */
+} sv_gate_params;
+
+sv_status sv_gate_update(double* hits, double* trials, int32_t B, int32_t NB, int32_t K,
+                         const int32_t* draft_lens, const int32_t* n_accepted, const int32_t* buckets,
+                         double decay, void* stream);
+
+sv_status sv_gate_choose(const double* hits, const double* trials, int32_t B, int32_t NB, int32_t K,
+                         const int32_t* buckets, const float* top2_margin, const sv_gate_params* params,
+                         int32_t* next_lens, void* stream);
+
+/*
  * sv_accept -- speculative-sampling verification.
  *
  * For i < K_b accept t_i iff u[b, i] < p_i(t_i) / q_i(t_i), i.e. with

@@ -30,9 +30,10 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_last_error", "sv_set_wait_limit",
-                                    "sv_softmax_warp", "sv_softmax_warp_filtered", "sv_softmax_warp_workspace_bytes",
-                                    "sv_status_string", "sv_verify_greedy"]
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_gate_choose", "sv_gate_update",
+                                    "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
+                                    "sv_softmax_warp_workspace_bytes", "sv_status_string", "sv_verify_greedy",
+                                    "sv_verify_greedy_margin"]
 
 
 def test_library_exports_every_declared_symbol(sv):
@@ -168,3 +169,48 @@ def test_softmax_warp_filtered_rejects_bad_arguments(sv, args, fragment):
     assert fragment in sv._lib.sv_last_error().decode()
     # B == 0 is an empty call
     assert sv._lib.sv_softmax_warp_filtered(None, 0, 0, 3, 100, None, 1, 1.0, None, None, None, None) == 0
+
+
+def test_verify_greedy_margin_rejects_bad_arguments(sv):
+    lib = sv._lib
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None, None) == 1
+    assert "null" in lib.sv_last_error().decode()
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, ODD, None) == 1
+    assert "misaligned" in lib.sv_last_error().decode()
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    assert "K = 65" in lib.sv_last_error().decode()
+    assert lib.sv_verify_greedy_margin(None, 0, 0, 4, 100, None, None, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, FAKE, -1, 5, 5, None, FAKE, None, 0.9, None), "B = -1"),
+    ((FAKE, FAKE, 2, 0, 5, None, FAKE, None, 0.9, None), "NB = 0"),
+    ((FAKE, FAKE, 2, 5, 65, None, FAKE, None, 0.9, None), "K = 65"),
+    ((FAKE, FAKE, 2, 3, 5, None, FAKE, None, 0.9, None), "position buckets"),
+    ((FAKE, FAKE, 2, 5, 5, None, FAKE, None, 1.5, None), "decay"),
+    ((FAKE, FAKE, 2, 5, 5, None, FAKE, None, float("nan"), None), "decay"),
+    ((FAKE, None, 2, 5, 5, None, FAKE, None, 0.9, None), "null"),
+    ((ODD, FAKE, 2, 5, 5, None, FAKE, None, 0.9, None), "misaligned"),
+])
+def test_gate_update_rejects_bad_arguments(sv, args, fragment):
+    assert sv._lib.sv_gate_update(*args) == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+
+
+def _params(sv, **kw):
+    P = dict(sv.GATE_DEFAULTS)
+    P.update(kw)
+    return ctypes.byref(sv.GateParams(P["draft_ms"], P["verify_base_ms"], P["verify_slope_ms"], P["plain_ms"],
+                                      P["margin"], P["min_draft"], P["margin_threshold"]))
+
+
+@pytest.mark.parametrize("kw,fragment", [
+    (dict(plain_ms=0.0), "costs"), (dict(draft_ms=-1.0), "costs"), (dict(verify_slope_ms=float("inf")), "costs"),
+    (dict(draft_ms=0.0, verify_base_ms=0.0, verify_slope_ms=0.0), "costs"), (dict(margin=0.0), "margin"),
+    (dict(min_draft=-1), "min_draft"), (dict(margin_threshold=float("nan")), "margin_threshold"),
+])
+def test_gate_choose_rejects_bad_parameters(sv, kw, fragment):
+    assert sv._lib.sv_gate_choose(FAKE, FAKE, 2, 5, 5, None, None, _params(sv, **kw), FAKE, None) == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+    assert sv._lib.sv_gate_choose(FAKE, FAKE, 2, 5, 5, None, None, None, FAKE, None) == 1
+    assert sv._lib.sv_gate_choose(None, None, 0, 5, 5, None, None, _params(sv), None, None) == 0
