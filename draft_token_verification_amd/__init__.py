@@ -22,7 +22,7 @@ import torch  # loads the HIP runtime first, so the library binds to the same on
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
            "sv_accept_logits", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
-           "sv_gate_choose", "GATE_DEFAULTS",
+           "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
@@ -69,6 +69,8 @@ def _load():
     lib.sv_gate_update.restype = c_int
     lib.sv_gate_choose.argtypes = [vp, vp, i32, i32, i32, vp, vp, ctypes.POINTER(GateParams), vp, vp]
     lib.sv_gate_choose.restype = c_int
+    lib.sv_commit.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, i32, vp]
+    lib.sv_commit.restype = c_int
     lib.sv_softmax_warp_filtered.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, vp, vp]
     lib.sv_softmax_warp_filtered.restype = c_int
     lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
@@ -293,6 +295,29 @@ def sv_gate_choose(hits: torch.Tensor, trials: torch.Tensor, K: int, buckets: Op
     return nl
 
 
+def sv_commit(seq: torch.Tensor, seq_len: torch.Tensor, done: torch.Tensor, draft_tokens: Optional[torch.Tensor],
+              n_accepted: torch.Tensor, next_token: torch.Tensor, limit: Optional[torch.Tensor] = None,
+              eos: Optional[int] = None) -> None:
+    """Append draft_tokens[b, :n_accepted[b]] and next_token[b] to seq[b] in place (int32 device tensors:
+    seq [B, cap], seq_len / done / n_accepted / next_token / limit [B], draft_tokens [B, K])."""
+    for t, name in ((seq, "seq"), (seq_len, "seq_len"), (done, "done"), (n_accepted, "n_accepted"),
+                    (next_token, "next_token")):
+        _dev(t, name)
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    B, cap = seq.shape
+    K = 0 if draft_tokens is None else draft_tokens.shape[1]
+    if draft_tokens is not None and (draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous()
+                                     or draft_tokens.shape[0] != B):
+        raise ValueError("draft_tokens must be contiguous int32 [B, K]")
+    if limit is not None and (limit.dtype != torch.int32 or tuple(limit.shape) != (B,)):
+        raise ValueError("limit must be int32 [B]")
+    with torch.cuda.device(seq.device):
+        st = _lib.sv_commit(_ptr(seq), _ptr(seq_len), _ptr(done), B, cap, _ptr(draft_tokens), K, _ptr(n_accepted),
+                            _ptr(next_token), _ptr(limit), -1 if eos is None else int(eos), _stream(seq.device))
+    _check("sv_commit", st)
+
+
 def _per_sequence(v, B: int, dtype: torch.dtype, dev: torch.device, name: str) -> Optional[torch.Tensor]:
     """None stays None; a Python number is broadcast to [B]; a tensor must be [B] (moved and cast)."""
     if v is None:
@@ -467,3 +492,6 @@ def accept(target_probs: torch.Tensor, draft_probs: torch.Tensor, draft_tokens: 
     if single:
         return int(n[0]), int(nx[0])
     return n, nx
+
+
+from .decoder import SpeculativeDecoder  # noqa: E402  (uses the functions above)

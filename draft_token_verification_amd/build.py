@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["api.hip", "greedy.hip", "accept.hip", "warp.hip", "filter.hip", "gate.hip"]
+SOURCES = ["api.hip", "greedy.hip", "accept.hip", "warp.hip", "filter.hip", "gate.hip", "commit.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

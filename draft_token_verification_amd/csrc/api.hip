@@ -230,6 +230,26 @@ sv_status sv_gate_choose(const double* hits, const double* trials, int32_t B, in
                                                (hipStream_t)stream));
 }
 
+sv_status sv_commit(int32_t* seq, int32_t* seq_len, int32_t* done, int32_t B, int32_t cap, const int32_t* draft_tokens,
+                    int32_t K, const int32_t* n_accepted, const int32_t* next_token, const int32_t* limit, int32_t eos,
+                    void* stream) {
+    const char* fn = "sv_commit";
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (cap < 1) return fail(SV_ERR_INVALID_ARG, "%s: cap = %d < 1", fn, cap);
+    if (K < 0 || K > SV_MAX_K) return fail(SV_ERR_INVALID_ARG, "%s: K = %d not in [0, %d]", fn, K, SV_MAX_K);
+    if ((int64_t)B * cap > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*cap exceeds 2^31-1", fn);
+    if (B == 0) return ok();
+    if (!seq || !seq_len || !done || !n_accepted || !next_token || (K > 0 && !draft_tokens))
+        return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
+    if (!aligned(seq, 4) || !aligned(seq_len, 4) || !aligned(done, 4) || !aligned(n_accepted, 4) ||
+        !aligned(next_token, 4) || (draft_tokens && !aligned(draft_tokens, 4)) || (limit && !aligned(limit, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    sv_status st;
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_commit(seq, seq_len, done, B, cap, draft_tokens, K, n_accepted, next_token, limit,
+                                          eos, (hipStream_t)stream));
+}
+
 sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t B, int32_t K, int64_t V,
                     const int32_t* draft_tokens, const int32_t* draft_lens, const float* uniforms, int32_t* n_accepted,
                     int32_t* next_token, void* stream) {

@@ -40,6 +40,10 @@ hipError_t launch_gate_update(double* hits, double* trials, int B, int NB, int K
 hipError_t launch_gate_choose(const double* hits, const double* trials, int B, int NB, int K, const int32_t* buckets,
                               const float* top2_margin, const GateCosts& g, int32_t* next_lens, hipStream_t stream);
 
+hipError_t launch_commit(int32_t* seq, int32_t* seq_len, int32_t* done, int B, int cap, const int32_t* tokens, int K,
+                         const int32_t* n_accepted, const int32_t* next_token, const int32_t* limit, int eos,
+                         hipStream_t stream);
+
 // Workspace the cooperative warp path needs (0: that path does not apply to V).
 size_t warp_workspace_bytes(int B, int R, int V);
 

@@ -295,6 +295,25 @@ sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, 
                            int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
                            const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* stream);
 
+/*
+ * sv_commit -- append one verify round to each sequence's token buffer on the
+ * device: draft_tokens[b, :n] followed by next_token[b], n = n_accepted[b]
+ * clamped to [0, K] (spec-verify card, "Usage": keep draft_tokens[:n_accepted],
+ * append next_token). Lets a draft/verify loop keep its buffers in HBM.
+ * seq       [B, cap] int32 token buffers; sequence b holds seq_len[b] tokens.
+ * seq_len   [B] int32, updated.
+ * done      [B] int32 flags, updated: a sequence is done once it reaches
+ *           min(limit[b], cap) tokens, or right after committing `eos` (when
+ *           eos >= 0); a done sequence is left unchanged by later calls.
+ * limit     [B] int32 length limits, or NULL (cap for every sequence).
+ * Tokens past the limit are dropped. All pointers are device memory.
+ * Errors: SV_ERR_INVALID_ARG for B < 0, cap < 1, K not in [0, SV_MAX_K],
+ * B*cap > INT32_MAX, null required pointers, misalignment.
+ */
+sv_status sv_commit(int32_t* seq, int32_t* seq_len, int32_t* done, int32_t B, int32_t cap,
+                    const int32_t* draft_tokens, int32_t K, const int32_t* n_accepted,
+                    const int32_t* next_token, const int32_t* limit, int32_t eos, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

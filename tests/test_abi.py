@@ -30,7 +30,8 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_gate_choose", "sv_gate_update",
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_commit", "sv_gate_choose",
+                                    "sv_gate_update",
                                     "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
                                     "sv_softmax_warp_workspace_bytes", "sv_status_string", "sv_verify_greedy",
                                     "sv_verify_greedy_margin"]
@@ -214,3 +215,17 @@ def test_gate_choose_rejects_bad_parameters(sv, kw, fragment):
     assert fragment in sv._lib.sv_last_error().decode()
     assert sv._lib.sv_gate_choose(FAKE, FAKE, 2, 5, 5, None, None, None, FAKE, None) == 1
     assert sv._lib.sv_gate_choose(None, None, 0, 5, 5, None, None, _params(sv), None, None) == 0
+
+
+@pytest.mark.parametrize("args,fragment", [
+    ((FAKE, FAKE, FAKE, -1, 10, FAKE, 4, FAKE, FAKE, None, -1, None), "B = -1"),
+    ((FAKE, FAKE, FAKE, 2, 0, FAKE, 4, FAKE, FAKE, None, -1, None), "cap = 0"),
+    ((FAKE, FAKE, FAKE, 2, 10, FAKE, 65, FAKE, FAKE, None, -1, None), "K = 65"),
+    ((FAKE, FAKE, None, 2, 10, FAKE, 4, FAKE, FAKE, None, -1, None), "null"),
+    ((FAKE, FAKE, FAKE, 2, 10, None, 4, FAKE, FAKE, None, -1, None), "null"),
+    ((FAKE, FAKE, FAKE, 2, 10, FAKE, 4, FAKE, FAKE, ODD, -1, None), "misaligned"),
+    ((FAKE, FAKE, FAKE, 1 << 20, 1 << 12, FAKE, 4, FAKE, FAKE, None, -1, None), "B*cap"),
+])
+def test_commit_rejects_bad_arguments(sv, args, fragment):
+    assert sv._lib.sv_commit(*args) == 1
+    assert fragment in sv._lib.sv_last_error().decode()
