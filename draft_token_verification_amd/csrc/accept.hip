@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 2;
 constexpr int kSub = 4 * kWave;     // elements per sub-block: 4 per lane
 constexpr int kMaxSeg = 7936;       // segment totals kept in LDS (62 KiB)
 
@@ -54,26 +53,41 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 // draw weights.
 
 // fp32 probability rows: w = max(0, p - q) (residual) or max(0, p) (q null).
-template <bool VEC>
+template <bool VEC, bool D>
 struct ProbSource {
+    static constexpr int kUnroll = 2;  // segments in flight per wavefront (register budget)
     const float* p;
-    const float* q;
+    const float* q;  // read only when D
     int V;
     struct Raw {
         f32x4 p, q;
     };
+    // Loads are unconditional (from a clamped address) and the value is
+    // selected afterwards, so no branch separates the loads in flight.
     __device__ Raw load(int64_t x) const {
         Raw r;
         r.q = f32x4{0.f, 0.f, 0.f, 0.f};
         if (VEC) {
             const bool in = x < V;
-            r.p = in ? load_nt((const f32x4*)(p + x)) : f32x4{0.f, 0.f, 0.f, 0.f};
-            if (q) r.q = in ? load_nt((const f32x4*)(q + x)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int64_t xs = in ? x : 0;
+            const f32x4 zero{0.f, 0.f, 0.f, 0.f};
+            const f32x4 a = load_nt((const f32x4*)(p + xs));
+            r.p = in ? a : zero;
+            if (D) {
+                const f32x4 b = load_nt((const f32x4*)(q + xs));
+                r.q = in ? b : zero;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                r.p[j] = (x + j < V) ? p[x + j] : 0.f;
-                if (q) r.q[j] = (x + j < V) ? q[x + j] : 0.f;
+                const bool in = x + j < V;
+                const int64_t xs = in ? x + j : 0;
+                const float a = p[xs];
+                r.p[j] = in ? a : 0.f;
+                if (D) {
+                    const float b = q[xs];
+                    r.q[j] = in ? b : 0.f;
+                }
             }
         }
         return r;
@@ -81,7 +95,7 @@ struct ProbSource {
     __device__ void weights(const Raw& r, double w[4]) const {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            double d = q ? (double)r.p[j] - (double)r.q[j] : (double)r.p[j];
+            double d = D ? (double)r.p[j] - (double)r.q[j] : (double)r.p[j];
             w[j] = d > 0.0 ? d : 0.0;
         }
     }
@@ -132,11 +146,13 @@ __device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) 
     return (double)ex2(fmaf(z, c, -st.m)) * st.inv;
 }
 
-// Logits rows with their statistics: w = max(0, p - q) (residual) or max(0, p).
-template <bool BF16, bool VEC>
+// Logits rows with their statistics: w = max(0, p - q) (residual, D) or
+// max(0, p) (bonus or zero-residual fallback).
+template <bool BF16, bool VEC, bool D>
 struct LogitSource {
+    static constexpr int kUnroll = 2;  // segments in flight per wavefront (register budget)
     const void* zt;
-    const void* zd;  // null: bonus row
+    const void* zd;  // read only when D
     int V;
     float c;
     RowStats st, sd;
@@ -146,16 +162,30 @@ struct LogitSource {
     };
     __device__ Raw load(int64_t x) const {
         Raw r;
+        r.d = L::neg_inf();
         if (VEC) {
             const bool in = x < V;
-            r.t = in ? L::load(zt, x) : L::neg_inf();
-            r.d = (zd && in) ? L::load(zd, x) : L::neg_inf();
+            const int64_t xs = in ? x : 0;
+            const typename L::Raw a = L::load(zt, xs);
+            r.t = in ? a : L::neg_inf();
+            if (D) {
+                const typename L::Raw b = L::load(zd, xs);
+                r.d = in ? b : L::neg_inf();
+            }
         } else {
             float a[4], d[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                a[j] = (x + j < V) ? L::at(zt, x + j) : -INFINITY;
-                d[j] = (zd && x + j < V) ? L::at(zd, x + j) : -INFINITY;
+                const bool in = x + j < V;
+                const int64_t xs = in ? x + j : 0;
+                const float va = L::at(zt, xs);
+                a[j] = in ? va : -INFINITY;
+                if (D) {
+                    const float vd = L::at(zd, xs);
+                    d[j] = in ? vd : -INFINITY;
+                } else {
+                    d[j] = -INFINITY;
+                }
             }
             r.t = L::pack(a);
             r.d = L::pack(d);
@@ -172,7 +202,7 @@ struct LogitSource {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const double p = prob_of(a[j], c, st);
-            const double v = zd ? p - prob_of(d[j], c, sd) : p;
+            const double v = D ? p - prob_of(d[j], c, sd) : p;
             w[j] = v > 0.0 ? v : 0.0;
         }
     }
@@ -187,26 +217,26 @@ template <class Src>
 __device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t L = (int64_t)m * kSub;
-    for (int s0 = wave; s0 < nseg; s0 += kWaves * kUnroll) {
-        double acc[kUnroll];
+    for (int s0 = wave; s0 < nseg; s0 += kWaves * Src::kUnroll) {
+        double acc[Src::kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc[u] = 0.0;
+        for (int u = 0; u < Src::kUnroll; ++u) acc[u] = 0.0;
         for (int k = 0; k < m; ++k) {
-            typename Src::Raw raw[kUnroll];
+            typename Src::Raw raw[Src::kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < Src::kUnroll; ++u) {
                 const int64_t x = (int64_t)(s0 + u * kWaves) * L + (int64_t)k * kSub + 4 * lane;
                 raw[u] = src.load(x);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < Src::kUnroll; ++u) {
                 double w[4];
                 src.weights(raw[u], w);
                 acc[u] += ((w[0] + w[1]) + w[2]) + w[3];
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < Src::kUnroll; ++u) {
             const double tot = wave_sum_d(acc[u]);
             const int s = s0 + u * kWaves;
             if (lane == 0 && s < nseg) seg[s] = tot;
@@ -287,6 +317,21 @@ __device__ int draw(const Src& src, int m, int nseg, const double* seg, float u,
     return locate(src, m, nseg, seg, (double)u * S);
 }
 
+// The final draw of a sequence: from the residual source `res` when
+// `residual` (falling back to `bon`, the same target row alone, if the
+// residual has no mass), else from the bonus source `bon`. Every lane of the
+// workgroup calls it; the id is valid in lane 0.
+template <class Res, class Bon>
+__device__ int final_draw(const Res& res, const Bon& bon, bool residual, int m, int nseg, double* seg, float u) {
+    if (residual) {
+        const double S = segment_totals(res, m, nseg, seg);
+        if (S > 0.0) return draw(res, m, nseg, seg, u, S);
+        __syncthreads();  // p_n == q_n: no residual mass, draw from max(0, p_n)
+    }
+    const double S = segment_totals(bon, m, nseg, seg);
+    return draw(bon, m, nseg, seg, u, S);
+}
+
 // ---- accept_kernel: probability rows ----------------------------------------
 
 template <bool VEC>
@@ -325,23 +370,12 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(const float* __restric
     const int n = s_n;
 
     // 2-3. the draw from the row (pair) it needs
-    ProbSource<VEC> src;
-    src.V = V;
-    if (n < kb) {
-        src.p = p + ((int64_t)b * (K + 1) + n) * Vl;
-        src.q = q + ((int64_t)b * K + n) * Vl;
-    } else {
-        src.p = p + ((int64_t)b * (K + 1) + kb) * Vl;
-        src.q = nullptr;
-    }
-    double S = segment_totals(src, m, nseg, seg);
-    if (!(S > 0.0) && src.q != nullptr) {
-        // p_n == q_n leaves no residual mass: draw from max(0, p_n) instead
-        __syncthreads();
-        src.q = nullptr;
-        S = segment_totals(src, m, nseg, seg);
-    }
-    const int next = draw(src, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb], S);
+    const bool residual = n < kb;
+    const int prow = residual ? n : kb;
+    ProbSource<VEC, true> res{p + ((int64_t)b * (K + 1) + prow) * Vl, residual ? q + ((int64_t)b * K + n) * Vl : nullptr,
+                              V};
+    ProbSource<VEC, false> bon{p + ((int64_t)b * (K + 1) + prow) * Vl, nullptr, V};
+    const int next = final_draw(res, bon, residual, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb]);
     if (threadIdx.x == 0) {
         n_accepted[b] = n;
         next_token[b] = next;
@@ -370,6 +404,26 @@ __device__ __forceinline__ void online_add4(const float z[4], float c, Online& o
     o.s += (double)part;
 }
 
+// N elements at once: one max, at most one rescale, one fp32 partial sum and
+// one binary64 add per N elements (a few VALU operations per element; the
+// statistics pass is bound by these when a workgroup works alone).
+template <int N>
+__device__ __forceinline__ void online_addn(const float* z, float c, Online& o) {
+    float zm = z[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) zm = fmaxf(zm, z[k]);
+    const float ym = zm * c;
+    if (ym > o.m) {
+        o.s = (o.m == -INFINITY) ? 0.0 : o.s * (double)ex2(o.m - ym);
+        o.m = ym;
+    }
+    if (o.m == -INFINITY) return;  // all -inf so far: nothing to add (and no -inf - -inf)
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) part += ex2(fmaf(z[k], c, -o.m));
+    o.s += (double)part;
+}
+
 __device__ __forceinline__ void online_merge(Online& a, float m2, double s2) {
     const float mm = fmaxf(a.m, m2);
     const double x = (a.m == -INFINITY) ? 0.0 : a.s * (double)ex2(a.m - mm);
@@ -395,41 +449,53 @@ struct StatsLds {
     double s[2][kWaves];
 };
 
-// Statistics of target row zt and (unless zd is null) draft row zd in one
-// pass, merged over the workgroup; every lane gets them. Contains barriers.
-template <bool BF16, bool VEC>
-__device__ void row_stats(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
-                          RowStats& sd) {
+// Statistics of target row zt and (D) draft row zd in one pass, merged over
+// the workgroup; every lane gets them. Contains barriers.
+template <bool BF16, bool VEC, bool D>
+__device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
+                               RowStats& sd) {
     using L = Logit4<BF16>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     Online ot{-INFINITY, 0.0}, od{-INFINITY, 0.0};
     if (VEC) {
-        constexpr int U = 4;
+        // Software-pipelined: the next U quads of the row(s) are in flight while
+        // the current ones are consumed.
+        constexpr int U = D ? 4 : 8;
+        constexpr int kStep = U * kThreads;
         const int nq = V / 4;
-        int j = tid;
-        for (; j + (U - 1) * kThreads < nq; j += U * kThreads) {
-            typename L::Raw rt[U], rd[U];
+        const int nfull = nq / kStep;  // whole steps
+        typename L::Raw ct[U], cd[U], nt[U], nd[U];
+        auto fetch = [&](int base, typename L::Raw* t, typename L::Raw* d) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                rt[u] = L::load(zt, 4 * (int64_t)(j + u * kThreads));
-                rd[u] = zd ? L::load(zd, 4 * (int64_t)(j + u * kThreads)) : L::neg_inf();
+                const int64_t x = 4 * (int64_t)(base + u * kThreads + tid);
+                t[u] = L::load(zt, x);
+                if (D) d[u] = L::load(zd, x);
             }
+        };
+        if (nfull > 0) fetch(0, nt, nd);
+        for (int it = 0; it < nfull; ++it) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float a[4];
-                L::unpack(rt[u], a);
-                online_add4(a, c, ot);
-                if (zd) {
-                    L::unpack(rd[u], a);
-                    online_add4(a, c, od);
-                }
+                ct[u] = nt[u];
+                if (D) cd[u] = nd[u];
+            }
+            if (it + 1 < nfull) fetch((it + 1) * kStep, nt, nd);
+            float a[4 * U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) L::unpack(ct[u], a + 4 * u);
+            online_addn<4 * U>(a, c, ot);
+            if (D) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) L::unpack(cd[u], a + 4 * u);
+                online_addn<4 * U>(a, c, od);
             }
         }
-        for (; j < nq; j += kThreads) {
+        for (int j = nfull * kStep + tid; j < nq; j += kThreads) {
             float a[4];
             L::unpack(L::load(zt, 4 * (int64_t)j), a);
             online_add4(a, c, ot);
-            if (zd) {
+            if (D) {
                 L::unpack(L::load(zd, 4 * (int64_t)j), a);
                 online_add4(a, c, od);
             }
@@ -438,14 +504,14 @@ __device__ void row_stats(const void* zt, const void* zd, int V, float c, StatsL
         for (int x = tid; x < V; x += kThreads) {
             const float a[4] = {L::at(zt, x), -INFINITY, -INFINITY, -INFINITY};
             online_add4(a, c, ot);
-            if (zd) {
+            if (D) {
                 const float d[4] = {L::at(zd, x), -INFINITY, -INFINITY, -INFINITY};
                 online_add4(d, c, od);
             }
         }
     }
     wave_online(ot);
-    if (zd) wave_online(od);
+    if (D) wave_online(od);
     __syncthreads();  // the LDS slots may still be read from the previous call
     if (lane == 0) {
         lds->m[0][wave] = ot.m;
@@ -457,11 +523,21 @@ __device__ void row_stats(const void* zt, const void* zd, int V, float c, StatsL
     Online rt{lane < kWaves ? lds->m[0][lane] : -INFINITY, lane < kWaves ? lds->s[0][lane] : 0.0};
     wave_online(rt);
     st = RowStats{rt.m, 1.0 / rt.s};
-    if (zd) {
+    if (D) {
         Online rd{lane < kWaves ? lds->m[1][lane] : -INFINITY, lane < kWaves ? lds->s[1][lane] : 0.0};
         wave_online(rd);
         sd = RowStats{rd.m, 1.0 / rd.s};
     }
+}
+
+// zd == nullptr: target row only (sd is left as it was).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void row_stats(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
+                                          RowStats& sd) {
+    if (zd)
+        row_stats_pass<BF16, VEC, true>(zt, zd, V, c, lds, st, sd);
+    else
+        row_stats_pass<BF16, VEC, false>(zt, nullptr, V, c, lds, st, sd);
 }
 
 template <bool BF16, bool VEC>
@@ -505,28 +581,13 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
     }
 
     // 2-3. the draw
-    LogitSource<BF16, VEC> src;
-    src.V = V;
-    src.c = c;
-    if (n < kb) {
-        src.zt = tbase + (size_t)n * row_bytes;
-        src.zd = dbase + (size_t)n * row_bytes;
-        if (!have) row_stats<BF16, VEC>(src.zt, src.zd, V, c, &lds, st, sd);
-    } else {
-        src.zt = tbase + (size_t)kb * row_bytes;
-        src.zd = nullptr;
-        row_stats<BF16, VEC>(src.zt, nullptr, V, c, &lds, st, sd);
-    }
-    src.st = st;
-    src.sd = sd;
-    double S = segment_totals(src, m, nseg, seg);
-    if (!(S > 0.0) && src.zd != nullptr) {
-        // p_n == q_n leaves no residual mass: draw from max(0, p_n) instead
-        __syncthreads();
-        src.zd = nullptr;
-        S = segment_totals(src, m, nseg, seg);
-    }
-    const int next = draw(src, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb], S);
+    const bool residual = n < kb;
+    const void* zt_row = tbase + (size_t)(residual ? n : kb) * row_bytes;
+    const void* zd_row = residual ? (const void*)(dbase + (size_t)n * row_bytes) : nullptr;
+    if (!(residual && have)) row_stats<BF16, VEC>(zt_row, zd_row, V, c, &lds, st, sd);
+    const LogitSource<BF16, VEC, true> res{zt_row, zd_row, V, c, st, sd};
+    const LogitSource<BF16, VEC, false> bon{zt_row, nullptr, V, c, st, sd};
+    const int next = final_draw(res, bon, residual, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb]);
     if (threadIdx.x == 0) {
         n_accepted[b] = n;
         next_token[b] = next;
