@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
-           "sv_accept_logits", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
+           "sv_accept_logits", "sv_accept_logits_workspace_bytes", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
            "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
@@ -81,7 +81,10 @@ def _load():
     lib.sv_verify_greedy.restype = c_int
     lib.sv_accept.argtypes = [vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.sv_accept.restype = c_int
-    lib.sv_accept_logits.argtypes = [vp, vp, c_int, i32, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp]
+    lib.sv_accept_logits.argtypes = [vp, vp, c_int, i32, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+    lib.sv_accept_logits_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_accept_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_accept_logits.restype = c_int
     if lib.sv_abi_version() != 1:
         raise ImportError("libspecverify ABI version mismatch")
@@ -417,11 +420,19 @@ def sv_accept(target_probs: torch.Tensor, draft_probs: Optional[torch.Tensor], d
     return n, nx
 
 
+def sv_accept_logits_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(_lib.sv_accept_logits_workspace_bytes(B, K, V))
+
+
 def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
                      draft_tokens: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: float = 1.0,
                      draft_lens: Optional[torch.Tensor] = None,
-                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Speculative-sampling verify from logits (fp32 or bf16) -> (n_accepted[B], next_token[B]).
+
+    ``workspace`` (uint8 device tensor) defaults to one kept per device and stream, sized by
+    sv_accept_logits_workspace_bytes; a zero-size one selects one workgroup per sequence.
 
     target_logits [B, K+1, V], draft_logits [B, K, V] (same dtype), draft_tokens [B, K],
     uniforms [B, K+1] fp32; the rows are warped with temperature T on the fly.
@@ -450,9 +461,16 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
     with torch.cuda.device(dev):
+        stream = _stream(dev)
+        if workspace is None:
+            need = _lib.sv_accept_logits_workspace_bytes(B, K, V) if B > 0 else 0
+            workspace = _workspace(need, dev, stream.value)
+        elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the logits' device")
+        ws_bytes = 0 if workspace is None else workspace.numel()
         st = _lib.sv_accept_logits(_ptr(target_logits), _ptr(draft_logits if K > 0 else None), code, B, K, V,
                                    float(temperature), _ptr(toks), _ptr(lens), _ptr(uniforms), _ptr(n), _ptr(nx),
-                                   _stream(dev))
+                                   _ptr(workspace), ws_bytes, stream)
     _check("sv_accept_logits", st)
     return n, nx
 

@@ -210,14 +210,14 @@ struct LogitSource {
 
 // ---- the draw ---------------------------------------------------------------
 
-// All wavefronts write seg[s] = sum of the weights of segment s
+// All NW wavefronts write seg[s] = sum of the weights of segment s
 // (L = m * kSub elements). Returns the row's total weight S, identical in
 // every lane (each wavefront sums seg[] in the same order).
-template <class Src>
+template <int NW, class Src>
 __device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t L = (int64_t)m * kSub;
-    for (int s0 = wave; s0 < nseg; s0 += kWaves * Src::kUnroll) {
+    for (int s0 = wave; s0 < nseg; s0 += NW * Src::kUnroll) {
         double acc[Src::kUnroll];
 #pragma unroll
         for (int u = 0; u < Src::kUnroll; ++u) acc[u] = 0.0;
@@ -225,7 +225,7 @@ __device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
             typename Src::Raw raw[Src::kUnroll];
 #pragma unroll
             for (int u = 0; u < Src::kUnroll; ++u) {
-                const int64_t x = (int64_t)(s0 + u * kWaves) * L + (int64_t)k * kSub + 4 * lane;
+                const int64_t x = (int64_t)(s0 + u * NW) * L + (int64_t)k * kSub + 4 * lane;
                 raw[u] = src.load(x);
             }
 #pragma unroll
@@ -238,7 +238,7 @@ __device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
 #pragma unroll
         for (int u = 0; u < Src::kUnroll; ++u) {
             const double tot = wave_sum_d(acc[u]);
-            const int s = s0 + u * kWaves;
+            const int s = s0 + u * NW;
             if (lane == 0 && s < nseg) seg[s] = tot;
         }
     }
@@ -324,11 +324,11 @@ __device__ int draw(const Src& src, int m, int nseg, const double* seg, float u,
 template <class Res, class Bon>
 __device__ int final_draw(const Res& res, const Bon& bon, bool residual, int m, int nseg, double* seg, float u) {
     if (residual) {
-        const double S = segment_totals(res, m, nseg, seg);
+        const double S = segment_totals<kWaves>(res, m, nseg, seg);
         if (S > 0.0) return draw(res, m, nseg, seg, u, S);
         __syncthreads();  // p_n == q_n: no residual mass, draw from max(0, p_n)
     }
-    const double S = segment_totals(bon, m, nseg, seg);
+    const double S = segment_totals<kWaves>(bon, m, nseg, seg);
     return draw(bon, m, nseg, seg, u, S);
 }
 
@@ -449,26 +449,28 @@ struct StatsLds {
     double s[2][kWaves];
 };
 
-// Statistics of target row zt and (D) draft row zd in one pass, merged over
-// the workgroup; every lane gets them. Contains barriers.
-template <bool BF16, bool VEC, bool D>
-__device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
-                               RowStats& sd) {
+// Online (max, sum) of elements [x0, x0 + len) of target row zt and (D) draft
+// row zd, merged over the NW wavefronts of the workgroup: rt and rd are
+// uniform. For VEC, x0 and len are multiples of 4. Contains barriers.
+template <bool BF16, bool VEC, bool D, int NW, int UD = 4>
+__device__ void span_stats(const void* zt, const void* zd, int64_t x0, int len, float c, StatsLds* lds, Online& rt,
+                           Online& rd) {
     using L = Logit4<BF16>;
+    constexpr int NT = NW * kWave;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     Online ot{-INFINITY, 0.0}, od{-INFINITY, 0.0};
     if (VEC) {
         // Software-pipelined: the next U quads of the row(s) are in flight while
         // the current ones are consumed.
-        constexpr int U = D ? 4 : 8;
-        constexpr int kStep = U * kThreads;
-        const int nq = V / 4;
+        constexpr int U = D ? UD : 2 * UD;
+        constexpr int kStep = U * NT;
+        const int nq = len / 4;
         const int nfull = nq / kStep;  // whole steps
         typename L::Raw ct[U], cd[U], nt[U], nd[U];
         auto fetch = [&](int base, typename L::Raw* t, typename L::Raw* d) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t x = 4 * (int64_t)(base + u * kThreads + tid);
+                const int64_t x = x0 + 4 * (int64_t)(base + u * NT + tid);
                 t[u] = L::load(zt, x);
                 if (D) d[u] = L::load(zd, x);
             }
@@ -491,21 +493,21 @@ __device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, S
                 online_addn<4 * U>(a, c, od);
             }
         }
-        for (int j = nfull * kStep + tid; j < nq; j += kThreads) {
+        for (int j = nfull * kStep + tid; j < nq; j += NT) {
             float a[4];
-            L::unpack(L::load(zt, 4 * (int64_t)j), a);
+            L::unpack(L::load(zt, x0 + 4 * (int64_t)j), a);
             online_add4(a, c, ot);
             if (D) {
-                L::unpack(L::load(zd, 4 * (int64_t)j), a);
+                L::unpack(L::load(zd, x0 + 4 * (int64_t)j), a);
                 online_add4(a, c, od);
             }
         }
     } else {
-        for (int x = tid; x < V; x += kThreads) {
-            const float a[4] = {L::at(zt, x), -INFINITY, -INFINITY, -INFINITY};
+        for (int x = tid; x < len; x += NT) {
+            const float a[4] = {L::at(zt, x0 + x), -INFINITY, -INFINITY, -INFINITY};
             online_add4(a, c, ot);
             if (D) {
-                const float d[4] = {L::at(zd, x), -INFINITY, -INFINITY, -INFINITY};
+                const float d[4] = {L::at(zd, x0 + x), -INFINITY, -INFINITY, -INFINITY};
                 online_add4(d, c, od);
             }
         }
@@ -520,14 +522,23 @@ __device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, S
         lds->s[1][wave] = od.s;
     }
     __syncthreads();
-    Online rt{lane < kWaves ? lds->m[0][lane] : -INFINITY, lane < kWaves ? lds->s[0][lane] : 0.0};
+    rt = Online{lane < NW ? lds->m[0][lane] : -INFINITY, lane < NW ? lds->s[0][lane] : 0.0};
     wave_online(rt);
-    st = RowStats{rt.m, 1.0 / rt.s};
     if (D) {
-        Online rd{lane < kWaves ? lds->m[1][lane] : -INFINITY, lane < kWaves ? lds->s[1][lane] : 0.0};
+        rd = Online{lane < NW ? lds->m[1][lane] : -INFINITY, lane < NW ? lds->s[1][lane] : 0.0};
         wave_online(rd);
-        sd = RowStats{rd.m, 1.0 / rd.s};
     }
+}
+
+// Statistics of whole rows (target, and draft when D), merged over the
+// 1024-lane workgroup; every lane gets them. Contains barriers.
+template <bool BF16, bool VEC, bool D>
+__device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
+                               RowStats& sd) {
+    Online rt, rd;
+    span_stats<BF16, VEC, D, kWaves>(zt, zd, 0, V, c, lds, rt, rd);
+    st = RowStats{rt.m, 1.0 / rt.s};
+    if (D) sd = RowStats{rd.m, 1.0 / rd.s};
 }
 
 // zd == nullptr: target row only (sd is left as it was).
@@ -594,6 +605,243 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
     }
 }
 
+// ---- accept_logits_sliced_kernel: each sequence over G workgroups ----------
+//
+// The same procedure as accept_logits_kernel, with the rows of a sequence
+// split into G slices of Ls elements; workgroup (b, g) of 256 lanes owns
+// slice g of every row of sequence b. At each examined position the G
+// workgroups publish their slices' (max, sum) of the target and draft rows
+// into sentinel-filled slots of the caller's workspace and merge all G in a
+// fixed order, so every slice takes the same accept decision; for the draw
+// each publishes its slice's total weight, all find the slice holding u * S,
+// and that one locates the id inside it. A long chain of accepted positions
+// thus runs on G compute units instead of one. Every wait is bounded: a
+// workgroup that gives up recomputes the missing slices' values itself with
+// the same code and lane mapping, so results are bitwise identical either way.
+
+constexpr int kSliceWaves = 4;
+constexpr int kSliceThreads = kSliceWaves * kWave;
+constexpr int kMaxSlices = 8;
+constexpr unsigned long long kEmptySlot = ~0ull;  // a NaN pattern: never a published value
+
+__device__ __forceinline__ unsigned long long pack_online(const Online& o) {
+    return ((unsigned long long)__float_as_uint((float)o.s) << 32) | __float_as_uint(o.m);
+}
+
+__device__ __forceinline__ void merge_packed(Online& r, unsigned long long v) {
+    online_merge(r, __uint_as_float((unsigned)v), (double)__uint_as_float((unsigned)(v >> 32)));
+}
+
+// Wavefront 0 polls words set[0 .. nw) (bounded) and copies them to LDS;
+// returns whether all were published (uniform after the barrier).
+__device__ __forceinline__ bool gather_words(const unsigned long long* set, int nw, int wait_limit,
+                                             unsigned long long* s_words, int* s_ready) {
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        bool ready = false;
+        for (int tries = 0; tries <= wait_limit; ++tries) {
+            bool mine = true;
+            for (int k = tid; k < nw; k += kWave) {
+                const unsigned long long v = __hip_atomic_load(set + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == kEmptySlot)
+                    mine = false;
+                else
+                    s_words[k] = v;
+            }
+            if (__ballot(!mine) == 0) {
+                ready = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (tid == 0) *s_ready = ready;
+    }
+    __syncthreads();
+    return *s_ready;
+}
+
+__device__ __forceinline__ void publish_word(unsigned long long* slot, unsigned long long v) {
+    if (threadIdx.x == 0) __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Row statistics of the examined rows (target, and draft when D) from the G
+// slices: publish this slice's partials into set[2g], set[2g + 1], gather all,
+// merge in slice order. Called by the whole workgroup.
+template <bool BF16, bool VEC, bool D>
+__device__ void sliced_row_stats(unsigned long long* set, int G, int g, int Ls, int V, const void* zt, const void* zd,
+                                 float c, StatsLds* lds, int wait_limit, unsigned long long* s_words, int* s_ready,
+                                 RowStats& st, RowStats& sd) {
+    const int64_t x0 = (int64_t)g * Ls;
+    Online a, d;
+    span_stats<BF16, VEC, D, kSliceWaves, BF16 ? 2 : 1>(zt, zd, x0, (int)min((int64_t)Ls, (int64_t)V - x0), c, lds, a, d);
+    publish_word(set + 2 * g, pack_online(a));
+    publish_word(set + 2 * g + 1, D ? pack_online(d) : 0ull);  // both words: the gather waits for all 2G
+    if (!gather_words(set, 2 * G, wait_limit, s_words, s_ready)) {
+        // bounded wait ran out: every slice's partials, recomputed here alike
+        for (int k = 0; k < G; ++k) {
+            const int64_t xk = (int64_t)k * Ls;
+            Online ak, dk;
+            span_stats<BF16, VEC, D, kSliceWaves, BF16 ? 2 : 1>(zt, zd, xk, (int)min((int64_t)Ls, (int64_t)V - xk), c, lds, ak,
+                                                     dk);
+            if (threadIdx.x == 0) {
+                s_words[2 * k] = pack_online(ak);
+                s_words[2 * k + 1] = D ? pack_online(dk) : 0ull;
+            }
+        }
+        __syncthreads();
+    }
+    Online rt{-INFINITY, 0.0}, rd{-INFINITY, 0.0};
+    for (int k = 0; k < G; ++k) {
+        merge_packed(rt, s_words[2 * k]);
+        if (D) merge_packed(rd, s_words[2 * k + 1]);
+    }
+    st = RowStats{rt.m, 1.0 / rt.s};
+    if (D) sd = RowStats{rd.m, 1.0 / rd.s};
+    __syncthreads();  // s_words is reused by the next exchange
+}
+
+// Slice totals of the draw weights: this slice's table into seg (its total
+// published into set[g]); all G totals into s_tot, in slice order.
+template <class Src, class MakeSrc>
+__device__ void sliced_totals(unsigned long long* set, int G, int g, int m, int nseg_max, int Ls, int V, double* seg,
+                              int wait_limit, unsigned long long* s_words, int* s_ready, double* s_tot,
+                              MakeSrc make) {
+    const int64_t L = (int64_t)m * kSub;
+    auto nseg_of = [&](int k) {
+        const int64_t len = min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls);
+        return (int)((len + L - 1) / L);
+    };
+    const Src mine = make(g);
+    const double Sg = segment_totals<kSliceWaves>(mine, m, nseg_of(g), seg);
+    publish_word(set + g, (unsigned long long)__double_as_longlong(Sg));
+    if (gather_words(set, G, wait_limit, s_words, s_ready)) {
+        if (threadIdx.x < G) s_tot[threadIdx.x] = __longlong_as_double((long long)s_words[threadIdx.x]);
+    } else {
+        double* scratch = seg + nseg_max;  // keep this slice's table intact
+        for (int k = 0; k < G; ++k) {
+            const double Sk = segment_totals<kSliceWaves>(make(k), m, nseg_of(k), scratch);
+            if (threadIdx.x == 0) s_tot[k] = Sk;
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void accept_logits_sliced_kernel(
+    const void* __restrict__ zt, const void* __restrict__ zd, int K, int V, int G, int Ls, int m, int nseg_max, float c,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens, const float* __restrict__ uniforms,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token, unsigned long long* __restrict__ slots,
+    int wait_limit) {
+    extern __shared__ double seg[];  // 2 * nseg_max: this slice's table, then a scratch table
+    __shared__ StatsLds lds;
+    __shared__ unsigned long long s_words[2 * kMaxSlices];
+    __shared__ double s_tot[kMaxSlices];
+    __shared__ int s_ready;
+    using L = Logit4<BF16>;
+    constexpr int kElem = BF16 ? 2 : 4;
+    const int b = blockIdx.x / G, g = blockIdx.x - b * G;
+    const int kb = clamp_len(lens, b, K);
+    const size_t row_bytes = (size_t)V * kElem;
+    const char* tbase = (const char*)zt + (size_t)b * (size_t)(K + 1) * row_bytes;
+    const char* dbase = (const char*)zd + (size_t)b * (size_t)K * row_bytes;
+    const int64_t x0 = (int64_t)g * Ls;
+    const int len = (int)min((int64_t)Ls, (int64_t)V - x0);
+    unsigned long long* my = slots + (size_t)b * (size_t)((K + 1) * 2 * G + 2 * G);
+    unsigned long long* draw_sets = my + (size_t)(K + 1) * 2 * G;
+
+    // 1. positions in order; stop at the first rejection
+    int n = kb;
+    bool have = false;
+    RowStats st{0.f, 0.0}, sd{0.f, 0.0};
+    for (int i = 0; i < kb; ++i) {
+        const int t = tokens[(int64_t)b * K + i];
+        if (t < 0 || t >= V) {  // out-of-range draft token: rejected, never dereferenced
+            n = i;
+            break;
+        }
+        const void* tr = tbase + (size_t)i * row_bytes;
+        const void* dr = dbase + (size_t)i * row_bytes;
+        sliced_row_stats<BF16, VEC, true>(my + (size_t)i * 2 * G, G, g, Ls, V, tr, dr, c, &lds, wait_limit, s_words,
+                                          &s_ready, st, sd);
+        const double pt = prob_of(L::at(tr, t), c, st);
+        const double qt = prob_of(L::at(dr, t), c, sd);
+        const double u = uniforms[(int64_t)b * (K + 1) + i];
+        if (!(u * qt < pt)) {
+            n = i;
+            have = true;
+            break;
+        }
+    }
+
+    // 2-3. the draw, slice by slice
+    const bool residual = n < kb;
+    const int pos = residual ? n : kb;
+    const char* zt_row = tbase + (size_t)pos * row_bytes;
+    const char* zd_row = residual ? dbase + (size_t)n * row_bytes : nullptr;
+    if (!(residual && have)) {
+        if (residual)
+            sliced_row_stats<BF16, VEC, true>(my + (size_t)pos * 2 * G, G, g, Ls, V, zt_row, zd_row, c, &lds,
+                                              wait_limit, s_words, &s_ready, st, sd);
+        else
+            sliced_row_stats<BF16, VEC, false>(my + (size_t)pos * 2 * G, G, g, Ls, V, zt_row, nullptr, c, &lds,
+                                               wait_limit, s_words, &s_ready, st, sd);
+    }
+    using Res = LogitSource<BF16, VEC, true>;
+    using Bon = LogitSource<BF16, VEC, false>;
+    auto slice_len = [&](int k) { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); };
+    auto make_res = [&](int k) {
+        return Res{zt_row + (size_t)k * Ls * kElem, zd_row + (size_t)k * Ls * kElem, slice_len(k), c, st, sd};
+    };
+    auto make_bon = [&](int k) { return Bon{zt_row + (size_t)k * Ls * kElem, nullptr, slice_len(k), c, st, sd}; };
+    bool use_bon = !residual;
+    if (residual)
+        sliced_totals<Res>(draw_sets, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot, make_res);
+    else
+        sliced_totals<Bon>(draw_sets, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot, make_bon);
+    double S = 0.0;
+    for (int k = 0; k < G; ++k) S += s_tot[k];
+    if (residual && !(S > 0.0)) {
+        // p_n == q_n: no residual mass, draw from max(0, p_n)
+        use_bon = true;
+        sliced_totals<Bon>(draw_sets + G, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot,
+                           make_bon);
+        S = 0.0;
+        for (int k = 0; k < G; ++k) S += s_tot[k];
+    }
+    if (g == 0 && threadIdx.x == 0) {
+        n_accepted[b] = n;
+        if (!(S > 0.0)) next_token[b] = -1;
+    }
+    if (!(S > 0.0)) return;
+    // the slice holding u * S: the first with positive total whose running sum
+    // exceeds it; if rounding leaves none, the last with positive total
+    const double thr = (double)uniforms[(int64_t)b * (K + 1) + kb] * S;
+    int ks = -1, klast = -1;
+    double pre = 0.0, pre_ks = 0.0;
+    for (int k = 0; k < G; ++k) {
+        if (s_tot[k] > 0.0) {
+            klast = k;
+            if (ks < 0 && pre + s_tot[k] > thr) {
+                ks = k;
+                pre_ks = pre;
+            }
+        }
+        pre += s_tot[k];
+    }
+    const double thr_local = ks < 0 ? INFINITY : thr - pre_ks;
+    if (ks < 0) ks = klast;
+    if (g != ks || threadIdx.x >= kWave) return;
+    const int nseg = (len + (int)((int64_t)m * kSub) - 1) / (int)((int64_t)m * kSub);
+    const int x = use_bon ? locate(make_bon(g), m, nseg, seg, thr_local) : locate(make_res(g), m, nseg, seg, thr_local);
+    if (threadIdx.x == 0) next_token[b] = x < 0 ? -1 : (int)(x0 + x);
+}
+
+__global__ void fill_empty(unsigned long long* __restrict__ p, int64_t n) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < n) p[i] = kEmptySlot;
+}
+
 // m sub-blocks per segment keep the segment count within the LDS table
 void segment_shape(int V, int& m, int& nseg) {
     const int64_t per_seg_min = ((int64_t)V + kMaxSeg - 1) / kMaxSeg;
@@ -620,15 +868,72 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
     return hipGetLastError();
 }
 
+namespace {
+
+// Slices of the sliced fused verify: at most 8, B * G <= 4096 workgroups of
+// 256 lanes (twice what the chip holds at once; the dispatch order keeps a
+// sequence's slices together), each slice at least 32768 elements (shorter
+// slices spend more on the exchanges than they save); Ls is a multiple of 1024
+// elements and every slice is non-empty. Measured on MI355X at B = 512,
+// K = 16, V = 256000 (G = 8): 0.58 ms, against 0.63 (G = 4) and 0.79 (G = 2).
+void slice_shape(int B, int V, int& G, int& Ls) {
+    int g = 4096 / (B > 0 ? B : 1);
+    g = g < 1 ? 1 : (g > kMaxSlices ? kMaxSlices : g);
+    const int gv = (V + 32767) / 32768;
+    g = g < gv ? g : (gv > 1 ? gv : 1);
+    int64_t ls = ((int64_t)V + g - 1) / g;
+    ls = (ls + 1023) / 1024 * 1024;
+    G = (int)(((int64_t)V + ls - 1) / ls);
+    Ls = (int)ls;
+}
+
+}  // namespace
+
+size_t accept_logits_workspace_bytes(int B, int K, int V) {
+    int G, Ls;
+    slice_shape(B, V, G, Ls);
+    if (G < 2) return 0;
+    return (size_t)B * ((size_t)(K + 1) * 2 * G + 2 * (size_t)G) * sizeof(unsigned long long);
+}
+
 hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
                                 const int32_t* tokens, const int32_t* lens, const float* uniforms,
-                                int32_t* n_accepted, int32_t* next_token, hipStream_t stream) {
-    int m, nseg;
-    segment_shape(V, m, nseg);
-    const size_t lds = (size_t)nseg * sizeof(double);
+                                int32_t* n_accepted, int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
     const float c = 1.4426950408889634f / temperature;
     const uintptr_t al = bf16 ? 8 : 16;
     const bool vec = (V % 4 == 0) && ((uintptr_t)zt % al == 0) && ((uintptr_t)zd % al == 0);
+    const size_t need = accept_logits_workspace_bytes(B, K, V);
+    if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
+        int G, Ls, m, nseg;
+        slice_shape(B, V, G, Ls);
+        segment_shape(Ls, m, nseg);
+        const int64_t words = (int64_t)(need / sizeof(unsigned long long));
+        unsigned long long* slots = (unsigned long long*)workspace;
+        hipLaunchKernelGGL(fill_empty, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, slots, words);
+        const size_t lds = 2 * (size_t)nseg * sizeof(double);
+        const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
+        const int wl = get_wait_limit();
+        if (bf16) {
+            if (vec)
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, true>), grid, block, lds, stream, zt, zd, K, V, G,
+                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+            else
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, false>), grid, block, lds, stream, zt, zd, K, V, G,
+                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+        } else {
+            if (vec)
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, true>), grid, block, lds, stream, zt, zd, K, V, G,
+                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+            else
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, false>), grid, block, lds, stream, zt, zd, K, V,
+                                   G, Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+        }
+        return hipGetLastError();
+    }
+    int m, nseg;
+    segment_shape(V, m, nseg);
+    const size_t lds = (size_t)nseg * sizeof(double);
     if (bf16) {
         if (vec)
             hipLaunchKernelGGL((accept_logits_kernel<true, true>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K, V,

@@ -268,9 +268,15 @@ sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t
                                           n_accepted, next_token, (hipStream_t)stream));
 }
 
+size_t sv_accept_logits_workspace_bytes(int32_t B, int32_t K, int64_t V) {
+    if (B < 1 || K < 0 || K > SV_MAX_K || V < 1 || V > INT32_MAX) return 0;
+    return sv::accept_logits_workspace_bytes(B, K, (int)V);
+}
+
 sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
                            int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
-                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* stream) {
+                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     const char* fn = "sv_accept_logits";
     sv_status st;
     if ((st = check_dtype(dtype)) != SV_OK) return st;
@@ -288,7 +294,7 @@ sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, 
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_accept_logits(target_logits, draft_logits, dtype == SV_BF16, B, K, (int)V,
                                                  temperature, draft_tokens, draft_lens, uniforms, n_accepted,
-                                                 next_token, (hipStream_t)stream));
+                                                 next_token, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -16,9 +16,16 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
                          const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
                          hipStream_t stream);
 
+// With a workspace of at least accept_logits_workspace_bytes(B, K, V) bytes
+// (8-byte aligned), each sequence is split over several workgroups; otherwise
+// one workgroup per sequence.
 hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
                                 const int32_t* tokens, const int32_t* lens, const float* uniforms,
-                                int32_t* n_accepted, int32_t* next_token, hipStream_t stream);
+                                int32_t* n_accepted, int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+// 0 when one workgroup per sequence is used regardless (short rows).
+size_t accept_logits_workspace_bytes(int B, int K, int V);
 
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
                        float temperature, float* probs, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -50,5 +57,6 @@ size_t warp_workspace_bytes(int B, int R, int V);
 // Polls a cooperative warp workgroup makes before it recomputes its row alone
 // (applies to launches made after the call, on every device).
 void set_wait_limit(int tries);
+int get_wait_limit();
 
 }  // namespace sv

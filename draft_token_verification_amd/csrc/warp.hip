@@ -393,4 +393,6 @@ hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const
     return hipGetLastError();
 }
 
+int get_wait_limit() { return g_wait_limit.load(); }
+
 }  // namespace sv

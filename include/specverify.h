@@ -285,15 +285,32 @@ sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t
  * target_logits [B, K+1, V], draft_logits [B, K, V] of `dtype` (SV_F32 or
  * SV_BF16), element-aligned; draft_tokens, draft_lens, uniforms, outputs as
  * for sv_accept; temperature finite, > 0.
- * Accuracy: p and q are evaluated in fp32 (absolute error well below 1e-6 per
- * element) and the test and draw weights in binary64, so decisions and ids
- * agree with an exact evaluation except where u lies within about 1e-6 of a
- * ratio or cumulative-weight boundary.
+ * workspace    device memory of at least sv_accept_logits_workspace_bytes(B,
+ *              K, V) bytes, 8-byte aligned, owned by the caller, contents
+ *              irrelevant (initialised on `stream`): the slots in which the
+ *              workgroups sharing a sequence's rows exchange partial
+ *              statistics. With it each sequence's rows are split over
+ *              several workgroups (a long chain of accepted positions runs on
+ *              several compute units); NULL, too small, or a size of 0 from
+ *              the query selects one workgroup per sequence. Results are
+ *              identical either way up to the rounding of the partial sums.
+ *              Calls that overlap in time must not share a workspace.
+ * Accuracy: p and q come from fp32 exponentials with fp64 sums (relative
+ * error below ~1e-5 on a ratio, absolute below ~1e-5 on a cumulative weight),
+ * and the test and draw weights are compared in binary64, so decisions and
+ * ids agree with an exact evaluation except where u lies that close to a
+ * ratio or cumulative-weight boundary. Bitwise identical run to run.
  * Errors: as sv_accept, plus SV_ERR_INVALID_ARG for a bad dtype or temperature.
  */
 sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
                            int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
-                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* stream);
+                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sv_accept_logits uses for these sizes (0 when it uses one
+ * workgroup per sequence regardless: rows of at most 32768 elements, or
+ * more than 2048 sequences). */
+size_t sv_accept_logits_workspace_bytes(int32_t B, int32_t K, int64_t V);
 
 /*
  * sv_commit -- append one verify round to each sequence's token buffer on the

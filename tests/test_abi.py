@@ -30,7 +30,8 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_commit", "sv_gate_choose",
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_accept_logits_workspace_bytes",
+                                    "sv_commit", "sv_gate_choose",
                                     "sv_gate_update",
                                     "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
                                     "sv_softmax_warp_workspace_bytes", "sv_status_string", "sv_verify_greedy",
@@ -141,12 +142,12 @@ def test_wait_limit_rejects_negative(sv):
 
 
 @pytest.mark.parametrize("args,fragment", [
-    ((FAKE, FAKE, 0, -1, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "B = -1"),
-    ((FAKE, FAKE, 1, 2, 65, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "K = 65"),
-    ((FAKE, FAKE, 9, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "unknown dtype"),
-    ((FAKE, FAKE, 1, 2, 4, 100, 0.0, FAKE, None, FAKE, FAKE, FAKE, None), "temperature"),
-    ((FAKE, None, 1, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "null"),
-    ((ODD, FAKE, 0, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None), "misaligned"),
+    ((FAKE, FAKE, 0, -1, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "B = -1"),
+    ((FAKE, FAKE, 1, 2, 65, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "K = 65"),
+    ((FAKE, FAKE, 9, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "unknown dtype"),
+    ((FAKE, FAKE, 1, 2, 4, 100, 0.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "temperature"),
+    ((FAKE, None, 1, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "null"),
+    ((ODD, FAKE, 0, 2, 4, 100, 1.0, FAKE, None, FAKE, FAKE, FAKE, None, 0, None), "misaligned"),
 ])
 def test_accept_logits_rejects_bad_arguments(sv, args, fragment):
     assert sv._lib.sv_accept_logits(*args) == 1
@@ -229,3 +230,14 @@ def test_gate_choose_rejects_bad_parameters(sv, kw, fragment):
 def test_commit_rejects_bad_arguments(sv, args, fragment):
     assert sv._lib.sv_commit(*args) == 1
     assert fragment in sv._lib.sv_last_error().decode()
+
+
+def test_accept_logits_workspace_size(sv):
+    # B * ((K + 1) * 2 * G + 2 * G) 8-byte slots; G = 8 slices for B = 512 at V = 256000
+    assert sv.sv_accept_logits_workspace_bytes(512, 16, 256000) == 512 * (17 * 2 * 8 + 2 * 8) * 8
+    assert sv.sv_accept_logits_workspace_bytes(1, 4, 256000) == 1 * (5 * 2 * 8 + 2 * 8) * 8
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 70000) == 64 * (5 * 2 * 3 + 2 * 3) * 8
+    assert sv.sv_accept_logits_workspace_bytes(1024, 7, 152064) == 1024 * (8 * 2 * 4 + 2 * 4) * 8
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 32768) == 0     # short rows: one workgroup per sequence
+    assert sv.sv_accept_logits_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
+    assert sv.sv_accept_logits_workspace_bytes(0, 4, 256000) == 0

@@ -41,17 +41,23 @@ def host(t):
     return None if t is None else t.detach().cpu()
 
 
-def run(sv, zt, zd, tokens, u, lens, T):
+PATHS = ["sliced", "single"]
+
+
+def run(sv, zt, zd, tokens, u, lens, T, path="sliced"):
+    """path "sliced": the default workspace (each sequence over several workgroups when
+    the rows are long enough); "single": a zero-size workspace (one workgroup per sequence)."""
     B = zt.shape[0]
     n = torch.full((B,), SENTINEL, dtype=torch.int32, device=zt.device)
     nx = torch.full((B,), SENTINEL, dtype=torch.int32, device=zt.device)
-    sv.sv_accept_logits(zt, zd, tokens, u, T, lens, out=(n, nx))
+    ws = None if path == "sliced" else torch.empty(0, dtype=torch.uint8, device=zt.device)
+    sv.sv_accept_logits(zt, zd, tokens, u, T, lens, out=(n, nx), workspace=ws)
     torch.cuda.synchronize()
     return host(n).numpy(), host(nx).numpy()
 
 
-def compare(sv, zt, zd, tokens, u, lens, T, label, sample=None, max_flag_frac=0.35):
-    n, nx = run(sv, zt, zd, tokens, u, lens, T)
+def compare(sv, zt, zd, tokens, u, lens, T, label, sample=None, max_flag_frac=0.35, path="sliced"):
+    n, nx = run(sv, zt, zd, tokens, u, lens, T, path)
     B = zt.shape[0]
     idx = np.arange(B) if sample is None else np.sort(sample)
     it = torch.as_tensor(idx, device=zt.device)
@@ -88,18 +94,21 @@ def case_id(c):
     return name + "".join(f"-{k}{v}" for k, v in ov.items())
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", REDUCED, ids=[case_id(c) for c in REDUCED])
-def test_accept_logits_parity_reduced(sv, case):
+def test_accept_logits_parity_reduced(sv, case, path):
     name, ov = case
     b = synth.generate(name, "cuda", poison=True, **ov)  # rows past each sequence's length hold NaN
-    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, case_id(case))
+    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, case_id(case) + "/" + path, path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", LOGITS)
-def test_accept_logits_full_size(sv, name):
+def test_accept_logits_full_size(sv, name, path):
     b = synth.generate(name, "cuda", poison=True)
     sample = np.arange(b.B) if b.B <= 64 else np.random.default_rng(2).choice(b.B, 48, replace=False)
-    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, name + "/full", sample=sample)
+    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, name + "/full/" + path, sample=sample,
+            path=path)
 
 
 def test_accept_logits_matches_two_step_path_in_law(sv):
@@ -123,10 +132,11 @@ def dev(x, dtype=None):
     return torch.as_tensor(x, dtype=dtype).cuda()
 
 
+@pytest.mark.parametrize("V", [1000, 40000])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_accept_logits_edge_cases(sv, dtype):
+def test_accept_logits_edge_cases(sv, dtype, V):
     g = torch.Generator().manual_seed(11)
-    B, K, V, T = 10, 4, 1000, 0.7
+    B, K, T = 10, 4, 0.7
     zt = (2 * torch.randn(B, K + 1, V, generator=g)).to(dtype)
     zd = (zt[:, :K].float() + torch.randn(B, K, V, generator=g)).to(dtype)
     q = torch.softmax(zd.double() / T, -1)
@@ -140,7 +150,7 @@ def test_accept_logits_edge_cases(sv, dtype):
     # a token the target gives essentially zero mass -> rejected, correction drawn
     zt[3, 0, int(tok[3, 0])] = -1e4
     lens = torch.tensor([K, K, K, K, 0, 1, 2, -4, K + 9, 3], dtype=torch.int32)
-    n, nx, _ = compare(sv, dev(zt), dev(zd), dev(tok), dev(u), dev(lens), T, f"edges-{dtype}")
+    n, nx, _ = compare(sv, dev(zt), dev(zd), dev(tok), dev(u), dev(lens), T, f"edges-{dtype}-V{V}")
     assert n[0] >= 1 and n[1] <= 1 and n[2] == 0 and n[3] == 0
     assert n[4] == 0 and n[7] == 0 and n[5] <= 1
 
@@ -154,6 +164,7 @@ def test_accept_logits_k0_identical_rows_and_bonus(sv):
     zt = torch.randn(B, 1, V, generator=g)
     u = torch.rand(B, 1, generator=g)
     compare(sv, dev(zt), None, None, dev(u), None, T, "k0")
+    compare(sv, dev(4 * torch.randn(B, 1, 50000, generator=g)), None, None, dev(u), None, T, "k0-sliced")
     K = 3
     zt = torch.randn(B, K + 1, V, generator=g)
     zd = zt[:, :K].clone()
@@ -182,9 +193,25 @@ def test_accept_logits_zero_residual_row(sv):
 
 def test_accept_logits_bitwise_determinism(sv):
     b = synth.generate("logits-bf16-b256-k5-v128256", "cuda", B=64)
+    for path in PATHS:
+        r1 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, path)
+        r2 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, path)
+        assert (r1[0] == r2[0]).all() and (r1[1] == r2[1]).all()
+
+
+@pytest.mark.parametrize("name", ["logits-bf16-b512-k16-v256000-zipf", "logits-f32-b1024-ragged7-v152064"])
+def test_accept_logits_sliced_fallback_is_bitwise_identical(sv, name):
+    """With the bounded wait forced to give up at once, every slice recomputes the
+    others' partial statistics and totals itself; the results must not change."""
+    b = synth.generate(name, "cuda", B=96)
     r1 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature)
-    r2 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature)
+    try:
+        sv.sv_set_wait_limit(0)
+        r2 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature)
+    finally:
+        sv.sv_set_wait_limit(1 << 14)
     assert (r1[0] == r2[0]).all() and (r1[1] == r2[1]).all()
+    print(f"[{name}] forced fallback: identical over {b.B} sequences, mean n {r1[0].mean():.3f}", flush=True)
 
 
 def test_accept_logits_empty_batch(sv):
