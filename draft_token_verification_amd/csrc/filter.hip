@@ -12,21 +12,37 @@
 //          times the survivors' mass; equal logits share one decision; the
 //          largest logit is always kept; top_p >= 1 or NaN: off.
 //
-// One workgroup of 1024 lanes per live row. The thresholds are found by a
-// radix descent over order-preserving integer keys of the logits (16-bit keys
-// for bf16, 32-bit for fp32; -0.0 is folded into +0.0 so that equal values
-// have equal keys), one 8-bit digit per pass over the row:
-//   top-k  counts per digit, among the keys that match the digits chosen so
-//          far, give the digit of the k-th largest key;
-//   top-p  masses per digit, 2^(z*c - M) (c = log2(e)/T, M = c * max z) in
-//          fixed point (integers, 2^fxs per unit), give the digit of the last
-//          kept value. Integer sums are exact and order-free, so the descent is
-//          deterministic and a bin's mass equals the sum of its sub-bins.
-// Counts and masses go into per-wavefront histograms in LDS (integer atomics)
-// and are summed over the wavefronts between passes. The final pass writes
-// 2^(z*c - M) / S_kept for kept ids and 0 elsewhere. Passes after the first
-// re-read the row from the caches in front of HBM.
+// One workgroup of 1024 lanes per live row. The first pass over the row
+// computes the softmax statistics (logits in log2 units, y = z*c - M with
+// c = log2(e)/T and M the row maximum) and, per wavefront, collects the keys
+// of the logits within 12 log2 units of its running maximum into LDS.
+//   common path  the collected keys are sorted (bitonic network) and the
+//                thresholds read off the sorted order: the k-th largest key,
+//                then the nucleus from prefix masses, one decision per group
+//                of equal keys. It applies when the collected set holds at
+//                least k ids and (top-p alone) the nucleus ends inside it; a
+//                wavefront whose buffer overflows keeps only its largest keys
+//                (a key floor), and the common path then needs k and the
+//                nucleus above the highest floor.
+//   general path a radix descent over order-preserving integer keys of the
+//                logits (16-bit keys for bf16, 32-bit for fp32; -0.0 folded
+//                into +0.0 so that equal values have equal keys), one 8-bit
+//                digit per pass over the row: counts per digit among the keys
+//                that match the digits chosen so far give the digit of the
+//                k-th largest key; masses per digit, restricted to the top-k
+//                survivors, give the digit of the last kept value. Counts and
+//                masses go into per-wavefront histograms in LDS (integer
+//                atomics), summed over the wavefronts between passes.
+// Masses are 2^y in fixed point (integers, 2^fxs per unit) on both paths:
+// integer sums are exact and order-free, so the thresholds are deterministic.
+// The paths agree exactly except for top-p without top-k, where the common
+// path takes the whole row's mass from the fp32 statistics (relative error
+// ~1e-6) instead of an exact sum. The last pass writes 2^y / S_kept for kept
+// ids and 0 elsewhere. Passes after the first re-read the row from the caches
+// in front of HBM.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -62,6 +78,23 @@ __device__ __forceinline__ unsigned long long fixed_of(float e, int fxs) {
     if (sh >= 0) return mant << sh;
     if (sh < -24) return 0ull;
     return (mant + (1ull << (-sh - 1))) >> (-sh);
+}
+
+// Online (max, sum) of y = z*c in log2 units over N elements (-inf skipped):
+// m is the running max, s = sum 2^(y - m).
+template <int N>
+__device__ __forceinline__ void online_addf(const float* z, float c, float& m, float& s) {
+    float zm = z[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) zm = fmaxf(zm, z[k]);
+    const float ym = zm * c;
+    if (ym > m) {
+        s = (m == -INFINITY) ? 0.0f : s * ex2(m - ym);
+        m = ym;
+    }
+    if (m == -INFINITY) return;
+#pragma unroll
+    for (int k = 0; k < N; ++k) s += ex2(fmaf(z[k], c, -m));
 }
 
 // Element access: VEC rows are read 16 bytes per lane (8 bf16 or 4 fp32).
@@ -124,12 +157,20 @@ __device__ __forceinline__ void for_each(const void* row, int V, F&& f) {
 }
 
 struct FilterLds {
-    uint32_t cnt[kWaves][kBins];
-    unsigned long long mass[kWaves][kBins];
+    uint32_t cnt[kWaves][kBins];             // also: the candidate keys (kCand of them)
+    unsigned long long mass[kWaves][kBins];  // also: the candidates' exclusive prefix masses
     uint32_t tcnt[kBins];
     unsigned long long tmass[kBins];
+    unsigned long long wsum[kWaves];
     float wmax[kWaves];
+    float wsum_f[kWaves];
+    int wcnt[kWaves];
+    int ncand;
+    int istar;
 };
+
+constexpr int kCand = kWaves * kBins;  // candidates the sorted path holds (4096)
+constexpr float kSpan = 12.0f;         // candidates: logits within 12 log2 units of the maximum
 
 // Sum the per-wavefront histograms into the totals and clear them for the
 // next pass. Barrier before (the pass's atomics) and after (the totals).
@@ -207,62 +248,313 @@ __device__ __forceinline__ int find_bin(const unsigned long long* tot, unsigned 
     return kBins - 1 - 4 * l - i;
 }
 
+// Inverse of key_of: the logit a key stands for (+0.0 for the folded zeros).
+template <bool BF16>
+__device__ __forceinline__ float value_of(uint32_t key) {
+    const uint32_t k = BF16 ? ((key << 16) | ((key & 0x8000u) ? 0u : 0xFFFFu)) : key;
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Sort keys[0 .. P) descending (P a power of two <= kCand), bitonic network.
+__device__ void sort_desc(uint32_t* keys, int P) {
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (P >> 1); i += kThreads) {
+                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint32_t a = keys[lo], b = keys[hi];
+                if ((a < b) == desc) {
+                    keys[lo] = b;
+                    keys[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+constexpr int kWaveCap = kCand / kWaves;  // candidate slots per wavefront (256)
+
+__device__ __forceinline__ float wave_max_f(float m) {
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+    m = fmaxf(m, dpp_f<kDppRowHalfMirror>(m));
+    m = fmaxf(m, dpp_f<kDppRowMirror>(m));
+    m = fmaxf(m, swz16_f(m));
+    return fmaxf(readlane_f(m, 0), readlane_f(m, 32));
+}
+
+// Keep the entries of a wavefront's candidate buffer whose key is above fkey
+// and whose logit lies within kSpan log2 units of `run`, packed to the front.
+// Wave-local.
+template <bool BF16>
+__device__ __forceinline__ int wave_compact(uint32_t* buf, int cnt, float c, float run, uint32_t fkey) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t e[kWaveCap / kWave];
+    bool keep[kWaveCap / kWave];
+#pragma unroll
+    for (int q = 0; q < kWaveCap / kWave; ++q) {
+        const int i = q * kWave + lane;
+        e[q] = i < cnt ? buf[i] : 0u;
+        keep[q] = i < cnt && e[q] > fkey && fmaf(value_of<BF16>(e[q]), c, -run) > -kSpan;
+    }
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < kWaveCap / kWave; ++q) {
+        const uint64_t m = __ballot(keep[q]);
+        if (keep[q]) buf[n + __popcll(m & ((1ull << lane) - 1ull))] = e[q];
+        n += __popcll(m);
+    }
+    return n;
+}
+
+// The largest key f such that at most `room` buffer entries have key > f
+// (bitwise search; wave-local, uniform result).
+__device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int room) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t e[kWaveCap / kWave];
+#pragma unroll
+    for (int q = 0; q < kWaveCap / kWave; ++q) {
+        const int i = q * kWave + lane;
+        e[q] = i < cnt ? buf[i] : 0u;
+    }
+    // find the smallest f with count(key > f) <= room, bit by bit from the top
+    uint32_t f = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = f | ((1u << bit) - 1u);  // keep bit clear, all lower set
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < kWaveCap / kWave; ++q) n += __popcll(__ballot(e[q] > t));
+        if (n > room) f |= 1u << bit;  // must go higher
+    }
+    return f;
+}
+
+// First pass over a row: the softmax statistics (y = z*c in log2 units;
+// Mc = max y, S = sum 2^(y - Mc) in fp32, as the plain warp) and, per
+// wavefront, the keys of its logits that lie within kSpan log2 units of its
+// running maximum and above its key floor. A buffer that fills is compacted;
+// if that is not enough the floor rises to keep the 64 largest. Entries only
+// ever leave for being below the row's window or the floor, so at the end the
+// set {key > F, y > Mc - kSpan} (F: the highest floor) is complete: those ids
+// are packed into cand[0 .. nc) (any order).
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __restrict__ logits, int R, int V,
-                                                          const int32_t* __restrict__ lens, int extra_rows,
-                                                          float c, const int32_t* __restrict__ top_k,
-                                                          const float* __restrict__ top_p, int fxs,
-                                                          float* __restrict__ probs) {
+__device__ void gather_pass(const void* zrow, int V, float c, FilterLds* L, float& Mc, float& S, int& nc) {
+    using E = Elems<BF16>;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    uint32_t* buf = &L->cnt[0][0] + wave * kWaveCap;
+    float om = -INFINITY, os = 0.0f;  // this lane's online statistics
+    float run = -INFINITY;            // the wavefront's running maximum (log2 units)
+    uint32_t fkey = 0u;               // the wavefront's key floor
+    int cnt = 0;                      // entries in buf (wave-uniform)
+    auto take = [&](const float* z, const bool* valid, auto n_const) {
+        constexpr int n = decltype(n_const)::value;
+        // running maximum first, so that the test below is as tight as possible
+        float smax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < n; ++e) smax = fmaxf(smax, z[e]);
+        run = fmaxf(run, wave_max_f(smax) * c);
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < n; ++e) any |= valid[e] && fmaf(z[e], c, -run) > -kSpan && key_of<BF16>(z[e]) > fkey;
+        if (__ballot(any) == 0ull) return;
+#pragma unroll
+        for (int e = 0; e < n; ++e) {
+            const uint32_t key = key_of<BF16>(z[e]);
+            const bool near = valid[e] && fmaf(z[e], c, -run) > -kSpan;
+            uint64_t m = __ballot(near && key > fkey);
+            if (m == 0ull) continue;
+            if (cnt + __popcll(m) > kWaveCap) {
+                cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
+                if (cnt + __popcll(m) > kWaveCap) {
+                    // keep the 64 largest: rare raises, room for the next entries
+                    fkey = wave_floor(buf, cnt, kWaveCap / 4);
+                    cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
+                    m = __ballot(near && key > fkey);
+                }
+            }
+            if (near && key > fkey) buf[cnt + __popcll(m & ((1ull << lane) - 1ull))] = key;
+            cnt += __popcll(m);
+        }
+    };
+    if (VEC) {
+        constexpr int U = 2;  // 16 bf16 or 8 fp32 elements per lane per step
+        constexpr int N = U * E::N;
+        const u32x4* v = (const u32x4*)zrow;
+        const int nv = V / E::N;
+        for (int j0 = 0; j0 < nv; j0 += U * kThreads) {
+            u32x4 raw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u * kThreads + tid;
+                raw[u] = v[j < nv ? j : 0];
+            }
+            float z[N];
+            bool valid[N];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = j0 + u * kThreads + tid < nv;
+                E::unpack(raw[u], z + u * E::N);
+#pragma unroll
+                for (int e = 0; e < E::N; ++e) {
+                    valid[u * E::N + e] = in;
+                    z[u * E::N + e] = in ? z[u * E::N + e] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) online_addf<E::N>(z + u * E::N, c, om, os);
+            take(z, valid, std::integral_constant<int, N>{});
+        }
+    } else {
+        for (int x0 = 0; x0 < V; x0 += kThreads) {
+            const bool in = x0 + tid < V;
+            float z[1] = {in ? E::at(zrow, x0 + tid) : -INFINITY};
+            bool valid[1] = {in};
+            online_addf<1>(z, c, om, os);
+            take(z, valid, std::integral_constant<int, 1>{});
+        }
+    }
+    // the row's statistics
+    wave_lse(om, os);
+    if (lane == 0) {
+        L->wmax[wave] = om;
+        L->wsum_f[wave] = os;
+        L->wcnt[wave] = (int)fkey;
+    }
+    __syncthreads();
+    om = lane < kWaves ? L->wmax[lane] : -INFINITY;
+    os = lane < kWaves ? L->wsum_f[lane] : 0.0f;
+    wave_lse(om, os);
+    Mc = om;
+    S = os;
+    uint32_t F = 0u;
+    for (int w = 0; w < kWaves; ++w) F = max(F, (uint32_t)L->wcnt[w]);
+    __syncthreads();  // wcnt is reused below
+    // final filter against the row's window and the highest floor, then pack
+    const int kept = wave_compact<BF16>(buf, cnt, c, Mc, F);
+    if (lane == 0) L->wcnt[wave] = kept;
+    __syncthreads();
+    int off = 0, total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) off += L->wcnt[w];
+        total += L->wcnt[w];
+    }
+    uint32_t e[kWaveCap / kWave];
+#pragma unroll
+    for (int q = 0; q < kWaveCap / kWave; ++q) {
+        const int i = q * kWave + lane;
+        e[q] = i < kept ? buf[i] : 0u;
+    }
+    __syncthreads();  // every wavefront holds its entries before any moves
+    uint32_t* cand = &L->cnt[0][0];
+#pragma unroll
+    for (int q = 0; q < kWaveCap / kWave; ++q) {
+        const int i = q * kWave + lane;
+        if (i < kept) cand[off + i] = e[q];
+    }
+    __syncthreads();
+    nc = total;
+}
+
+// Thresholds from the nc candidates in cand[] (all logits within kSpan log2
+// units of the maximum), sorted in LDS: tau (smallest kept key) and s_kept
+// (fixed-point mass of the kept ids). S_total is the row's mass in fixed-point
+// units (from the first pass, used as the top-p reference without top-k).
+// Returns false when the candidates cannot decide: fewer than k of them, or
+// (top-p alone) a nucleus that reaches past them. Contains barriers.
+template <bool BF16>
+__device__ bool sorted_thresholds(int nc, int V, float c, float Mc, int fxs, bool kon, int k, bool pon, float pp,
+                                  double S_total, FilterLds* L, uint32_t& tau, double& s_kept) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    uint32_t* cand = &L->cnt[0][0];
+    unsigned long long* pre = &L->mass[0][0];
+    if (kon && nc < k) return false;
+    int P = 1;
+    while (P < nc) P <<= 1;
+    for (int i = nc + tid; i < P; i += kThreads) cand[i] = 0u;  // sorts last
+    __syncthreads();
+    sort_desc(cand, P);
+    // exclusive prefix masses in sorted order: thread t owns entries 4t .. 4t+3
+    unsigned long long part[4], run = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = 4 * tid + j;
+        part[j] = run;
+        run += i < nc ? fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs) : 0ull;
+    }
+    {
+        const int wave = tid / kWave;
+        unsigned long long v = run;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) v += shfl_up_u64(v, d) * (lane >= d);
+        __syncthreads();
+        if (lane == kWave - 1) L->wsum[wave] = v;
+        __syncthreads();
+        unsigned long long off = v - run;
+        for (int w = 0; w < wave; ++w) off += L->wsum[w];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[4 * tid + j] = off + part[j];
+    }
+    __syncthreads();
+    auto incl = [&](int i) { return pre[i] + fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs); };
+    // top-k survivors: the first nk candidates (all ties of the k-th largest)
+    int nk = nc;
+    if (kon) {
+        const uint32_t kth = cand[k - 1];
+        if (tid == 0) L->istar = nc;
+        __syncthreads();
+        for (int i = tid; i < nc; i += kThreads)
+            if (cand[i] >= kth && (i + 1 == nc || cand[i + 1] < kth)) L->istar = i + 1;
+        __syncthreads();
+        nk = L->istar;
+        __syncthreads();
+    }
+    if (!pon) {  // top-k alone
+        tau = cand[nk - 1];
+        s_kept = (double)incl(nk - 1);
+        return true;
+    }
+    // top-p over the survivors, one decision per group of equal keys: group
+    // start i is kept iff it is the first or its exclusive prefix mass is
+    // below the target; the kept groups are a prefix of the order
+    double target = (double)pp * (kon ? (double)incl(nk - 1) : S_total);
+    if (!(target > 0.0)) target = 0.5;  // top_p <= 0: keep the largest value only
+    if (tid == 0) L->istar = 0;
+    __syncthreads();
+    int dropped = 0;
+    for (int i = tid; i < nk; i += kThreads) {
+        const bool start = i == 0 || cand[i] != cand[i - 1];
+        if (!start) continue;
+        if (i == 0 || (double)pre[i] < target)
+            atomicMax(&L->istar, i);
+        else
+            dropped = 1;
+    }
+    const int any_dropped = __syncthreads_or(dropped);
+    const int istar = L->istar;
+    // top-p alone: if every candidate group is kept, the nucleus may reach
+    // past the candidates into the rest of the row
+    if (!kon && !any_dropped && nc < V) return false;
+    int iend = istar;  // last member of the kept group
+    while (iend + 1 < nk && cand[iend + 1] == cand[istar]) ++iend;
+    tau = cand[istar];
+    s_kept = (double)incl(iend);
+    return true;
+}
+
+// The general path (any row): radix descent with per-wavefront histograms.
+template <bool BF16, bool VEC>
+__device__ void radix_thresholds(const void* zrow, int V, float c, float Mc, int fxs, bool kon, int k, bool pon,
+                                 float pp, FilterLds* Lp, uint32_t& tau_out, unsigned long long& s_kept_out) {
     constexpr int kBits = BF16 ? 16 : 32;
     constexpr int kLevels = kBits / 8;
-    __shared__ FilterLds L;
-    const int row = blockIdx.x;
-    const int b = row / R, r = row - b * R;
-    const int live = clamp_len(lens, b, R - extra_rows) + extra_rows;
-    if (r >= live) return;
+    FilterLds& L = *Lp;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const char* zrow = (const char*)logits + (size_t)row * (size_t)V * (BF16 ? 2 : 4);
-    float* prow = probs + (size_t)row * (size_t)V;
-
-    const int k = top_k ? top_k[b] : 0;
-    const bool kon = k > 0 && k < V;
-    const float pp = top_p ? top_p[b] : 1.0f;
-    const bool pon = pp < 1.0f;  // false for NaN
-
     for (int i = tid; i < kWaves * kBins; i += kThreads) {
         (&L.cnt[0][0])[i] = 0u;
         (&L.mass[0][0])[i] = 0ull;
     }
     __syncthreads();
-
-    // pass 1: the row maximum, and the top digit's counts for top-k
-    float zmax = -INFINITY;
-    for_each<BF16, VEC>(zrow, V, [&](float z, int64_t) {
-        zmax = fmaxf(zmax, z);
-        if (kon) atomicAdd(&L.cnt[wave][key_of<BF16>(z) >> (kBits - 8)], 1u);
-    });
-    {
-        float m = zmax;
-        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-        m = fmaxf(m, dpp_f<kDppRowHalfMirror>(m));
-        m = fmaxf(m, dpp_f<kDppRowMirror>(m));
-        m = fmaxf(m, swz16_f(m));
-        m = fmaxf(readlane_f(m, 0), readlane_f(m, 32));
-        if (lane == 0) L.wmax[wave] = m;
-    }
-    __syncthreads();
-    {
-        float m = lane < kWaves ? L.wmax[lane] : -INFINITY;
-        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-        m = fmaxf(m, dpp_f<kDppRowHalfMirror>(m));
-        m = fmaxf(m, dpp_f<kDppRowMirror>(m));
-        m = fmaxf(m, swz16_f(m));
-        zmax = fmaxf(readlane_f(m, 0), readlane_f(m, 32));
-    }
-    const float Mc = zmax * c;
-
     // top-k: descend to the key of the k-th largest logit
     uint32_t tau_k = 0u;
     if (kon) {
@@ -270,12 +562,10 @@ __global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __res
         unsigned long long need = (unsigned long long)k;
         for (int l = 0; l < kLevels; ++l) {
             const int sh = kBits - 8 * (l + 1);
-            if (l > 0) {
-                for_each<BF16, VEC>(zrow, V, [&](float z, int64_t) {
-                    const uint32_t key = key_of<BF16>(z);
-                    if ((key >> (sh + 8)) == prefix) atomicAdd(&L.cnt[wave][(key >> sh) & 0xFFu], 1u);
-                });
-            }
+            for_each<BF16, VEC>(zrow, V, [&](float z, int64_t) {
+                const uint32_t key = key_of<BF16>(z);
+                if (l == 0 || (key >> (sh + 8)) == prefix) atomicAdd(&L.cnt[wave][(key >> sh) & 0xFFu], 1u);
+            });
             reduce_hist(&L, true, false);
             // totals as 64-bit for the common scan
             unsigned long long* tot = L.tmass;
@@ -335,9 +625,16 @@ __global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __res
             __syncthreads();  // the totals are rewritten by the next reduction
         }
     }
+    tau_out = tau;
+    s_kept_out = s_kept;
+}
 
-    // final pass: normalised kept probabilities, zeros elsewhere
-    const float inv = (float)(ldexp(1.0, fxs) / (double)s_kept);
+// Final pass: normalised kept probabilities, zeros elsewhere.
+template <bool BF16, bool VEC>
+__device__ void write_filtered(const void* zrow, float* prow, int V, float c, float Mc, int fxs, uint32_t tau,
+                               double s_kept) {
+    const int tid = threadIdx.x;
+    const float inv = (float)(ldexp(1.0, fxs) / s_kept);
     if (VEC) {
         using E = Elems<BF16>;
         const u32x4* v = (const u32x4*)zrow;
@@ -363,6 +660,47 @@ __global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __res
             prow[x] = key_of<BF16>(zz) >= tau ? ex2(fmaf(zz, c, -Mc)) * inv : 0.0f;
         }
     }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __restrict__ logits, int R, int V,
+                                                          const int32_t* __restrict__ lens, int extra_rows,
+                                                          float c, const int32_t* __restrict__ top_k,
+                                                          const float* __restrict__ top_p, int fxs,
+                                                          float* __restrict__ probs) {
+    __shared__ FilterLds L;
+    const int row = blockIdx.x;
+    const int b = row / R, r = row - b * R;
+    const int live = clamp_len(lens, b, R - extra_rows) + extra_rows;
+    if (r >= live) return;
+    const char* zrow = (const char*)logits + (size_t)row * (size_t)V * (BF16 ? 2 : 4);
+    float* prow = probs + (size_t)row * (size_t)V;
+
+    const int k = top_k ? top_k[b] : 0;
+    const bool kon = k > 0 && k < V;
+    const float pp = top_p ? top_p[b] : 1.0f;
+    const bool pon = pp < 1.0f;  // false for NaN
+
+    // pass 1: the statistics and the candidate ids
+    float Mc, S;
+    int nc;
+    gather_pass<BF16, VEC>(zrow, V, c, &L, Mc, S, nc);
+    uint32_t tau = 0u;
+    double s_kept = 0.0;
+    bool decided = false;
+    if (!kon && !pon) {  // no filter: the plain softmax
+        s_kept = (double)S * ldexp(1.0, fxs);
+        decided = true;
+    } else {
+        decided = sorted_thresholds<BF16>(nc, V, c, Mc, fxs, kon, k, pon, pp, (double)S * ldexp(1.0, fxs), &L, tau,
+                                          s_kept);
+    }
+    if (!decided) {
+        unsigned long long sk = 0;
+        radix_thresholds<BF16, VEC>(zrow, V, c, Mc, fxs, kon, k, pon, pp, &L, tau, sk);
+        s_kept = (double)sk;
+    }
+    write_filtered<BF16, VEC>(zrow, prow, V, c, Mc, fxs, tau, s_kept);
 }
 
 }  // namespace

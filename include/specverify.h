@@ -109,11 +109,12 @@ sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, i
  * does not apply: V not a multiple of 4, or V above about 2 million). */
 size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
 
-/* Diagnostic control, process-wide: how many times a workgroup of
- * sv_softmax_warp's fast path polls for the partial statistics of its row
+/* Diagnostic control, process-wide: how many times a workgroup polls for the
+ * partial results of the other workgroups that share its row or sequence
  * before computing them all itself (default 16384), for calls made after
- * this one. Any value gives the same results; 0 forces the
- * self-computation. */
+ * this one. It governs sv_softmax_warp's fast path and sv_accept_logits
+ * with a workspace. Any value gives the same results; 0 forces the
+ * self-computation. Returns SV_ERR_INVALID_ARG for a negative value. */
 sv_status sv_set_wait_limit(int32_t polls);
 
 /*
@@ -138,7 +139,10 @@ sv_status sv_set_wait_limit(int32_t polls);
  * Kept sets are decided exactly for top-k; top-p decides with fixed-point
  * masses (2^-40 or finer per unit) of fp32 exponentials, so a value within
  * ~1e-5 relative of its threshold may fall either way. Results are bitwise
- * identical run to run. No workspace; one workgroup per live row.
+ * identical run to run. No workspace; one workgroup per live row, two passes
+ * over it when the kept ids lie within 12 log2 units of the row maximum
+ * (more otherwise). Rows with neither filter are correct but pay the filter
+ * machinery: sv_softmax_warp is the faster call for them.
  * Errors: as sv_softmax_warp, plus misaligned top_k / top_p.
  */
 sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
