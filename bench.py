@@ -255,56 +255,67 @@ def main():
 
 
 def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
-    """HBM bytes per warp launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
 
     Each counter is scaled by what it reads for the calibration copy of
     COPY_BYTES (read once, written once) in the same run: on gfx950
     FETCH_SIZE reports about half the bytes a copy reads, WRITE_SIZE all of
-    them. The warp's two launches per step (target rows, draft rows) are
-    averaged, like the roofline's ``achieved``.
+    them. The roofline's figure is the warp's fast-path kernel, its two
+    launches per step (target rows, draft rows) averaged like ``achieved``;
+    every other library kernel is recorded per launch shape beside it.
     """
     import csv
     import re
 
+    kernel_re = re.compile(r"\b(warp_coop_kernel|warp_rows_kernel|warp_filter_kernel|accept_kernel|"
+                           r"accept_logits_kernel|accept_logits_sliced_kernel|greedy_kernel|fill_slots|fill_empty)\b")
+
     def load(path, counter):
-        warp, copy = [], []
+        per, copy = {}, []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
-            if re.search(r"\bwarp_\w*kernel\b", r["Kernel_Name"]):
-                warp.append((int(r["Grid_Size"]), v))
+            m = kernel_re.search(r["Kernel_Name"])
+            if m:
+                per.setdefault((m.group(1), int(r["Grid_Size"])), []).append(v)
             elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
                 copy.append(v)
         big = [v for v in copy if v > 0.25 * COPY_BYTES]  # the calibration copies, not small transfers
+        warp = {g: v for (k, g), v in per.items() if k == "warp_coop_kernel"}
         if not warp or not big:
             raise SystemExit(f"{path}: no warp kernel or calibration-copy dispatches with {counter}")
         factor = COPY_BYTES / (sum(big) / len(big))
-        by_grid = {}
-        for g, v in warp:
-            by_grid.setdefault(g, []).append(v)
-        per_launch = sum(sum(v) / len(v) for v in by_grid.values()) / len(by_grid)
-        return factor, per_launch * factor, {g: sum(v) / len(v) * factor for g, v in by_grid.items()}
+        avg = {kg: sum(v) / len(v) * factor for kg, v in per.items()}
+        per_launch = sum(avg[("warp_coop_kernel", g)] for g in warp) / len(warp)
+        return factor, per_launch, avg
 
     ff, fetch, fetch_by = load(fetch_csv, "FETCH_SIZE")
     wf, write, write_by = load(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for (k, g), v in sorted(fetch_by.items()):
+        kernels.setdefault(k, {})[str(g)] = {"fetch": int(v), "write": int(write_by.get((k, g), 0))}
     rec = {"workload": workload, "kernel": "warp_coop_kernel", "kernel_source_sha": kernel_source_sha(),
+           "library_source_sha": kernel_source_sha(all_sources=True),
            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
            "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
            "bytes_per_launch": int(fetch + write),
-           "per_grid": {str(g): {"fetch": int(fetch_by[g]), "write": int(write_by.get(g, 0))} for g in fetch_by},
+           "per_grid": kernels["warp_coop_kernel"],
+           "kernels": kernels,
            "source": [os.path.basename(fetch_csv), os.path.basename(write_csv)]}
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def kernel_source_sha():
-    """Hash of the warp kernel's sources: measured traffic is void once they change."""
+def kernel_source_sha(all_sources=False):
+    """Hash of the warp kernel's sources (or of every library source): measured
+    traffic is void once they change."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "draft_token_verification_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("common.hpp", "warp.hip"):
+    files = sorted(os.listdir(d)) if all_sources else ["common.hpp", "warp.hip"]
+    for f in files:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -536,19 +536,9 @@ template <bool BF16, bool VEC, bool D>
 __device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
                                RowStats& sd) {
     Online rt, rd;
-    span_stats<BF16, VEC, D, kWaves>(zt, zd, 0, V, c, lds, rt, rd);
+    span_stats<BF16, VEC, D, kWaves, BF16 ? 2 : 1>(zt, zd, 0, V, c, lds, rt, rd);
     st = RowStats{rt.m, 1.0 / rt.s};
     if (D) sd = RowStats{rd.m, 1.0 / rd.s};
-}
-
-// zd == nullptr: target row only (sd is left as it was).
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void row_stats(const void* zt, const void* zd, int V, float c, StatsLds* lds, RowStats& st,
-                                          RowStats& sd) {
-    if (zd)
-        row_stats_pass<BF16, VEC, true>(zt, zd, V, c, lds, st, sd);
-    else
-        row_stats_pass<BF16, VEC, false>(zt, nullptr, V, c, lds, st, sd);
 }
 
 template <bool BF16, bool VEC>
@@ -580,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
         }
         const void* tr = tbase + (size_t)i * row_bytes;
         const void* dr = dbase + (size_t)i * row_bytes;
-        row_stats<BF16, VEC>(tr, dr, V, c, &lds, st, sd);
+        row_stats_pass<BF16, VEC, true>(tr, dr, V, c, &lds, st, sd);
         const double pt = prob_of(L::at(tr, t), c, st);
         const double qt = prob_of(L::at(dr, t), c, sd);
         const double u = uniforms[(int64_t)b * (K + 1) + i];
@@ -595,7 +585,12 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
     const bool residual = n < kb;
     const void* zt_row = tbase + (size_t)(residual ? n : kb) * row_bytes;
     const void* zd_row = residual ? (const void*)(dbase + (size_t)n * row_bytes) : nullptr;
-    if (!(residual && have)) row_stats<BF16, VEC>(zt_row, zd_row, V, c, &lds, st, sd);
+    if (!(residual && have)) {
+        if (residual)
+            row_stats_pass<BF16, VEC, true>(zt_row, zd_row, V, c, &lds, st, sd);
+        else
+            row_stats_pass<BF16, VEC, false>(zt_row, nullptr, V, c, &lds, st, sd);
+    }
     const LogitSource<BF16, VEC, true> res{zt_row, zd_row, V, c, st, sd};
     const LogitSource<BF16, VEC, false> bon{zt_row, nullptr, V, c, st, sd};
     const int next = final_draw(res, bon, residual, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb]);

@@ -13,17 +13,20 @@
 //          largest logit is always kept; top_p >= 1 or NaN: off.
 //
 // One workgroup of 1024 lanes per live row. The first pass over the row
-// computes the softmax statistics (logits in log2 units, y = z*c - M with
-// c = log2(e)/T and M the row maximum) and, per wavefront, collects the keys
-// of the logits within 12 log2 units of its running maximum into LDS.
-//   common path  the collected keys are sorted (bitonic network) and the
-//                thresholds read off the sorted order: the k-th largest key,
-//                then the nucleus from prefix masses, one decision per group
-//                of equal keys. It applies when the collected set holds at
-//                least k ids and (top-p alone) the nucleus ends inside it; a
-//                wavefront whose buffer overflows keeps only its largest keys
-//                (a key floor), and the common path then needs k and the
-//                nucleus above the highest floor.
+// finds the row maximum M (logits in log2 units, y = z*c - M with
+// c = log2(e)/T), the softmax sum when the row has no top-k (top-p needs it
+// as the reference mass; top-k rows skip the exponentials), and, per
+// wavefront, collects the keys of the logits within 20 log2 units of its
+// running maximum into LDS.
+//   common path  the k-th largest collected key comes from a bitwise search
+//                with block-wide counts; for top-p the top-k survivors are
+//                sorted (bitonic network) and the nucleus read off their
+//                prefix masses, one decision per group of equal keys. It
+//                applies when the collected set holds at least k ids and
+//                (top-p alone) the nucleus ends inside it; a wavefront whose
+//                buffer overflows keeps only its largest keys (a key floor),
+//                and the common path then needs k and the nucleus above the
+//                highest floor.
 //   general path a radix descent over order-preserving integer keys of the
 //                logits (16-bit keys for bf16, 32-bit for fp32; -0.0 folded
 //                into +0.0 so that equal values have equal keys), one 8-bit
@@ -161,16 +164,15 @@ struct FilterLds {
     unsigned long long mass[kWaves][kBins];  // also: the candidates' exclusive prefix masses
     uint32_t tcnt[kBins];
     unsigned long long tmass[kBins];
-    unsigned long long wsum[kWaves];
+    unsigned long long wmass[2][kWaves];  // per-wavefront partials of the threshold searches
+    int wnum[2][kWaves];
     float wmax[kWaves];
     float wsum_f[kWaves];
     int wcnt[kWaves];
-    int ncand;
-    int istar;
 };
 
 constexpr int kCand = kWaves * kBins;  // candidates the sorted path holds (4096)
-constexpr float kSpan = 12.0f;         // candidates: logits within 12 log2 units of the maximum
+constexpr float kSpan = 20.0f;         // candidates: logits within 20 log2 units of the maximum
 
 // Sum the per-wavefront histograms into the totals and clear them for the
 // next pass. Barrier before (the pass's atomics) and after (the totals).
@@ -255,24 +257,6 @@ __device__ __forceinline__ float value_of(uint32_t key) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// Sort keys[0 .. P) descending (P a power of two <= kCand), bitonic network.
-__device__ void sort_desc(uint32_t* keys, int P) {
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (P >> 1); i += kThreads) {
-                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint32_t a = keys[lo], b = keys[hi];
-                if ((a < b) == desc) {
-                    keys[lo] = b;
-                    keys[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 constexpr int kWaveCap = kCand / kWaves;  // candidate slots per wavefront (256)
 
 __device__ __forceinline__ float wave_max_f(float m) {
@@ -308,9 +292,11 @@ __device__ __forceinline__ int wave_compact(uint32_t* buf, int cnt, float c, flo
     return n;
 }
 
-// The largest key f such that at most `room` buffer entries have key > f
-// (bitwise search; wave-local, uniform result).
-__device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int room) {
+// The smallest key f such that at most `room` entries have key > f, counting
+// the buffer and the step's pending elements (z[e] where bit e of want is
+// set); bitwise search over the key's bits. Wave-local, uniform result.
+template <bool BF16, int N>
+__device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int room, const float* z, uint32_t want) {
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t e[kWaveCap / kWave];
 #pragma unroll
@@ -318,62 +304,89 @@ __device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int
         const int i = q * kWave + lane;
         e[q] = i < cnt ? buf[i] : 0u;
     }
-    // find the smallest f with count(key > f) <= room, bit by bit from the top
     uint32_t f = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll 1
+    for (int bit = BF16 ? 15 : 31; bit >= 0; --bit) {
         const uint32_t t = f | ((1u << bit) - 1u);  // keep bit clear, all lower set
         int n = 0;
 #pragma unroll
         for (int q = 0; q < kWaveCap / kWave; ++q) n += __popcll(__ballot(e[q] > t));
+#pragma unroll
+        for (int q = 0; q < N; ++q) n += __popcll(__ballot(((want >> q) & 1u) && key_of<BF16>(z[q]) > t));
         if (n > room) f |= 1u << bit;  // must go higher
     }
     return f;
 }
 
 // First pass over a row: the softmax statistics (y = z*c in log2 units;
-// Mc = max y, S = sum 2^(y - Mc) in fp32, as the plain warp) and, per
-// wavefront, the keys of its logits that lie within kSpan log2 units of its
-// running maximum and above its key floor. A buffer that fills is compacted;
-// if that is not enough the floor rises to keep the 64 largest. Entries only
-// ever leave for being below the row's window or the floor, so at the end the
-// set {key > F, y > Mc - kSpan} (F: the highest floor) is complete: those ids
-// are packed into cand[0 .. nc) (any order).
+// Mc = max y and, when `stats`, S = sum 2^(y - Mc) in fp32 as the plain warp;
+// S = 0 otherwise) and, per wavefront, the keys of its logits that lie within
+// kSpan log2 units of its running maximum and above its key floor. When a
+// step's entries do not fit, the buffer is compacted; if that is not enough
+// the floor rises so that at most 64 of the buffer's and the step's entries
+// stay above it. Entries only ever leave for being below the row's window or
+// the floor, so at the end the set {key > F, y > Mc - kSpan} (F: the highest
+// floor) is complete: those ids are packed into cand[0 .. nc) (any order).
+// The per-element test is one float comparison against the larger of the
+// window's lower end (rounded down by a safe margin, so the gather never
+// misses an id the final set holds) and the value of the floor's key.
 template <bool BF16, bool VEC>
-__device__ void gather_pass(const void* zrow, int V, float c, FilterLds* L, float& Mc, float& S, int& nc) {
+__device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bool stats, FilterLds* L, float& Mc,
+                                            float& S, int& nc) {
     using E = Elems<BF16>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     uint32_t* buf = &L->cnt[0][0] + wave * kWaveCap;
+    const float inv_c = 1.0f / c;
     float om = -INFINITY, os = 0.0f;  // this lane's online statistics
     float run = -INFINITY;            // the wavefront's running maximum (log2 units)
     uint32_t fkey = 0u;               // the wavefront's key floor
+    float zf = -INFINITY;             // the logit of the floor's key (-inf: no floor)
     int cnt = 0;                      // entries in buf (wave-uniform)
-    auto take = [&](const float* z, const bool* valid, auto n_const) {
+    // out-of-row elements come in as -inf: never above a threshold
+    // running maximum first, so that the test in take() is as tight as possible
+    float zlo = -INFINITY;  // the window's lower end for the current step
+    auto update_run = [&](const float* z, auto n_const) {
         constexpr int n = decltype(n_const)::value;
-        // running maximum first, so that the test below is as tight as possible
         float smax = -INFINITY;
 #pragma unroll
         for (int e = 0; e < n; ++e) smax = fmaxf(smax, z[e]);
         run = fmaxf(run, wave_max_f(smax) * c);
+        zlo = (run - kSpan - 1e-3f) * inv_c;
+        zlo = run == -INFINITY ? -INFINITY : zlo - fabsf(zlo) * 1e-6f;
+    };
+    auto take = [&](const float* z, auto n_const) {
+        constexpr int n = decltype(n_const)::value;
+        float thr = fmaxf(zlo, zf);
         bool any = false;
 #pragma unroll
-        for (int e = 0; e < n; ++e) any |= valid[e] && fmaf(z[e], c, -run) > -kSpan && key_of<BF16>(z[e]) > fkey;
-        if (__ballot(any) == 0ull) return;
+        for (int e = 0; e < n; ++e) any |= z[e] > thr;
+        if (__ballot(any) == 0ull) return;  // the common case: nothing near the maximum
+        uint32_t want = 0u;  // bit e: element e goes into the buffer (lane masks would cost 2 SGPRs each)
+        int need = 0;
 #pragma unroll
         for (int e = 0; e < n; ++e) {
-            const uint32_t key = key_of<BF16>(z[e]);
-            const bool near = valid[e] && fmaf(z[e], c, -run) > -kSpan;
-            uint64_t m = __ballot(near && key > fkey);
-            if (m == 0ull) continue;
-            if (cnt + __popcll(m) > kWaveCap) {
+            const bool w = z[e] > thr;
+            want |= (uint32_t)w << e;
+            need += __popcll(__ballot(w));
+        }
+        if (cnt + need > kWaveCap) {  // rare: make room once for the whole step
+            cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
+            if (cnt + need > kWaveCap) {
+                // raise the floor so that at most 64 entries remain above it
+                fkey = max(fkey, wave_floor<BF16, n>(buf, cnt, kWaveCap / 4, z, want));
+                zf = value_of<BF16>(fkey);
                 cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
-                if (cnt + __popcll(m) > kWaveCap) {
-                    // keep the 64 largest: rare raises, room for the next entries
-                    fkey = wave_floor(buf, cnt, kWaveCap / 4);
-                    cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
-                    m = __ballot(near && key > fkey);
-                }
+                thr = fmaxf(zlo, zf);
+                want = 0u;
+#pragma unroll
+                for (int e = 0; e < n; ++e) want |= (uint32_t)(z[e] > thr) << e;
             }
-            if (near && key > fkey) buf[cnt + __popcll(m & ((1ull << lane) - 1ull))] = key;
+        }
+#pragma unroll
+        for (int e = 0; e < n; ++e) {
+            const bool w = (want >> e) & 1u;
+            const uint64_t m = __ballot(w);
+            if (w) buf[cnt + __popcll(m & ((1ull << lane) - 1ull))] = key_of<BF16>(z[e]);
             cnt += __popcll(m);
         }
     };
@@ -382,49 +395,61 @@ __device__ void gather_pass(const void* zrow, int V, float c, FilterLds* L, floa
         constexpr int N = U * E::N;
         const u32x4* v = (const u32x4*)zrow;
         const int nv = V / E::N;
-        for (int j0 = 0; j0 < nv; j0 += U * kThreads) {
-            u32x4 raw[U];
+        // software-pipelined: the next step's loads are in flight while this
+        // step is processed (clamped indexes, so the loads are unconditional)
+        u32x4 nxt[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = j0 + u * kThreads + tid;
-                raw[u] = v[j < nv ? j : 0];
-            }
+        for (int u = 0; u < U; ++u) {
+            const int j = u * kThreads + tid;
+            nxt[u] = v[j < nv ? j : 0];
+        }
+        for (int j0 = 0; j0 < nv; j0 += U * kThreads) {
             float z[N];
-            bool valid[N];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool in = j0 + u * kThreads + tid < nv;
-                E::unpack(raw[u], z + u * E::N);
+                E::unpack(nxt[u], z + u * E::N);
 #pragma unroll
-                for (int e = 0; e < E::N; ++e) {
-                    valid[u * E::N + e] = in;
-                    z[u * E::N + e] = in ? z[u * E::N + e] : -INFINITY;
-                }
+                for (int e = 0; e < E::N; ++e) z[u * E::N + e] = in ? z[u * E::N + e] : -INFINITY;
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) online_addf<E::N>(z + u * E::N, c, om, os);
-            take(z, valid, std::integral_constant<int, N>{});
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + (U + u) * kThreads + tid;
+                nxt[u] = v[j < nv ? j : 0];
+            }
+            if (stats) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) online_addf<E::N>(z + u * E::N, c, om, os);
+            }
+            update_run(z, std::integral_constant<int, N>{});
+#pragma unroll
+            for (int u = 0; u < U; ++u) take(z + u * E::N, std::integral_constant<int, E::N>{});
         }
     } else {
         for (int x0 = 0; x0 < V; x0 += kThreads) {
             const bool in = x0 + tid < V;
             float z[1] = {in ? E::at(zrow, x0 + tid) : -INFINITY};
-            bool valid[1] = {in};
-            online_addf<1>(z, c, om, os);
-            take(z, valid, std::integral_constant<int, 1>{});
+            if (stats) online_addf<1>(z, c, om, os);
+            update_run(z, std::integral_constant<int, 1>{});
+            take(z, std::integral_constant<int, 1>{});
         }
     }
-    // the row's statistics
-    wave_lse(om, os);
+    // the row's statistics (without `stats`, the maximum is the running one)
+    if (stats) wave_lse(om, os);
     if (lane == 0) {
-        L->wmax[wave] = om;
+        L->wmax[wave] = stats ? om : run;
         L->wsum_f[wave] = os;
         L->wcnt[wave] = (int)fkey;
     }
     __syncthreads();
     om = lane < kWaves ? L->wmax[lane] : -INFINITY;
     os = lane < kWaves ? L->wsum_f[lane] : 0.0f;
-    wave_lse(om, os);
+    if (stats) {
+        wave_lse(om, os);
+    } else {
+        om = wave_max_f(om);
+        os = 0.0f;
+    }
     Mc = om;
     S = os;
     uint32_t F = 0u;
@@ -456,95 +481,185 @@ __device__ void gather_pass(const void* zrow, int V, float c, FilterLds* L, floa
     nc = total;
 }
 
-// Thresholds from the nc candidates in cand[] (all logits within kSpan log2
-// units of the maximum), sorted in LDS: tau (smallest kept key) and s_kept
-// (fixed-point mass of the kept ids). S_total is the row's mass in fixed-point
-// units (from the first pass, used as the top-p reference without top-k).
-// Returns false when the candidates cannot decide: fewer than k of them, or
-// (top-p alone) a nucleus that reaches past them. Contains barriers.
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int lo = __shfl_xor((int)(uint32_t)v, d, kWave), hi = __shfl_xor((int)(uint32_t)(v >> 32), d, kWave);
+        v += ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+    }
+    return v;
+}
+
+// Sort keys[0 .. P) descending (P a power of two <= kCand), bitonic network.
+__device__ __forceinline__ void sort_desc(uint32_t* keys, int P) {
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (P >> 1); i += kThreads) {
+                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint32_t a = keys[lo], b = keys[hi];
+                if ((a < b) == desc) {
+                    keys[lo] = b;
+                    keys[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Thresholds from the nc candidates in cand[] (every key above the gather's
+// cut): tau (smallest kept key) and s_kept (fixed-point mass of the kept
+// ids). Each thread holds up to 4 candidates in registers.
+//   top-k  the k-th largest key: the largest t with at least k candidate keys
+//          >= t, by a bitwise search with block-wide counts.
+//   top-p  the survivors of top-k (keys >= that) are packed and sorted in
+//          LDS; an id is kept iff the survivors strictly above it weigh less
+//          than the target, one decision per group of equal keys, read off the
+//          exclusive prefix masses of the sorted order.
+// S_total is the row's mass in fixed-point units (the top-p reference without
+// top-k). Returns false when the candidates cannot decide: fewer than k of
+// them, or (top-p alone) a nucleus that keeps every candidate and may reach
+// past them. Contains barriers.
 template <bool BF16>
-__device__ bool sorted_thresholds(int nc, int V, float c, float Mc, int fxs, bool kon, int k, bool pon, float pp,
-                                  double S_total, FilterLds* L, uint32_t& tau, double& s_kept) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    uint32_t* cand = &L->cnt[0][0];
-    unsigned long long* pre = &L->mass[0][0];
+__device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float Mc, int fxs, bool kon, int k, bool pon,
+                                                  float pp, double S_total, FilterLds* L, uint32_t& tau,
+                                                  double& s_kept) {
+    constexpr int kPer = kCand / kThreads;
+    constexpr int kBits = BF16 ? 16 : 32;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     if (kon && nc < k) return false;
+    uint32_t* cand = &L->cnt[0][0];
+    uint32_t key[kPer];
+    unsigned long long mass[kPer];
+    bool valid[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = j * kThreads + tid;
+        valid[j] = i < nc;
+        key[j] = valid[j] ? cand[i] : 0u;
+        mass[j] = valid[j] ? fixed_of(ex2(fmaf(value_of<BF16>(key[j]), c, -Mc)), fxs) : 0ull;
+    }
+    // block-wide sums: per-wavefront partials in alternating LDS halves, so a
+    // half is rewritten only after every wavefront has passed the barrier
+    // that follows its last read
+    int half = 0;
+    auto count_ge = [&](uint32_t t) {
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) n += __popcll(__ballot(valid[j] && key[j] >= t));
+        if (lane == 0) L->wnum[half][wave] = n;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += L->wnum[half][w];
+        half ^= 1;
+        return tot;
+    };
+    auto mass_ge = [&](uint32_t t) {
+        unsigned long long m = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) m += valid[j] && key[j] >= t ? mass[j] : 0ull;
+        m = wave_sum_u64(m);
+        if (lane == 0) L->wmass[half][wave] = m;
+        __syncthreads();
+        unsigned long long tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += L->wmass[half][w];
+        half ^= 1;
+        return tot;
+    };
+    uint32_t kth = 0u;
+    if (kon) {
+        for (int bit = kBits - 1; bit >= 0; --bit) {
+            const uint32_t t = kth | (1u << bit);
+            if (count_ge(t) >= k) kth = t;
+        }
+    }
+    if (!pon) {
+        tau = kth;
+        s_kept = (double)mass_ge(kth);
+        return true;
+    }
+    // pack the survivors (keys >= kth) to the front of cand[], then sort them
+    int ns = 0, off = 0;
+    {
+        int mine[kPer], wtot = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint64_t m = __ballot(valid[j] && key[j] >= kth);
+            mine[j] = wtot + __popcll(m & ((1ull << lane) - 1ull));
+            wtot += __popcll(m);
+        }
+        if (lane == 0) L->wnum[half][wave] = wtot;
+        __syncthreads();  // also: every candidate has been read from cand[]
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int n = L->wnum[half][w];
+            off += w < wave ? n : 0;
+            ns += n;
+        }
+        half ^= 1;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (valid[j] && key[j] >= kth) cand[off + mine[j]] = key[j];
+    }
     int P = 1;
-    while (P < nc) P <<= 1;
-    for (int i = nc + tid; i < P; i += kThreads) cand[i] = 0u;  // sorts last
+    while (P < ns) P <<= 1;
+    for (int i = ns + tid; i < P; i += kThreads) cand[i] = 0u;  // sorts last
     __syncthreads();
     sort_desc(cand, P);
     // exclusive prefix masses in sorted order: thread t owns entries 4t .. 4t+3
-    unsigned long long part[4], run = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = 4 * tid + j;
-        part[j] = run;
-        run += i < nc ? fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs) : 0ull;
-    }
+    unsigned long long* pre = &L->mass[0][0];
     {
-        const int wave = tid / kWave;
+        unsigned long long part[4], run = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * tid + j;
+            part[j] = run;
+            run += i < ns ? fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs) : 0ull;
+        }
         unsigned long long v = run;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) v += shfl_up_u64(v, d) * (lane >= d);
+        if (lane == kWave - 1) L->wmass[half][wave] = v;
         __syncthreads();
-        if (lane == kWave - 1) L->wsum[wave] = v;
-        __syncthreads();
-        unsigned long long off = v - run;
-        for (int w = 0; w < wave; ++w) off += L->wsum[w];
+        unsigned long long base = v - run;
+        for (int w = 0; w < wave; ++w) base += L->wmass[half][w];
+        half ^= 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pre[4 * tid + j] = off + part[j];
+        for (int j = 0; j < 4; ++j) pre[4 * tid + j] = base + part[j];
     }
-    __syncthreads();
-    auto incl = [&](int i) { return pre[i] + fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs); };
-    // top-k survivors: the first nk candidates (all ties of the k-th largest)
-    int nk = nc;
-    if (kon) {
-        const uint32_t kth = cand[k - 1];
-        if (tid == 0) L->istar = nc;
-        __syncthreads();
-        for (int i = tid; i < nc; i += kThreads)
-            if (cand[i] >= kth && (i + 1 == nc || cand[i + 1] < kth)) L->istar = i + 1;
-        __syncthreads();
-        nk = L->istar;
-        __syncthreads();
-    }
-    if (!pon) {  // top-k alone
-        tau = cand[nk - 1];
-        s_kept = (double)incl(nk - 1);
-        return true;
-    }
-    // top-p over the survivors, one decision per group of equal keys: group
-    // start i is kept iff it is the first or its exclusive prefix mass is
-    // below the target; the kept groups are a prefix of the order
-    double target = (double)pp * (kon ? (double)incl(nk - 1) : S_total);
+    const unsigned long long H0 = mass_ge(kth);  // the survivors' mass (also orders the writes above)
+    double target = (double)pp * (kon ? (double)H0 : S_total);
     if (!(target > 0.0)) target = 0.5;  // top_p <= 0: keep the largest value only
-    if (tid == 0) L->istar = 0;
+    // the last group start whose exclusive prefix is below the target (the
+    // first group is always kept); kept groups are a prefix of the order
+    int last = 0;
+    for (int i = tid; i < ns; i += kThreads)
+        if (i > 0 && cand[i] != cand[i - 1] && (double)pre[i] < target) last = max(last, i);
+    last = max(last, __shfl_xor(last, 1));
+    last = max(last, __shfl_xor(last, 2));
+    last = max(last, __shfl_xor(last, 4));
+    last = max(last, __shfl_xor(last, 8));
+    last = max(last, __shfl_xor(last, 16));
+    last = max(last, __shfl_xor(last, 32));
+    if (lane == 0) L->wnum[half][wave] = last;
     __syncthreads();
-    int dropped = 0;
-    for (int i = tid; i < nk; i += kThreads) {
-        const bool start = i == 0 || cand[i] != cand[i - 1];
-        if (!start) continue;
-        if (i == 0 || (double)pre[i] < target)
-            atomicMax(&L->istar, i);
-        else
-            dropped = 1;
-    }
-    const int any_dropped = __syncthreads_or(dropped);
-    const int istar = L->istar;
-    // top-p alone: if every candidate group is kept, the nucleus may reach
-    // past the candidates into the rest of the row
-    if (!kon && !any_dropped && nc < V) return false;
-    int iend = istar;  // last member of the kept group
-    while (iend + 1 < nk && cand[iend + 1] == cand[istar]) ++iend;
+    int istar = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) istar = max(istar, L->wnum[half][w]);
+    half ^= 1;
     tau = cand[istar];
-    s_kept = (double)incl(iend);
+    // top-p alone: if no candidate is dropped, ids below the cut may belong
+    if (!kon && nc < V && count_ge(tau) == nc) return false;
+    s_kept = (double)mass_ge(tau);
     return true;
 }
 
 // The general path (any row): radix descent with per-wavefront histograms.
 template <bool BF16, bool VEC>
-__device__ void radix_thresholds(const void* zrow, int V, float c, float Mc, int fxs, bool kon, int k, bool pon,
+__device__ __forceinline__ void radix_thresholds(const void* zrow, int V, float c, float Mc, int fxs, bool kon, int k, bool pon,
                                  float pp, FilterLds* Lp, uint32_t& tau_out, unsigned long long& s_kept_out) {
     constexpr int kBits = BF16 ? 16 : 32;
     constexpr int kLevels = kBits / 8;
@@ -629,41 +744,58 @@ __device__ void radix_thresholds(const void* zrow, int V, float c, float Mc, int
     s_kept_out = s_kept;
 }
 
-// Final pass: normalised kept probabilities, zeros elsewhere.
+// Final pass: normalised kept probabilities, zeros elsewhere. Kept means
+// key >= tau, tested as z >= the logit of tau (keys order like the logits
+// and equal logits have equal keys); a quad of four consecutive elements with
+// nothing kept in the whole wavefront skips the exponentials. Each lane takes
+// 4 consecutive elements, so every store instruction of a wavefront covers
+// 1 KB of the output contiguously (no partially written lines).
 template <bool BF16, bool VEC>
-__device__ void write_filtered(const void* zrow, float* prow, int V, float c, float Mc, int fxs, uint32_t tau,
-                               double s_kept) {
+__device__ __forceinline__ void write_filtered(const void* zrow, float* prow, int V, float c, float Mc, int fxs,
+                                               uint32_t tau, double s_kept) {
     const int tid = threadIdx.x;
     const float inv = (float)(ldexp(1.0, fxs) / s_kept);
+    const float zt = tau == 0u ? -INFINITY : value_of<BF16>(tau);
+    auto prob = [&](float zz) { return zz >= zt ? ex2(fmaf(zz, c, -Mc)) * inv : 0.0f; };
     if (VEC) {
-        using E = Elems<BF16>;
-        const u32x4* v = (const u32x4*)zrow;
+        constexpr int kU = BF16 ? 8 : 4;  // 64 bytes of logits per lane in flight
+        using Raw = typename std::conditional<BF16, uint2, float4>::type;
         f32x4* out = (f32x4*)prow;
-        const int nv = V / E::N;
-        for (int j = tid; j < nv; j += kThreads) {
-            float z[E::N];
-            E::unpack(v[j], z);
-#pragma unroll
-            for (int h = 0; h < E::N / 4; ++h) {
-                f32x4 o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float zz = z[4 * h + q];
-                    o[q] = key_of<BF16>(zz) >= tau ? ex2(fmaf(zz, c, -Mc)) * inv : 0.0f;
-                }
-                store_nt(out + (int64_t)j * (E::N / 4) + h, o);
+        const Raw* in = (const Raw*)zrow;
+        const int nq = V / 4;
+        auto quad = [&](const Raw& r) {
+            float z[4];
+            if constexpr (BF16) {
+                z[0] = bf16_lo(r.x);
+                z[1] = bf16_hi(r.x);
+                z[2] = bf16_lo(r.y);
+                z[3] = bf16_hi(r.y);
+            } else {
+                z[0] = r.x;
+                z[1] = r.y;
+                z[2] = r.z;
+                z[3] = r.w;
             }
+            const bool any = (z[0] >= zt) | (z[1] >= zt) | (z[2] >= zt) | (z[3] >= zt);
+            if (__ballot(any) == 0ull) return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            return f32x4{prob(z[0]), prob(z[1]), prob(z[2]), prob(z[3])};
+        };
+        int j = tid;
+        for (; j + (kU - 1) * kThreads < nq; j += kU * kThreads) {
+            Raw r[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) r[u] = in[j + u * kThreads];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) store_nt(out + j + u * kThreads, quad(r[u]));
         }
+        for (; j < nq; j += kThreads) store_nt(out + j, quad(in[j]));
     } else {
-        for (int x = tid; x < V; x += kThreads) {
-            const float zz = Elems<BF16>::at(zrow, x);
-            prow[x] = key_of<BF16>(zz) >= tau ? ex2(fmaf(zz, c, -Mc)) * inv : 0.0f;
-        }
+        for (int x = tid; x < V; x += kThreads) prow[x] = prob(Elems<BF16>::at(zrow, x));
     }
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __restrict__ logits, int R, int V,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void warp_filter_kernel(const void* __restrict__ logits, int R, int V,
                                                           const int32_t* __restrict__ lens, int extra_rows,
                                                           float c, const int32_t* __restrict__ top_k,
                                                           const float* __restrict__ top_p, int fxs,
@@ -684,7 +816,7 @@ __global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __res
     // pass 1: the statistics and the candidate ids
     float Mc, S;
     int nc;
-    gather_pass<BF16, VEC>(zrow, V, c, &L, Mc, S, nc);
+    gather_pass<BF16, VEC>(zrow, V, c, !kon, &L, Mc, S, nc);  // top-k rows need no row sum
     uint32_t tau = 0u;
     double s_kept = 0.0;
     bool decided = false;
@@ -692,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void warp_filter_kernel(const void* __res
         s_kept = (double)S * ldexp(1.0, fxs);
         decided = true;
     } else {
-        decided = sorted_thresholds<BF16>(nc, V, c, Mc, fxs, kon, k, pon, pp, (double)S * ldexp(1.0, fxs), &L, tau,
+        decided = select_thresholds<BF16>(nc, V, c, Mc, fxs, kon, k, pon, pp, (double)S * ldexp(1.0, fxs), &L, tau,
                                           s_kept);
     }
     if (!decided) {

@@ -140,7 +140,7 @@ sv_status sv_set_wait_limit(int32_t polls);
  * masses (2^-40 or finer per unit) of fp32 exponentials, so a value within
  * ~1e-5 relative of its threshold may fall either way. Results are bitwise
  * identical run to run. No workspace; one workgroup per live row, two passes
- * over it when the kept ids lie within 12 log2 units of the row maximum
+ * over it when the kept ids lie within 20 log2 units of the row maximum
  * (more otherwise). Rows with neither filter are correct but pay the filter
  * machinery: sv_softmax_warp is the faster call for them.
  * Errors: as sv_softmax_warp, plus misaligned top_k / top_p.
