@@ -241,6 +241,25 @@ def main():
             "fused_sampled_rounds_per_s": round(1000.0 / (fused_ms + greedy_ms), 3),
         })
 
+    # practical reference for the warp's stream: torch's own bf16/fp32 -> fp32
+    # conversion copy of one target-row launch's worth of logits (read s,
+    # write 4 bytes per element), timed the same way
+    if batch.kind == "logits":
+        src = batch.target.reshape(-1)[: rows_t * V]
+        dst = p.reshape(-1)[: rows_t * V]
+        for _ in range(2):
+            dst.copy_(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        out["kernels"]["torch_convert_copy_GBps"] = round(gbs(rows_t * V * (elem + 4), c0.elapsed_time(c1) / 5), 1)
+        del src, dst
+
     if args.copy_calibrate:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -268,7 +287,8 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
     import re
 
     kernel_re = re.compile(r"\b(warp_coop_kernel|warp_rows_kernel|warp_filter_kernel|accept_kernel|"
-                           r"accept_logits_kernel|accept_logits_sliced_kernel|greedy_kernel|fill_slots|fill_empty)\b")
+                           r"accept_logits_kernel|accept_logits_sliced_kernel|greedy_kernel|greedy_sliced_kernel|"
+                           r"fill_slots|fill_empty)\b")
 
     def load(path, counter):
         per, copy = {}, []
@@ -279,7 +299,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
             m = kernel_re.search(r["Kernel_Name"])
             if m:
                 per.setdefault((m.group(1), int(r["Grid_Size"])), []).append(v)
-            elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
+            elif "copyBuffer" in r["Kernel_Name"]:  # the runtime's device-to-device copy
                 copy.append(v)
         big = [v for v in copy if v > 0.25 * COPY_BYTES]  # the calibration copies, not small transfers
         warp = {g: v for (k, g), v in per.items() if k == "warp_coop_kernel"}

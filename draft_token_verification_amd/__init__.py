@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
-__all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy", "sv_accept",
+__all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy",
+           "sv_verify_greedy_workspace_bytes", "sv_accept",
            "sv_accept_logits", "sv_accept_logits_workspace_bytes", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
            "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder",
            "verify_greedy", "accept", "library_path",
@@ -63,7 +64,7 @@ def _load():
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.sv_softmax_warp_workspace_bytes.argtypes = [i32, i32, i64]
-    lib.sv_verify_greedy_margin.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, vp]
+    lib.sv_verify_greedy_margin.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sv_verify_greedy_margin.restype = c_int
     lib.sv_gate_update.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_double, vp]
     lib.sv_gate_update.restype = c_int
@@ -77,7 +78,9 @@ def _load():
     lib.sv_set_wait_limit.argtypes = [i32]
     lib.sv_set_wait_limit.restype = c_int
     lib.sv_softmax_warp.restype = c_int
-    lib.sv_verify_greedy.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.sv_verify_greedy.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sv_verify_greedy_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_verify_greedy_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_verify_greedy.restype = c_int
     lib.sv_accept.argtypes = [vp, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.sv_accept.restype = c_int
@@ -86,7 +89,7 @@ def _load():
     lib.sv_accept_logits_workspace_bytes.argtypes = [i32, i32, i64]
     lib.sv_accept_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_accept_logits.restype = c_int
-    if lib.sv_abi_version() != 1:
+    if lib.sv_abi_version() != 2:
         raise ImportError("libspecverify ABI version mismatch")
     return lib
 
@@ -167,6 +170,20 @@ def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
     return ws
 
 
+def _workspace_arg(workspace: Optional[torch.Tensor], need: int, device, stream, what: str):
+    """(pointer, bytes) of the caller's workspace, or of the one kept per
+    device and stream when none is given."""
+    if workspace is None:
+        workspace = _workspace(need, device, stream)
+    elif workspace.device != device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on the {what}' device")
+    return _ptr(workspace), 0 if workspace is None else workspace.numel()
+
+
+def sv_verify_greedy_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(_lib.sv_verify_greedy_workspace_bytes(B, K, V))
+
+
 def sv_softmax_warp_workspace_bytes(B: int, R: int, V: int) -> int:
     return int(_lib.sv_softmax_warp_workspace_bytes(B, R, V))
 
@@ -212,9 +229,11 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
 
 def sv_verify_greedy_margin(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
                             draft_lens: Optional[torch.Tensor] = None,
-                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                            workspace: Optional[torch.Tensor] = None):
     """Greedy verify plus the top1 - top2 margin of the row next_token comes from
-    -> (n_accepted[B], next_token[B], top2_margin[B] fp32)."""
+    -> (n_accepted[B], next_token[B], top2_margin[B] fp32). ``workspace`` as in
+    sv_verify_greedy."""
     _dev(target, "target")
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -231,8 +250,11 @@ def sv_verify_greedy_margin(target: torch.Tensor, draft_tokens: Optional[torch.T
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
     mg = _out((B,), dev, None if out is None else out[2], torch.float32, "top2_margin")
     with torch.cuda.device(dev):
+        stream = _stream(dev)
+        ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
+                                      stream.value, "target")
         st = _lib.sv_verify_greedy_margin(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
-                                          _ptr(n), _ptr(nx), _ptr(mg), _stream(dev))
+                                          _ptr(n), _ptr(nx), _ptr(mg), ws, ws_bytes, stream)
     _check("sv_verify_greedy_margin", st)
     return n, nx, mg
 
@@ -361,8 +383,13 @@ def sv_softmax_warp_filtered(logits: torch.Tensor, temperature: float = 1.0, dra
 
 def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
                      draft_lens: Optional[torch.Tensor] = None,
-                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Greedy verify of target [B, K+1, V] (fp32/bf16 logits or probs) -> (n_accepted[B], next_token[B])."""
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Greedy verify of target [B, K+1, V] (fp32/bf16 logits or probs) -> (n_accepted[B], next_token[B]).
+
+    ``workspace`` (uint8 device tensor) defaults to one kept per device and stream, sized by
+    sv_verify_greedy_workspace_bytes; a zero-size one selects one workgroup per sequence.
+    """
     _dev(target, "target")
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -378,8 +405,11 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
     with torch.cuda.device(dev):
+        stream = _stream(dev)
+        ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
+                                      stream.value, "target")
         st = _lib.sv_verify_greedy(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
-                                   _ptr(n), _ptr(nx), _stream(dev))
+                                   _ptr(n), _ptr(nx), ws, ws_bytes, stream)
     _check("sv_verify_greedy", st)
     return n, nx
 

@@ -616,8 +616,7 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
 
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
-constexpr int kMaxSlices = 8;
-constexpr unsigned long long kEmptySlot = ~0ull;  // a NaN pattern: never a published value
+constexpr int kMaxSlices = kMaxCoopSlices;
 
 __device__ __forceinline__ unsigned long long pack_online(const Online& o) {
     return ((unsigned long long)__float_as_uint((float)o.s) << 32) | __float_as_uint(o.m);
@@ -625,38 +624,6 @@ __device__ __forceinline__ unsigned long long pack_online(const Online& o) {
 
 __device__ __forceinline__ void merge_packed(Online& r, unsigned long long v) {
     online_merge(r, __uint_as_float((unsigned)v), (double)__uint_as_float((unsigned)(v >> 32)));
-}
-
-// Wavefront 0 polls words set[0 .. nw) (bounded) and copies them to LDS;
-// returns whether all were published (uniform after the barrier).
-__device__ __forceinline__ bool gather_words(const unsigned long long* set, int nw, int wait_limit,
-                                             unsigned long long* s_words, int* s_ready) {
-    const int tid = threadIdx.x;
-    if (tid < kWave) {
-        bool ready = false;
-        for (int tries = 0; tries <= wait_limit; ++tries) {
-            bool mine = true;
-            for (int k = tid; k < nw; k += kWave) {
-                const unsigned long long v = __hip_atomic_load(set + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (v == kEmptySlot)
-                    mine = false;
-                else
-                    s_words[k] = v;
-            }
-            if (__ballot(!mine) == 0) {
-                ready = true;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (tid == 0) *s_ready = ready;
-    }
-    __syncthreads();
-    return *s_ready;
-}
-
-__device__ __forceinline__ void publish_word(unsigned long long* slot, unsigned long long v) {
-    if (threadIdx.x == 0) __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Row statistics of the examined rows (target, and draft when D) from the G
@@ -863,15 +830,14 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
     return hipGetLastError();
 }
 
-namespace {
-
-// Slices of the sliced fused verify: at most 8, B * G <= 4096 workgroups of
+// Slices of the sliced verify kernels: at most 8, B * G <= 4096 workgroups of
 // 256 lanes (twice what the chip holds at once; the dispatch order keeps a
 // sequence's slices together), each slice at least 32768 elements (shorter
 // slices spend more on the exchanges than they save); Ls is a multiple of 1024
 // elements and every slice is non-empty. Measured on MI355X at B = 512,
-// K = 16, V = 256000 (G = 8): 0.58 ms, against 0.63 (G = 4) and 0.79 (G = 2).
-void slice_shape(int B, int V, int& G, int& Ls) {
+// K = 16, V = 256000 (G = 8) for the fused sampled verify: 0.58 ms, against
+// 0.63 (G = 4) and 0.79 (G = 2).
+void coop_slice_shape(int B, int V, int& G, int& Ls) {
     int g = 4096 / (B > 0 ? B : 1);
     g = g < 1 ? 1 : (g > kMaxSlices ? kMaxSlices : g);
     const int gv = (V + 32767) / 32768;
@@ -882,11 +848,15 @@ void slice_shape(int B, int V, int& G, int& Ls) {
     Ls = (int)ls;
 }
 
-}  // namespace
+hipError_t launch_fill_empty(unsigned long long* slots, int64_t words, hipStream_t stream) {
+    if (words <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_empty, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, slots, words);
+    return hipGetLastError();
+}
 
 size_t accept_logits_workspace_bytes(int B, int K, int V) {
     int G, Ls;
-    slice_shape(B, V, G, Ls);
+    coop_slice_shape(B, V, G, Ls);
     if (G < 2) return 0;
     return (size_t)B * ((size_t)(K + 1) * 2 * G + 2 * (size_t)G) * sizeof(unsigned long long);
 }
@@ -901,11 +871,11 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
     const size_t need = accept_logits_workspace_bytes(B, K, V);
     if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
         int G, Ls, m, nseg;
-        slice_shape(B, V, G, Ls);
+        coop_slice_shape(B, V, G, Ls);
         segment_shape(Ls, m, nseg);
         const int64_t words = (int64_t)(need / sizeof(unsigned long long));
         unsigned long long* slots = (unsigned long long*)workspace;
-        hipLaunchKernelGGL(fill_empty, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, slots, words);
+        launch_fill_empty(slots, words, stream);
         const size_t lds = 2 * (size_t)nseg * sizeof(double);
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
         const int wl = get_wait_limit();

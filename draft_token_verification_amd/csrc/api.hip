@@ -70,7 +70,8 @@ sv_status launched(const char* fn, hipError_t e) {
 
 sv_status greedy_common(const char* fn, const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                         const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
-                        int32_t* next_token, float* top2_margin, bool want_margin, void* stream) {
+                        int32_t* next_token, float* top2_margin, bool want_margin, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     sv_status st;
     if ((st = check_dtype(dtype)) != SV_OK) return st;
     if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
@@ -83,7 +84,7 @@ sv_status greedy_common(const char* fn, const void* target, int dtype, int32_t B
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_greedy(target, dtype == SV_BF16, B, K, (int)V, draft_tokens, draft_lens, n_accepted,
-                                          next_token, top2_margin, (hipStream_t)stream));
+                                          next_token, top2_margin, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -164,18 +165,24 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
                                                  temperature, top_k, top_p, probs, (hipStream_t)stream));
 }
 
+size_t sv_verify_greedy_workspace_bytes(int32_t B, int32_t K, int64_t V) {
+    if (B < 1 || K < 0 || K > SV_MAX_K || V < 1 || V > INT32_MAX) return 0;
+    return sv::greedy_workspace_bytes(B, K, (int)V);
+}
+
 sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                            const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
-                           int32_t* next_token, void* stream) {
+                           int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream) {
     return greedy_common("sv_verify_greedy", target, dtype, B, K, V, draft_tokens, draft_lens, n_accepted, next_token,
-                         nullptr, false, stream);
+                         nullptr, false, workspace, workspace_bytes, stream);
 }
 
 sv_status sv_verify_greedy_margin(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                                   const int32_t* draft_tokens, const int32_t* draft_lens, int32_t* n_accepted,
-                                  int32_t* next_token, float* top2_margin, void* stream) {
+                                  int32_t* next_token, float* top2_margin, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
     return greedy_common("sv_verify_greedy_margin", target, dtype, B, K, V, draft_tokens, draft_lens, n_accepted,
-                         next_token, top2_margin, true, stream);
+                         next_token, top2_margin, true, workspace, workspace_bytes, stream);
 }
 
 sv_status sv_gate_update(double* hits, double* trials, int32_t B, int32_t NB, int32_t K, const int32_t* draft_lens,

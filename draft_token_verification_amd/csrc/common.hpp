@@ -134,4 +134,42 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int K) {
     return k < 0 ? 0 : (k > K ? K : k);
 }
 
+// ---- exchange between the workgroups that share a row or a sequence --------
+// Slots are 64-bit words in a caller's workspace, filled with kEmptySlot
+// before the launch; a workgroup publishes its partial result into its own
+// slot with a relaxed agent-scope store and the others poll for it (bounded).
+constexpr unsigned long long kEmptySlot = ~0ull;  // a NaN pattern: never a published value
+
+// Wavefront 0 polls words set[0 .. nw) (bounded) and copies them to LDS;
+// returns whether all were published (uniform after the barrier).
+__device__ __forceinline__ bool gather_words(const unsigned long long* set, int nw, int wait_limit,
+                                             unsigned long long* s_words, int* s_ready) {
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        bool ready = false;
+        for (int tries = 0; tries <= wait_limit; ++tries) {
+            bool mine = true;
+            for (int k = tid; k < nw; k += kWave) {
+                const unsigned long long v = __hip_atomic_load(set + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == kEmptySlot)
+                    mine = false;
+                else
+                    s_words[k] = v;
+            }
+            if (__ballot(!mine) == 0) {
+                ready = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (tid == 0) *s_ready = ready;
+    }
+    __syncthreads();
+    return *s_ready;
+}
+
+__device__ __forceinline__ void publish_word(unsigned long long* slot, unsigned long long v) {
+    if (threadIdx.x == 0) __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace sv

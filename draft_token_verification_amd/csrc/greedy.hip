@@ -5,10 +5,14 @@
 // draft token t_i while it equals argmax(target row i); at the first miss emit
 // that row's argmax; if all K_b match emit argmax(target row K_b).
 //
-// Mapping: one workgroup (1024 lanes, 16 wavefronts) owns one sequence and
-// walks its rows in order, so the early exit at the first miss is a plain
-// loop exit: rows after the miss are never fetched and no workgroup waits on
-// another. Each row is one streaming argmax over V elements:
+// Mapping, without a workspace: one workgroup (1024 lanes, 16 wavefronts)
+// owns one sequence and walks its rows in order, so the early exit at the
+// first miss is a plain loop exit: rows after the miss are never fetched and
+// no workgroup waits on another. With a workspace (greedy_sliced_kernel
+// below) the rows of a sequence are split over up to 8 workgroups that
+// exchange their partial argmaxes at every position, so a long chain of
+// matches is read by several compute units. Each row (or slice) is one
+// streaming argmax:
 //   - 16-byte coalesced non-temporal loads (8 bf16 or 4 fp32 per load),
 //     UNROLL loads in flight per lane;
 //   - per lane, a strict '>' keeps the first of equal maxima (each lane sees
@@ -124,52 +128,56 @@ struct RowReader<false> {
     }
 };
 
-// Argmax of one row of V elements. Returns the wave-uniform index (and, with
-// M, the row's maximum and runner-up values in vmax / vsecond); every lane of
-// the workgroup must call it (it contains one barrier). `slot` alternates
-// between two LDS buffers so that consecutive rows never race on them.
-template <bool BF16, bool M>
-__device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int (*lds_i)[kWaves],
-                            float (*lds_s)[kWaves], int slot, float& vmax, float& vsecond) {
+// Argmax of elements [x0, x0 + len) of a row (len >= 1), over a workgroup of
+// NW wavefronts. Returns the wave-uniform index (and, with M, the maximum and
+// runner-up values in vmax / vsecond); every lane of the workgroup must call
+// it (it contains one barrier). `slot` alternates between two LDS buffers so
+// that consecutive calls never race on them.
+template <bool BF16, bool M, int NW, int U = kUnroll>
+__device__ __forceinline__ int span_argmax(const void* row, int x0, int len, float (*lds_v)[NW], int (*lds_i)[NW],
+                                           float (*lds_s)[NW], int slot, float& vmax, float& vsecond) {
     using R = RowReader<BF16>;
     constexpr int E = R::kPerVec;
+    constexpr int NT = NW * kWave;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const char* span = (const char*)row + (size_t)x0 * (BF16 ? 2 : 4);
 
     // Elements before the first 16-byte boundary, one per lane.
-    const uintptr_t addr = (uintptr_t)row;
+    const uintptr_t addr = (uintptr_t)span;
     int head = (int)(((16u - (addr & 15u)) & 15u) / (BF16 ? 2u : 4u));
-    if (head > V) head = V;
-    const int nvec = (V - head) / E;
+    if (head > len) head = len;
+    const int nvec = (len - head) / E;
     const int tail0 = head + nvec * E;
 
     float best = -INFINITY, second = -INFINITY;
     int bidx = INT32_MAX;
     if (tid < head) {
-        best = R::at(row, tid);
-        bidx = tid;
+        best = R::at(span, tid);
+        bidx = x0 + tid;
     }
-    const typename R::Vec* vrow = (const typename R::Vec*)((const char*)row + head * (BF16 ? 2 : 4));
+    const typename R::Vec* vrow = (const typename R::Vec*)(span + head * (BF16 ? 2 : 4));
+    const int base = x0 + head;
     int j = tid;
     if (j < nvec) {
-        R::template scan_first<M>(load_nt(vrow + j), head + j * E, best, bidx, second);
-        j += kThreads;
+        R::template scan_first<M>(load_nt(vrow + j), base + j * E, best, bidx, second);
+        j += NT;
     }
-    for (; j + (kUnroll - 1) * kThreads < nvec; j += kUnroll * kThreads) {
-        typename R::Vec w[kUnroll];
+    for (; j + (U - 1) * NT < nvec; j += U * NT) {
+        typename R::Vec w[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = load_nt(vrow + j + u * kThreads);
+        for (int u = 0; u < U; ++u) w[u] = load_nt(vrow + j + u * NT);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) R::template scan<M>(w[u], head + (j + u * kThreads) * E, best, bidx, second);
+        for (int u = 0; u < U; ++u) R::template scan<M>(w[u], base + (j + u * NT) * E, best, bidx, second);
     }
-    for (; j < nvec; j += kThreads) R::template scan<M>(load_nt(vrow + j), head + j * E, best, bidx, second);
-    if (tail0 + tid < V) {
-        const float v = R::at(row, tail0 + tid);
+    for (; j < nvec; j += NT) R::template scan<M>(load_nt(vrow + j), base + j * E, best, bidx, second);
+    if (tail0 + tid < len) {
+        const float v = R::at(span, tail0 + tid);
         if (bidx == INT32_MAX) {
             best = v;
-            bidx = tail0 + tid;
+            bidx = x0 + tail0 + tid;
         } else {
-            take<M>(v, tail0 + tid, best, bidx, second);
+            take<M>(v, x0 + tail0 + tid, best, bidx, second);
         }
     }
 
@@ -184,15 +192,16 @@ __device__ int block_argmax(const void* row, int V, float (*lds_v)[kWaves], int 
         if (M) lds_s[slot][wave] = second;
     }
     __syncthreads();
-    float v = lane < kWaves ? lds_v[slot][lane] : -INFINITY;
-    int i = lane < kWaves ? lds_i[slot][lane] : INT32_MAX;
+    float v = lane < NW ? lds_v[slot][lane] : -INFINITY;
+    int i = lane < NW ? lds_i[slot][lane] : INT32_MAX;
     if (M) {
-        float s = lane < kWaves ? lds_s[slot][lane] : -INFINITY;
+        float s = lane < NW ? lds_s[slot][lane] : -INFINITY;
         wave_top2(v, i, s);
         vmax = v;
         vsecond = s;
     } else {
         wave_argmax(v, i);
+        vmax = v;
     }
     return i;
 }
@@ -218,8 +227,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     int i = 0;
     for (;; ++i) {
         float vmax = 0.0f, vsecond = 0.0f;
-        const int am =
-            block_argmax<BF16, M>(base + (size_t)i * row_bytes, V, lds_v, lds_i, lds_s, i & 1, vmax, vsecond);
+        const int am = span_argmax<BF16, M, kWaves>(base + (size_t)i * row_bytes, 0, V, lds_v, lds_i, lds_s, i & 1,
+                                                    vmax, vsecond);
         // a token outside [0, V) never equals an argmax: it is a miss
         if (i == kb || readlane_i(my_tok, i) != am) {
             if (threadIdx.x == 0) {
@@ -232,11 +241,129 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     }
 }
 
+// ---- greedy_sliced_kernel: each sequence over G workgroups -----------------
+//
+// The same walk with the rows of a sequence split into G slices of Ls
+// elements; workgroup (b, g) of 256 lanes owns slice g of every row of
+// sequence b. At each position every slice publishes its (value, index) --
+// and, with M, its runner-up value -- into sentinel-filled slots of the
+// caller's workspace, and every workgroup merges all G in slice order, so all
+// take the same decision. A long chain of matches thus reads each row with G
+// compute units instead of one. Every wait is bounded: a workgroup that gives
+// up computes the missing slices itself with the same code and lane mapping,
+// so the result is the same either way.
+constexpr int kSliceWaves = 4;
+constexpr int kSliceThreads = kSliceWaves * kWave;
+constexpr int kSliceUnroll = 6;  // 96 bytes per lane in flight (8 would spill)
+
+template <bool BF16, bool M>
+__global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_sliced_kernel(
+    const void* __restrict__ target, int K, int V, int G, int Ls, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ lens, int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token,
+    float* __restrict__ top2_margin, unsigned long long* __restrict__ slots, int wait_limit) {
+    __shared__ float lds_v[2][kSliceWaves];
+    __shared__ int lds_i[2][kSliceWaves];
+    __shared__ float lds_s[M ? 2 : 1][kSliceWaves];
+    __shared__ unsigned long long s_words[2 * kMaxCoopSlices];
+    __shared__ int s_ready;
+    constexpr int W = M ? 2 : 1;  // words per slice and position
+    const int b = blockIdx.x / G, g = blockIdx.x - b * G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int kb = clamp_len(lens, b, K);
+    const int my_tok = lane < kb ? tokens[(int64_t)b * K + lane] : -1;
+    const size_t row_bytes = (size_t)V * (BF16 ? 2 : 4);
+    const char* base = (const char*)target + (size_t)b * (size_t)(K + 1) * row_bytes;
+    auto slice_len = [&](int k) { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); };
+    auto pack = [](float v, int i) {
+        return ((unsigned long long)__float_as_uint(v) << 32) | (unsigned long long)(uint32_t)i;
+    };
+    int parity = 0;
+    for (int i = 0;; ++i) {
+        const char* row = base + (size_t)i * row_bytes;
+        unsigned long long* set = slots + ((size_t)b * (K + 1) + i) * (size_t)(G * W);
+        float v, s = -INFINITY;
+        int am = span_argmax<BF16, M, kSliceWaves, kSliceUnroll>(row, g * Ls, slice_len(g), lds_v, lds_i, lds_s, parity, v, s);
+        parity ^= 1;
+        publish_word(set + g * W, pack(v, am));
+        if (M) publish_word(set + g * W + 1, (unsigned long long)__float_as_uint(s));
+        if (!gather_words(set, G * W, wait_limit, s_words, &s_ready)) {
+            // bounded wait ran out: every slice's result, computed here alike
+            for (int k = 0; k < G; ++k) {
+                float vk, sk = -INFINITY;
+                const int ik =
+                    span_argmax<BF16, M, kSliceWaves, kSliceUnroll>(row, k * Ls, slice_len(k), lds_v, lds_i, lds_s, parity, vk, sk);
+                parity ^= 1;
+                if (threadIdx.x == 0) {
+                    s_words[k * W] = pack(vk, ik);
+                    if (M) s_words[k * W + 1] = (unsigned long long)__float_as_uint(sk);
+                }
+            }
+            __syncthreads();
+        }
+        // merge the slices in slice order (the same in every workgroup)
+        v = __uint_as_float((uint32_t)(s_words[0] >> 32));
+        am = (int)(uint32_t)s_words[0];
+        if (M) s = __uint_as_float((uint32_t)s_words[1]);
+        for (int k = 1; k < G; ++k) {
+            const float vk = __uint_as_float((uint32_t)(s_words[k * W] >> 32));
+            const int ik = (int)(uint32_t)s_words[k * W];
+            if (M)
+                top2_merge(v, am, s, vk, ik, __uint_as_float((uint32_t)s_words[k * W + 1]));
+            else
+                argmax_merge(v, am, vk, ik);
+        }
+        __syncthreads();  // s_words is rewritten by the next position's gather
+        // a token outside [0, V) never equals an argmax: it is a miss
+        if (i == kb || readlane_i(my_tok, i) != am) {
+            if (g == 0 && threadIdx.x == 0) {
+                n_accepted[b] = i;
+                next_token[b] = am;
+                if (M) top2_margin[b] = v - s;
+            }
+            return;
+        }
+    }
+}
+
 }  // namespace
+
+size_t greedy_workspace_bytes(int B, int K, int V) {
+    int G, Ls;
+    coop_slice_shape(B, V, G, Ls);
+    if (G < 2) return 0;
+    return (size_t)B * (size_t)(K + 1) * 2 * (size_t)G * sizeof(unsigned long long);
+}
 
 hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
-                         hipStream_t stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const size_t need = greedy_workspace_bytes(B, K, V);
+    if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
+        int G, Ls;
+        coop_slice_shape(B, V, G, Ls);
+        unsigned long long* slots = (unsigned long long*)workspace;
+        const int64_t words = (int64_t)B * (K + 1) * (top2_margin ? 2 : 1) * G;
+        hipError_t e = launch_fill_empty(slots, words, stream);
+        if (e != hipSuccess) return e;
+        const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
+        const int wl = get_wait_limit();
+        if (top2_margin) {
+            if (bf16)
+                hipLaunchKernelGGL((greedy_sliced_kernel<true, true>), grid, block, 0, stream, target, K, V, G, Ls,
+                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+            else
+                hipLaunchKernelGGL((greedy_sliced_kernel<false, true>), grid, block, 0, stream, target, K, V, G, Ls,
+                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+        } else {
+            if (bf16)
+                hipLaunchKernelGGL((greedy_sliced_kernel<true, false>), grid, block, 0, stream, target, K, V, G, Ls,
+                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+            else
+                hipLaunchKernelGGL((greedy_sliced_kernel<false, false>), grid, block, 0, stream, target, K, V, G, Ls,
+                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid(B), block(kThreads);
     if (top2_margin) {
         if (bf16)

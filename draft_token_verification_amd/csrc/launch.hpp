@@ -7,10 +7,15 @@
 
 namespace sv {
 
-// top2_margin may be null (no margin output).
+// top2_margin may be null (no margin output). With a workspace of at least
+// greedy_workspace_bytes(B, K, V) bytes (8-byte aligned) each sequence's rows
+// are split over several workgroups; otherwise one workgroup per sequence.
 hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
-                         hipStream_t stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+// 0 when one workgroup per sequence is used regardless (short rows).
+size_t greedy_workspace_bytes(int B, int K, int V);
 
 hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, const float* uniforms, int32_t* n_accepted, int32_t* next_token,
@@ -26,6 +31,15 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
 
 // 0 when one workgroup per sequence is used regardless (short rows).
 size_t accept_logits_workspace_bytes(int B, int K, int V);
+
+// How the verify kernels split a sequence's rows over workgroups: G slices of
+// Ls elements (Ls a multiple of 1024, G <= kMaxCoopSlices, B * G <= 4096 where
+// possible).
+constexpr int kMaxCoopSlices = 8;
+void coop_slice_shape(int B, int V, int& G, int& Ls);
+
+// Fill `words` exchange slots with the empty marker, on `stream`.
+hipError_t launch_fill_empty(unsigned long long* slots, int64_t words, hipStream_t stream);
 
 hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
                        float temperature, float* probs, void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 #define SV_MAX_K 64 /* draft lengths up to 64, one wavefront lane per position */
 
 typedef enum {
@@ -112,8 +112,8 @@ size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
 /* Diagnostic control, process-wide: how many times a workgroup polls for the
  * partial results of the other workgroups that share its row or sequence
  * before computing them all itself (default 16384), for calls made after
- * this one. It governs sv_softmax_warp's fast path and sv_accept_logits
- * with a workspace. Any value gives the same results; 0 forces the
+ * this one. It governs sv_softmax_warp's fast path, and sv_accept_logits,
+ * sv_verify_greedy and sv_verify_greedy_margin with a workspace. Any value gives the same results; 0 forces the
  * self-computation. Returns SV_ERR_INVALID_ARG for a negative value. */
 sv_status sv_set_wait_limit(int32_t polls);
 
@@ -162,13 +162,28 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
  * target       [B, K+1, V] of `dtype` (SV_F32 or SV_BF16), element-aligned.
  * draft_tokens [B, K] int32 (may be NULL when K == 0).
  * draft_lens   [B] int32 or NULL.
+ * workspace    device memory of at least
+ *              sv_verify_greedy_workspace_bytes(B, K, V) bytes, 8-byte
+ *              aligned, owned by the caller, not used by another call that
+ *              may run at the same time; its contents need no preparation
+ *              and are scratch afterwards. With it, each sequence's rows are
+ *              split over up to 8 workgroups that exchange partial argmaxes
+ *              (a long chain of matches is read by several compute units);
+ *              NULL (or too small) selects one workgroup per sequence. The
+ *              results are identical either way.
  * Result: n_accepted[b] in [0, K_b], next_token[b] in [0, V); bit-exact.
  * Errors: SV_ERR_INVALID_ARG for null required pointers, B < 0, K < 0,
  * K > SV_MAX_K, V < 1 or V > INT32_MAX, a bad dtype, misaligned pointers.
  */
 sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                            const int32_t* draft_tokens, const int32_t* draft_lens,
-                           int32_t* n_accepted, int32_t* next_token, void* stream);
+                           int32_t* n_accepted, int32_t* next_token, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes the split path of sv_verify_greedy and
+ * sv_verify_greedy_margin uses for these sizes (0 when one workgroup per
+ * sequence is used regardless: V up to 32768, or invalid sizes). */
+size_t sv_verify_greedy_workspace_bytes(int32_t B, int32_t K, int64_t V);
 
 /*
  * sv_verify_greedy_margin -- sv_verify_greedy plus, per sequence, the top1 -
@@ -184,7 +199,7 @@ sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, 
 sv_status sv_verify_greedy_margin(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                                   const int32_t* draft_tokens, const int32_t* draft_lens,
                                   int32_t* n_accepted, int32_t* next_token, float* top2_margin,
-                                  void* stream);
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Acceptance-driven draft-length gate (PocketLLM DSpark notes, "gating"), on

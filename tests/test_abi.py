@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                                     "sv_gate_update",
                                     "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
                                     "sv_softmax_warp_workspace_bytes", "sv_status_string", "sv_verify_greedy",
-                                    "sv_verify_greedy_margin"]
+                                    "sv_verify_greedy_margin", "sv_verify_greedy_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol(sv):
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(sv):
 
 def test_constants_match_header(sv):
     text = open(HEADER).read()
-    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 1
+    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 2
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
     assert re.search(r"SV_F32 = 0", text) and re.search(r"SV_BF16 = 1", text)
     for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARG"), (2, "SV_ERR_UNSUPPORTED"), (3, "SV_ERR_HIP")]:
@@ -64,16 +64,16 @@ ODD = ctypes.c_void_p(0x1002)        # 2-byte aligned only
 
 
 @pytest.mark.parametrize("args,fragment", [
-    ((FAKE, 0, -1, 4, 100, None, None, FAKE, FAKE, None), "B = -1"),
-    ((FAKE, 0, 2, -1, 100, FAKE, None, FAKE, FAKE, None), "K = -1"),
-    ((FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, None), "K = 65"),
-    ((FAKE, 0, 2, 4, 0, FAKE, None, FAKE, FAKE, None), "V = 0"),
-    ((FAKE, 0, 2, 4, 1 << 31, FAKE, None, FAKE, FAKE, None), "V = 2147483648"),
-    ((FAKE, 7, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "unknown dtype"),
-    ((None, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "null"),
-    ((FAKE, 0, 2, 4, 100, None, None, FAKE, FAKE, None), "null"),
-    ((FAKE, 0, 2, 4, 100, FAKE, None, None, FAKE, None), "null"),
-    ((ODD, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None), "misaligned"),
+    ((FAKE, 0, -1, 4, 100, None, None, FAKE, FAKE, None, 0, None), "B = -1"),
+    ((FAKE, 0, 2, -1, 100, FAKE, None, FAKE, FAKE, None, 0, None), "K = -1"),
+    ((FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, None, 0, None), "K = 65"),
+    ((FAKE, 0, 2, 4, 0, FAKE, None, FAKE, FAKE, None, 0, None), "V = 0"),
+    ((FAKE, 0, 2, 4, 1 << 31, FAKE, None, FAKE, FAKE, None, 0, None), "V = 2147483648"),
+    ((FAKE, 7, 2, 4, 100, FAKE, None, FAKE, FAKE, None, 0, None), "unknown dtype"),
+    ((None, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None, 0, None), "null"),
+    ((FAKE, 0, 2, 4, 100, None, None, FAKE, FAKE, None, 0, None), "null"),
+    ((FAKE, 0, 2, 4, 100, FAKE, None, None, FAKE, None, 0, None), "null"),
+    ((ODD, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None, 0, None), "misaligned"),
 ])
 def test_verify_greedy_rejects_bad_arguments(sv, args, fragment):
     st = sv._lib.sv_verify_greedy(*args)
@@ -114,7 +114,7 @@ def test_softmax_warp_rejects_bad_arguments(sv, args, fragment):
 
 def test_empty_batch_is_a_no_op(sv):
     # B == 0 returns before any pointer is looked at or any device is queried
-    assert sv._lib.sv_verify_greedy(None, 0, 0, 4, 100, None, None, None, None, None) == 0
+    assert sv._lib.sv_verify_greedy(None, 0, 0, 4, 100, None, None, None, None, None, 0, None) == 0
     assert sv._lib.sv_accept(None, None, 0, 4, 100, None, None, None, None, None, None) == 0
     assert sv._lib.sv_softmax_warp(None, 1, 0, 3, 100, None, 1, 1.0, None, None, 0, None) == 0
     assert sv._lib.sv_last_error().decode() == ""
@@ -175,13 +175,13 @@ def test_softmax_warp_filtered_rejects_bad_arguments(sv, args, fragment):
 
 def test_verify_greedy_margin_rejects_bad_arguments(sv):
     lib = sv._lib
-    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None, None) == 1
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
     assert "null" in lib.sv_last_error().decode()
-    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, ODD, None) == 1
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 4, 100, FAKE, None, FAKE, FAKE, ODD, None, 0, None) == 1
     assert "misaligned" in lib.sv_last_error().decode()
-    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.sv_verify_greedy_margin(FAKE, 0, 2, 65, 100, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert "K = 65" in lib.sv_last_error().decode()
-    assert lib.sv_verify_greedy_margin(None, 0, 0, 4, 100, None, None, None, None, None, None) == 0
+    assert lib.sv_verify_greedy_margin(None, 0, 0, 4, 100, None, None, None, None, None, None, 0, None) == 0
 
 
 @pytest.mark.parametrize("args,fragment", [
@@ -241,3 +241,14 @@ def test_accept_logits_workspace_size(sv):
     assert sv.sv_accept_logits_workspace_bytes(64, 4, 32768) == 0     # short rows: one workgroup per sequence
     assert sv.sv_accept_logits_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
     assert sv.sv_accept_logits_workspace_bytes(0, 4, 256000) == 0
+
+
+def test_verify_greedy_workspace_size(sv):
+    # B * (K + 1) * 2 * G 8-byte slots (two words per slice and position); G as for the fused sampled verify
+    assert sv.sv_verify_greedy_workspace_bytes(512, 16, 256000) == 512 * 17 * 2 * 8 * 8
+    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 70000) == 64 * 5 * 2 * 3 * 8
+    assert sv.sv_verify_greedy_workspace_bytes(1024, 7, 152064) == 1024 * 8 * 2 * 4 * 8
+    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 32768) == 0     # short rows: one workgroup per sequence
+    assert sv.sv_verify_greedy_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
+    assert sv.sv_verify_greedy_workspace_bytes(0, 4, 256000) == 0
+    assert sv.sv_verify_greedy_workspace_bytes(8, 65, 256000) == 0

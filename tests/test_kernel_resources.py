@@ -22,7 +22,8 @@ RESOURCES = os.path.join(PKG, "libspecverify.resources.json")
 CSRC = os.path.join(PKG, "csrc")
 
 KERNELS = ["accept_kernel", "accept_logits_kernel", "accept_logits_sliced_kernel", "commit_kernel", "fill_empty",
-           "fill_slots", "gate_choose_kernel", "gate_update_kernel", "greedy_kernel", "warp_coop_kernel",
+           "fill_slots", "gate_choose_kernel", "gate_update_kernel", "greedy_kernel", "greedy_sliced_kernel",
+           "warp_coop_kernel",
            "warp_filter_kernel", "warp_rows_kernel"]
 
 
