@@ -241,6 +241,48 @@ def main():
             "fused_sampled_rounds_per_s": round(1000.0 / (fused_ms + greedy_ms), 3),
         })
 
+    # per-round latency, eager and replayed from a HIP graph (torch.cuda.CUDAGraph): the
+    # greedy round alone and the sampled round alone (probabilities: sv_accept; logits:
+    # the fused sv_accept_logits)
+    def latency_us(fn, reps=50):
+        fn()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        eager = a0.elapsed_time(a1) / reps * 1e3
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        a0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return {"eager": round(eager, 2), "graph": round(a0.elapsed_time(a1) / reps * 1e3, 2)}
+
+    lat = {"greedy_round": latency_us(lambda: sv.sv_verify_greedy(batch.target, batch.tokens, lens, out=(n_gr, nx_gr)))}
+    if batch.kind == "logits":
+        lat["sampled_round_fused"] = latency_us(lambda: sv.sv_accept_logits(batch.target, batch.draft, batch.tokens,
+                                                                           batch.uniforms, T, lens, out=(n_fu, nx_fu)))
+    else:
+        lat["sampled_round"] = latency_us(lambda: sv.sv_accept(batch.target, batch.draft, batch.tokens, batch.uniforms,
+                                                               lens, out=(n_acc, nxt)))
+    out["latency_us"] = lat
+
     # practical reference for the warp's stream: torch's own bf16/fp32 -> fp32
     # conversion copy of one target-row launch's worth of logits (read s,
     # write 4 bytes per element), timed the same way
