@@ -224,7 +224,6 @@ def main():
         else None,
         "accept_GBps_needed": round(gbs(accept_bytes, accept_ms), 1),
         "greedy_GBps_needed": round(gbs(greedy_bytes, greedy_ms), 1),
-        "greedy_full_read_GBps_equiv": round(gbs(B * (K + 1) * V * elem, greedy_ms), 1),
         "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
     }
     if filt_ms is not None:
@@ -282,6 +281,37 @@ def main():
         lat["sampled_round"] = latency_us(lambda: sv.sv_accept(batch.target, batch.draft, batch.tokens, batch.uniforms,
                                                                lens, out=(n_acc, nxt)))
     out["latency_us"] = lat
+
+    # a measured stream-read rate: the greedy verify with draft tokens equal to
+    # the target's argmax chain, so every live row of every sequence is read
+    # (the argmax kernel streaming with no early exit)
+    chain = batch.target.argmax(-1).to(torch.int32)[:, :K].contiguous()
+    n_ch = torch.empty(B, dtype=torch.int32, device=dev)
+    nx_ch = torch.empty(B, dtype=torch.int32, device=dev)
+    sv.sv_verify_greedy(batch.target, chain, lens, out=(n_ch, nx_ch))
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(5):
+        sv.sv_verify_greedy(batch.target, chain, lens, out=(n_ch, nx_ch))
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_bytes = int(((n_ch.cpu().numpy().astype(np.int64) + 1) * V * elem).sum())
+    out["kernels"]["stream_read_GBps"] = round(gbs(read_bytes, r0.elapsed_time(r1) / 5), 1)
+    del chain, n_ch, nx_ch
+
+    # bytes read by the round's kernels (rocprofv3 FETCH_SIZE, scaled, from the
+    # traffic file when it matches these sources) over the round time
+    if batch.kind == "logits" and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        ks = tr.get("kernels", {})
+        if tr.get("workload") == args.workload and tr.get("library_source_sha") == kernel_source_sha(True) and ks:
+            rd = lambda name: sum(x["fetch"] for x in ks.get(name, {}).values())
+            per_step = rd("warp_coop_kernel") + rd("accept_kernel") + rd("greedy_sliced_kernel") + rd("greedy_kernel")
+            out["kernels"]["round_bytes_read"] = per_step
+            out["kernels"]["round_read_GBps"] = round(gbs(per_step, ms_per_step), 1)
 
     # practical reference for the warp's stream: torch's own bf16/fp32 -> fp32
     # conversion copy of one target-row launch's worth of logits (read s,
