@@ -150,7 +150,9 @@ __device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) 
 // max(0, p) (bonus or zero-residual fallback).
 template <bool BF16, bool VEC, bool D>
 struct LogitSource {
-    static constexpr int kUnroll = 2;  // segments in flight per wavefront (register budget)
+    // segments per wavefront step; with the next step's loads in flight too,
+    // two fp32 pairs would not fit the register budget
+    static constexpr int kUnroll = BF16 ? 2 : 1;
     const void* zt;
     const void* zd;  // read only when D
     int V;
@@ -203,7 +205,7 @@ struct LogitSource {
         for (int j = 0; j < 4; ++j) {
             const double p = prob_of(a[j], c, st);
             const double v = D ? p - prob_of(d[j], c, sd) : p;
-            w[j] = v > 0.0 ? v : 0.0;
+            w[j] = fmax(v, 0.0);  // a NaN gives 0, as a failed v > 0 test would
         }
     }
 };
@@ -215,32 +217,50 @@ struct LogitSource {
 // every lane (each wavefront sums seg[] in the same order).
 template <int NW, class Src>
 __device__ double segment_totals(const Src& src, int m, int nseg, double* seg) {
+    constexpr int U = Src::kUnroll;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t L = (int64_t)m * kSub;
-    for (int s0 = wave; s0 < nseg; s0 += NW * Src::kUnroll) {
-        double acc[Src::kUnroll];
+    // A wavefront takes its segments U at a time (s0 + u * NW) and walks their
+    // sub-blocks k; the loads of the next (s0, k) step are issued before the
+    // current step's weights are summed, across segment boundaries too (for
+    // short rows m is 1 and each segment is a single step).
+    using Raw = typename Src::Raw;
+    auto fetch = [&](int s0, int k, Raw* r) {
 #pragma unroll
-        for (int u = 0; u < Src::kUnroll; ++u) acc[u] = 0.0;
-        for (int k = 0; k < m; ++k) {
-            typename Src::Raw raw[Src::kUnroll];
+        for (int u = 0; u < U; ++u) r[u] = src.load((int64_t)(s0 + u * NW) * L + (int64_t)k * kSub + 4 * lane);
+    };
+    Raw cur[U], nxt[U];
+    double acc[U];
 #pragma unroll
-            for (int u = 0; u < Src::kUnroll; ++u) {
-                const int64_t x = (int64_t)(s0 + u * NW) * L + (int64_t)k * kSub + 4 * lane;
-                raw[u] = src.load(x);
-            }
+    for (int u = 0; u < U; ++u) acc[u] = 0.0;
+    int s0 = wave, k = 0;
+    if (s0 < nseg) fetch(s0, 0, cur);
+    while (s0 < nseg) {
+        int s1 = s0, k1 = k + 1;
+        if (k1 == m) {
+            k1 = 0;
+            s1 = s0 + NW * U;
+        }
+        if (s1 < nseg) fetch(s1, k1, nxt);
 #pragma unroll
-            for (int u = 0; u < Src::kUnroll; ++u) {
-                double w[4];
-                src.weights(raw[u], w);
-                acc[u] += ((w[0] + w[1]) + w[2]) + w[3];
+        for (int u = 0; u < U; ++u) {
+            double w[4];
+            src.weights(cur[u], w);
+            acc[u] += ((w[0] + w[1]) + w[2]) + w[3];
+        }
+        if (k1 == 0) {  // the U segments are complete
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const double tot = wave_sum_d(acc[u]);
+                const int s = s0 + u * NW;
+                if (lane == 0 && s < nseg) seg[s] = tot;
+                acc[u] = 0.0;
             }
         }
 #pragma unroll
-        for (int u = 0; u < Src::kUnroll; ++u) {
-            const double tot = wave_sum_d(acc[u]);
-            const int s = s0 + u * NW;
-            if (lane == 0 && s < nseg) seg[s] = tot;
-        }
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        s0 = s1;
+        k = k1;
     }
     __syncthreads();
     double part = 0.0;
@@ -384,52 +404,79 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(const float* __restric
 
 // ---- accept_logits_kernel: logits rows, warped on the fly -------------------
 
-// Online (max, sum) of y = z*c: `s` accumulates 4-element fp32 partials in
-// binary64, rescaled when the running max grows.
+// Online statistics of y = z*c: s = sum of 2^(y - m) over the elements seen,
+// against a reference m that is an integer (the ceiling of the largest y so
+// far) or kNoRef before the first finite y. Moving the reference therefore
+// rescales s by an exact power of two, and every term 2^(y - m) is at most 1;
+// -inf elements add exp2(-inf) = 0 and need no test. The 4-element fp32
+// partials are summed in binary64.
 struct Online {
     float m;
     double s;
 };
 
-__device__ __forceinline__ void online_add4(const float z[4], float c, Online& o) {
-    const float zm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    const float ym = zm * c;
-    if (ym > o.m) {
-        o.s = (o.m == -INFINITY) ? 0.0 : o.s * (double)ex2(o.m - ym);
-        o.m = ym;
-    }
-    if (o.m == -INFINITY) return;  // all -inf so far: nothing to add (and no -inf - -inf)
-    const float part = (ex2(fmaf(z[0], c, -o.m)) + ex2(fmaf(z[1], c, -o.m))) +
-                       (ex2(fmaf(z[2], c, -o.m)) + ex2(fmaf(z[3], c, -o.m)));
-    o.s += (double)part;
+constexpr float kNoRef = -3.40282347e38f;  // -FLT_MAX: below every finite y
+
+// s * 2^(from - to) for integral from <= to (kNoRef included: shifts past
+// the binary64 range give 0).
+__device__ __forceinline__ double rescale(double s, float from, float to) {
+    return __builtin_ldexp(s, (int)fmaxf(from - to, -1100.0f));
 }
 
-// N elements at once: one max, at most one rescale, one fp32 partial sum and
-// one binary64 add per N elements (a few VALU operations per element; the
-// statistics pass is bound by these when a workgroup works alone).
+// Pairwise sum of N fp32 terms (a fixed tree: independent adds).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* e) {
+    if constexpr (N == 1) {
+        return e[0];
+    } else {
+        return tree_sum<N / 2>(e) + tree_sum<N - N / 2>(e + N / 2);
+    }
+}
+
+// N elements at once: one max, at most one (exact) rescale, one fp32 partial
+// sum and one binary64 add per N elements.
+// The largest of three floats in one instruction. Written out because
+// fmaxf on values that come from bit operations (unpacked bf16) or straight
+// from memory makes the compiler quiet each operand with an extra max first.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ float max_of(const float* z) {
+    static_assert(N >= 2, "");
+    float r = max3f(z[0], z[1], N > 2 ? z[2] : z[1]);
+#pragma unroll
+    for (int k = 3; k < N; k += 2) r = max3f(r, z[k], z[k + 1 < N ? k + 1 : k]);
+    return r;
+}
+
 template <int N>
 __device__ __forceinline__ void online_addn(const float* z, float c, Online& o) {
-    float zm = z[0];
+    const float zm = max_of<N>(z);
+    const float r = max2f(o.m, ceilf(zm * c));
+    o.s = rescale(o.s, o.m, r);  // exact; the identity when the reference stays
+    o.m = r;
+    float e[N];
 #pragma unroll
-    for (int k = 1; k < N; ++k) zm = fmaxf(zm, z[k]);
-    const float ym = zm * c;
-    if (ym > o.m) {
-        o.s = (o.m == -INFINITY) ? 0.0 : o.s * (double)ex2(o.m - ym);
-        o.m = ym;
-    }
-    if (o.m == -INFINITY) return;  // all -inf so far: nothing to add (and no -inf - -inf)
-    float part = 0.0f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) part += ex2(fmaf(z[k], c, -o.m));
-    o.s += (double)part;
+    for (int k = 0; k < N; ++k) e[k] = ex2(fmaf(z[k], c, -o.m));
+    o.s += (double)tree_sum<N>(e);
 }
+
+__device__ __forceinline__ void online_add4(const float z[4], float c, Online& o) { online_addn<4>(z, c, o); }
 
 __device__ __forceinline__ void online_merge(Online& a, float m2, double s2) {
     const float mm = fmaxf(a.m, m2);
-    const double x = (a.m == -INFINITY) ? 0.0 : a.s * (double)ex2(a.m - mm);
-    const double y = (m2 == -INFINITY) ? 0.0 : s2 * (double)ex2(m2 - mm);
+    a.s = rescale(a.s, a.m, mm) + rescale(s2, m2, mm);
     a.m = mm;
-    a.s = x + y;
 }
 
 // Wave-wide merge (same butterfly as the other reductions); result uniform.
@@ -458,7 +505,7 @@ __device__ void span_stats(const void* zt, const void* zd, int64_t x0, int len, 
     using L = Logit4<BF16>;
     constexpr int NT = NW * kWave;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    Online ot{-INFINITY, 0.0}, od{-INFINITY, 0.0};
+    Online ot{kNoRef, 0.0}, od{kNoRef, 0.0};
     if (VEC) {
         // Software-pipelined: the next U quads of the row(s) are in flight while
         // the current ones are consumed.
@@ -522,10 +569,10 @@ __device__ void span_stats(const void* zt, const void* zd, int64_t x0, int len, 
         lds->s[1][wave] = od.s;
     }
     __syncthreads();
-    rt = Online{lane < NW ? lds->m[0][lane] : -INFINITY, lane < NW ? lds->s[0][lane] : 0.0};
+    rt = Online{lane < NW ? lds->m[0][lane] : kNoRef, lane < NW ? lds->s[0][lane] : 0.0};
     wave_online(rt);
     if (D) {
-        rd = Online{lane < NW ? lds->m[1][lane] : -INFINITY, lane < NW ? lds->s[1][lane] : 0.0};
+        rd = Online{lane < NW ? lds->m[1][lane] : kNoRef, lane < NW ? lds->s[1][lane] : 0.0};
         wave_online(rd);
     }
 }
@@ -652,7 +699,7 @@ __device__ void sliced_row_stats(unsigned long long* set, int G, int g, int Ls, 
         }
         __syncthreads();
     }
-    Online rt{-INFINITY, 0.0}, rd{-INFINITY, 0.0};
+    Online rt{kNoRef, 0.0}, rd{kNoRef, 0.0};
     for (int k = 0; k < G; ++k) {
         merge_packed(rt, s_words[2 * k]);
         if (D) merge_packed(rd, s_words[2 * k + 1]);

@@ -155,6 +155,44 @@ def test_accept_logits_edge_cases(sv, dtype, V):
     assert n[4] == 0 and n[7] == 0 and n[5] <= 1
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_accept_logits_masked_and_shifted_rows(sv, dtype, path):
+    """Masked vocabularies (-inf logits, as top-k masking leaves them) and rows
+    shifted far from zero. -inf ids have probability 0 in both rows; a draft
+    token at an id the draft masks but the target does not is accepted
+    (q(t) = 0 < p(t)), one both mask is rejected. A constant shift of a row's
+    logits leaves its softmax unchanged, so the kernel's running reference must
+    follow logits near -1e4 or +1e4 as well as near 0."""
+    g = torch.Generator().manual_seed(21)
+    B, K, V, T = 12, 4, 70001, 0.9
+    zt = 3 * torch.randn(B, K + 1, V, generator=g)
+    zd = zt[:, :K] + torch.randn(B, K, V, generator=g)
+    mask = torch.rand(B, 1, V, generator=g) < 0.3
+    zt = zt.masked_fill(mask, float("-inf"))
+    zd = zd.masked_fill(mask, float("-inf"))
+    zd[1, 0, :100] = float("-inf")             # masked by the draft only
+    zt[2, 0, :100] = float("-inf")             # masked by the target only
+    zt[4] -= 1e4                               # shifted rows (bf16 keeps ~3 digits: the rows change,
+    zd[4] -= 1e4                               # the oracle sees the same stored values)
+    zt[5] += 1e4
+    zd[5] += 1e4
+    zt[6, :, : V // 2] = float("-inf")          # the first half of every row masked
+    zd[6, :, : V // 2] = float("-inf")
+    q = torch.softmax(zd.double() / T, -1)
+    tok = torch.multinomial(q.reshape(-1, V), 1, generator=g).reshape(B, K).int()
+    tok[1, 0] = int(torch.nonzero(~mask[1, 0, :100])[0])  # draft masks it, target does not: accepted
+    tok[2, 0] = 7                              # target masks it: p(t) = 0, rejected
+    tok[3, 0] = int(torch.nonzero(mask[3, 0])[0])  # both mask it: rejected
+    u = torch.rand(B, K + 1, generator=g)
+    zt, zd = zt.to(dtype), zd.to(dtype)
+    n, nx, _ = compare(sv, dev(zt), dev(zd), dev(tok), dev(u), None, T, f"masked-{dtype}-{path}", path=path)
+    assert n[1] >= 1 and n[2] == 0 and n[3] == 0
+    live = ~torch.isinf(zt.float())
+    for b in range(B):  # the emitted token is never a masked id of the row it is drawn from
+        assert bool(live[b, n[b], nx[b]]), (b, n[b], nx[b])
+
+
 def test_accept_logits_k0_identical_rows_and_bonus(sv):
     """K = 0: the bonus token is drawn from the target row alone; with identical
     target and draft rows every draft is accepted and the bonus is drawn from
