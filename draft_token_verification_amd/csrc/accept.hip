@@ -43,7 +43,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kSub = 4 * kWave;     // elements per sub-block: 4 per lane
 constexpr int kMaxSeg = 7936;       // segment totals kept in LDS (62 KiB)
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -435,30 +434,6 @@ __device__ __forceinline__ float tree_sum(const float* e) {
 
 // N elements at once: one max, at most one (exact) rescale, one fp32 partial
 // sum and one binary64 add per N elements.
-// The largest of three floats in one instruction. Written out because
-// fmaxf on values that come from bit operations (unpacked bf16) or straight
-// from memory makes the compiler quiet each operand with an extra max first.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
-__device__ __forceinline__ float max2f(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-
-template <int N>
-__device__ __forceinline__ float max_of(const float* z) {
-    static_assert(N >= 2, "");
-    float r = max3f(z[0], z[1], N > 2 ? z[2] : z[1]);
-#pragma unroll
-    for (int k = 3; k < N; k += 2) r = max3f(r, z[k], z[k + 1 < N ? k + 1 : k]);
-    return r;
-}
-
 template <int N>
 __device__ __forceinline__ void online_addn(const float* z, float c, Online& o) {
     const float zm = max_of<N>(z);

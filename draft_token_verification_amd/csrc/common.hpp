@@ -9,6 +9,7 @@ namespace sv {
 
 constexpr int kWave = 64;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -104,6 +105,30 @@ __device__ __forceinline__ double wave_incl_scan_d(double x, int lane) {
         if (lane >= d) x += y;
     }
     return x;
+}
+
+// The largest of three floats in one instruction. Written out because
+// fmaxf on values that come from bit operations (unpacked bf16) or straight
+// from memory makes the compiler quiet each operand with an extra max first.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ float max_of(const float* z) {
+    static_assert(N >= 2, "");
+    float r = max3f(z[0], z[1], N > 2 ? z[2] : z[1]);
+#pragma unroll
+    for (int k = 3; k < N; k += 2) r = max3f(r, z[k], z[k + 1 < N ? k + 1 : k]);
+    return r;
 }
 
 // ---- softmax statistics in the log2 domain --------------------------------

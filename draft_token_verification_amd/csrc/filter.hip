@@ -41,8 +41,11 @@
 // The paths agree exactly except for top-p without top-k, where the common
 // path takes the whole row's mass from the fp32 statistics (relative error
 // ~1e-6) instead of an exact sum. The last pass writes 2^y / S_kept for kept
-// ids and 0 elsewhere. Passes after the first re-read the row from the caches
-// in front of HBM.
+// ids and 0 elsewhere. When the common path decides, the candidates' element
+// ids (kept beside their keys) mark the quads of four elements that hold a
+// kept id in a bit map in LDS, and the last pass writes every other quad as
+// zeros without reading it: the row is read from HBM once. The general path's
+// passes, and the last pass without the map, re-read the row.
 #include <math.h>
 
 #include <type_traits>
@@ -161,7 +164,9 @@ __device__ __forceinline__ void for_each(const void* row, int V, F&& f) {
 
 struct FilterLds {
     uint32_t cnt[kWaves][kBins];             // also: the candidate keys (kCand of them)
-    unsigned long long mass[kWaves][kBins];  // also: the candidates' exclusive prefix masses
+    unsigned long long mass[kWaves][kBins];  // also: the candidates' exclusive prefix masses, then the
+                                             // map of the quads that hold a kept id
+    uint32_t ids[kWaves * kBins];            // the candidates' element ids, beside their keys
     uint32_t tcnt[kBins];
     unsigned long long tmass[kBins];
     unsigned long long wmass[2][kWaves];  // per-wavefront partials of the threshold searches
@@ -268,25 +273,28 @@ __device__ __forceinline__ float wave_max_f(float m) {
     return fmaxf(readlane_f(m, 0), readlane_f(m, 32));
 }
 
-// Keep the entries of a wavefront's candidate buffer whose key is above fkey
-// and whose logit lies within kSpan log2 units of `run`, packed to the front.
-// Wave-local.
+// Keep the entries of a wavefront's candidate buffer (keys in buf, element
+// ids in ibuf) whose key is above fkey and whose logit lies within kSpan log2
+// units of `run`, packed to the front. Wave-local and in place, 64 entries
+// per step: a step's writes land below the entries of every later step, and
+// the wavefront reads a step's entries before it writes any of them.
 template <bool BF16>
-__device__ __forceinline__ int wave_compact(uint32_t* buf, int cnt, float c, float run, uint32_t fkey) {
+__device__ __forceinline__ int wave_compact(uint32_t* buf, uint32_t* ibuf, int cnt, float c, float run,
+                                            uint32_t fkey) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t e[kWaveCap / kWave];
-    bool keep[kWaveCap / kWave];
-#pragma unroll
-    for (int q = 0; q < kWaveCap / kWave; ++q) {
-        const int i = q * kWave + lane;
-        e[q] = i < cnt ? buf[i] : 0u;
-        keep[q] = i < cnt && e[q] > fkey && fmaf(value_of<BF16>(e[q]), c, -run) > -kSpan;
-    }
     int n = 0;
 #pragma unroll
     for (int q = 0; q < kWaveCap / kWave; ++q) {
-        const uint64_t m = __ballot(keep[q]);
-        if (keep[q]) buf[n + __popcll(m & ((1ull << lane) - 1ull))] = e[q];
+        const int i = q * kWave + lane;
+        const uint32_t e = i < cnt ? buf[i] : 0u;
+        const uint32_t id = i < cnt ? ibuf[i] : 0u;
+        const bool keep = i < cnt && e > fkey && fmaf(value_of<BF16>(e), c, -run) > -kSpan;
+        const uint64_t m = __ballot(keep);
+        if (keep) {
+            const int at = n + __popcll(m & ((1ull << lane) - 1ull));
+            buf[at] = e;
+            ibuf[at] = id;
+        }
         n += __popcll(m);
     }
     return n;
@@ -326,7 +334,8 @@ __device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int
 // the floor rises so that at most 64 of the buffer's and the step's entries
 // stay above it. Entries only ever leave for being below the row's window or
 // the floor, so at the end the set {key > F, y > Mc - kSpan} (F: the highest
-// floor) is complete: those ids are packed into cand[0 .. nc) (any order).
+// floor) is complete: their keys are packed into cand[0 .. nc) (any order)
+// and their element ids into ids[0 .. nc) in the same order.
 // The per-element test is one float comparison against the larger of the
 // window's lower end (rounded down by a safe margin, so the gather never
 // misses an id the final set holds) and the value of the floor's key.
@@ -336,6 +345,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
     using E = Elems<BF16>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     uint32_t* buf = &L->cnt[0][0] + wave * kWaveCap;
+    uint32_t* ibuf = L->ids + wave * kWaveCap;
     const float inv_c = 1.0f / c;
     float om = -INFINITY, os = 0.0f;  // this lane's online statistics
     float run = -INFINITY;            // the wavefront's running maximum (log2 units)
@@ -354,7 +364,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
         zlo = (run - kSpan - 1e-3f) * inv_c;
         zlo = run == -INFINITY ? -INFINITY : zlo - fabsf(zlo) * 1e-6f;
     };
-    auto take = [&](const float* z, auto n_const) {
+    auto take = [&](const float* z, auto n_const, int id0) {  // z[e] is element id0 + e
         constexpr int n = decltype(n_const)::value;
         float thr = fmaxf(zlo, zf);
         bool any = false;
@@ -370,12 +380,12 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
             need += __popcll(__ballot(w));
         }
         if (cnt + need > kWaveCap) {  // rare: make room once for the whole step
-            cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
+            cnt = wave_compact<BF16>(buf, ibuf, cnt, c, run, fkey);
             if (cnt + need > kWaveCap) {
                 // raise the floor so that at most 64 entries remain above it
                 fkey = max(fkey, wave_floor<BF16, n>(buf, cnt, kWaveCap / 4, z, want));
                 zf = value_of<BF16>(fkey);
-                cnt = wave_compact<BF16>(buf, cnt, c, run, fkey);
+                cnt = wave_compact<BF16>(buf, ibuf, cnt, c, run, fkey);
                 thr = fmaxf(zlo, zf);
                 want = 0u;
 #pragma unroll
@@ -386,7 +396,11 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
         for (int e = 0; e < n; ++e) {
             const bool w = (want >> e) & 1u;
             const uint64_t m = __ballot(w);
-            if (w) buf[cnt + __popcll(m & ((1ull << lane) - 1ull))] = key_of<BF16>(z[e]);
+            if (w) {
+                const int at = cnt + __popcll(m & ((1ull << lane) - 1ull));
+                buf[at] = key_of<BF16>(z[e]);
+                ibuf[at] = (uint32_t)(id0 + e);
+            }
             cnt += __popcll(m);
         }
     };
@@ -423,7 +437,8 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
             }
             update_run(z, std::integral_constant<int, N>{});
 #pragma unroll
-            for (int u = 0; u < U; ++u) take(z + u * E::N, std::integral_constant<int, E::N>{});
+            for (int u = 0; u < U; ++u)
+                take(z + u * E::N, std::integral_constant<int, E::N>{}, (j0 + u * kThreads + tid) * E::N);
         }
     } else {
         for (int x0 = 0; x0 < V; x0 += kThreads) {
@@ -431,7 +446,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
             float z[1] = {in ? E::at(zrow, x0 + tid) : -INFINITY};
             if (stats) online_addf<1>(z, c, om, os);
             update_run(z, std::integral_constant<int, 1>{});
-            take(z, std::integral_constant<int, 1>{});
+            take(z, std::integral_constant<int, 1>{}, x0 + tid);
         }
     }
     // the row's statistics (without `stats`, the maximum is the running one)
@@ -456,7 +471,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
     for (int w = 0; w < kWaves; ++w) F = max(F, (uint32_t)L->wcnt[w]);
     __syncthreads();  // wcnt is reused below
     // final filter against the row's window and the highest floor, then pack
-    const int kept = wave_compact<BF16>(buf, cnt, c, Mc, F);
+    const int kept = wave_compact<BF16>(buf, ibuf, cnt, c, Mc, F);
     if (lane == 0) L->wcnt[wave] = kept;
     __syncthreads();
     int off = 0, total = 0;
@@ -464,18 +479,22 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
         if (w < wave) off += L->wcnt[w];
         total += L->wcnt[w];
     }
-    uint32_t e[kWaveCap / kWave];
+    uint32_t e[kWaveCap / kWave], id[kWaveCap / kWave];
 #pragma unroll
     for (int q = 0; q < kWaveCap / kWave; ++q) {
         const int i = q * kWave + lane;
         e[q] = i < kept ? buf[i] : 0u;
+        id[q] = i < kept ? ibuf[i] : 0u;
     }
     __syncthreads();  // every wavefront holds its entries before any moves
     uint32_t* cand = &L->cnt[0][0];
 #pragma unroll
     for (int q = 0; q < kWaveCap / kWave; ++q) {
         const int i = q * kWave + lane;
-        if (i < kept) cand[off + i] = e[q];
+        if (i < kept) {
+            cand[off + i] = e[q];
+            L->ids[off + i] = id[q];
+        }
     }
     __syncthreads();
     nc = total;
@@ -508,6 +527,32 @@ __device__ __forceinline__ void sort_desc(uint32_t* keys, int P) {
     }
 }
 
+constexpr int kMapWords = kWaves * kBins * 2;  // the kept-quad map: 32-bit words over the mass array
+
+// The map of the quads (4 consecutive elements) that hold a kept id: bit q of
+// map[] is set iff some candidate with key >= tau has its id in quad q. It
+// covers the whole row when the candidates hold every kept id (the common
+// path decided). `key`/`valid` are the caller's candidates (entry
+// j * kThreads + tid), ids[] their element ids. Contains barriers; the map's
+// memory (the mass array) must be free on entry.
+template <int kPer>
+__device__ __forceinline__ void mark_kept_quads(const uint32_t* key, const bool* valid, uint32_t tau,
+                                                const uint32_t* ids, int nquads, uint32_t* map) {
+    const int tid = threadIdx.x;
+    const int nw = (nquads + 31) / 32;
+    __syncthreads();
+    for (int i = tid; i < nw; i += kThreads) map[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (valid[j] && key[j] >= tau) {
+            const uint32_t q = ids[j * kThreads + tid] / 4u;
+            atomicOr(&map[q / 32u], 1u << (q % 32u));
+        }
+    }
+    __syncthreads();
+}
+
 // Thresholds from the nc candidates in cand[] (every key above the gather's
 // cut): tau (smallest kept key) and s_kept (fixed-point mass of the kept
 // ids). Each thread holds up to 4 candidates in registers.
@@ -520,11 +565,13 @@ __device__ __forceinline__ void sort_desc(uint32_t* keys, int P) {
 // S_total is the row's mass in fixed-point units (the top-p reference without
 // top-k). Returns false when the candidates cannot decide: fewer than k of
 // them, or (top-p alone) a nucleus that keeps every candidate and may reach
-// past them. Contains barriers.
+// past them. When it decides and `map` is set (the row's quads fit the map),
+// it also builds the kept-quad map in the mass array and sets `mapped`.
+// Contains barriers.
 template <bool BF16>
 __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float Mc, int fxs, bool kon, int k, bool pon,
-                                                  float pp, double S_total, FilterLds* L, uint32_t& tau,
-                                                  double& s_kept) {
+                                                  float pp, double S_total, FilterLds* L, bool map, uint32_t& tau,
+                                                  double& s_kept, bool& mapped) {
     constexpr int kPer = kCand / kThreads;
     constexpr int kBits = BF16 ? 16 : 32;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -576,9 +623,14 @@ __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float 
             if (count_ge(t) >= k) kth = t;
         }
     }
+    uint32_t* kmap = (uint32_t*)&L->mass[0][0];
     if (!pon) {
         tau = kth;
         s_kept = (double)mass_ge(kth);
+        if (map && tau != 0u) {
+            mark_kept_quads<kPer>(key, valid, tau, L->ids, V / 4, kmap);
+            mapped = true;
+        }
         return true;
     }
     // pack the survivors (keys >= kth) to the front of cand[], then sort them
@@ -654,6 +706,10 @@ __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float 
     // top-p alone: if no candidate is dropped, ids below the cut may belong
     if (!kon && nc < V && count_ge(tau) == nc) return false;
     s_kept = (double)mass_ge(tau);
+    if (map && tau != 0u) {  // the prefix masses in the mass array were last read before istar's barrier
+        mark_kept_quads<kPer>(key, valid, tau, L->ids, V / 4, kmap);
+        mapped = true;
+    }
     return true;
 }
 
@@ -747,19 +803,22 @@ __device__ __forceinline__ void radix_thresholds(const void* zrow, int V, float 
 // Final pass: normalised kept probabilities, zeros elsewhere. Kept means
 // key >= tau, tested as z >= the logit of tau (keys order like the logits
 // and equal logits have equal keys); a quad of four consecutive elements with
-// nothing kept in the whole wavefront skips the exponentials. Each lane takes
-// 4 consecutive elements, so every store instruction of a wavefront covers
-// 1 KB of the output contiguously (no partially written lines).
+// nothing kept in the whole wavefront skips the exponentials. With the
+// kept-quad map (VEC rows only), a quad whose bit is clear is written as
+// zeros without being read, so the row is read again only where it keeps
+// something. Each lane takes 4 consecutive elements, so every store
+// instruction of a wavefront covers 1 KB of the output contiguously (no
+// partially written lines).
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void write_filtered(const void* zrow, float* prow, int V, float c, float Mc, int fxs,
-                                               uint32_t tau, double s_kept) {
+                                               uint32_t tau, double s_kept, const uint32_t* map) {
     const int tid = threadIdx.x;
     const float inv = (float)(ldexp(1.0, fxs) / s_kept);
     const float zt = tau == 0u ? -INFINITY : value_of<BF16>(tau);
     auto prob = [&](float zz) { return zz >= zt ? ex2(fmaf(zz, c, -Mc)) * inv : 0.0f; };
     if (VEC) {
         constexpr int kU = BF16 ? 8 : 4;  // 64 bytes of logits per lane in flight
-        using Raw = typename std::conditional<BF16, uint2, float4>::type;
+        using Raw = typename std::conditional<BF16, u32x2, f32x4>::type;  // native vectors: selects stay in registers
         f32x4* out = (f32x4*)prow;
         const Raw* in = (const Raw*)zrow;
         const int nq = V / 4;
@@ -780,15 +839,25 @@ __device__ __forceinline__ void write_filtered(const void* zrow, float* prow, in
             if (__ballot(any) == 0ull) return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             return f32x4{prob(z[0]), prob(z[1]), prob(z[2]), prob(z[3])};
         };
+        Raw none;  // -inf logits: nothing kept
+        if constexpr (BF16) {
+            none = u32x2{0xFF80FF80u, 0xFF80FF80u};
+        } else {
+            none = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+        auto fetch = [&](int q) {
+            const bool hit = map == nullptr || ((map[q >> 5] >> (q & 31)) & 1u);
+            return hit ? in[q] : none;
+        };
         int j = tid;
         for (; j + (kU - 1) * kThreads < nq; j += kU * kThreads) {
             Raw r[kU];
 #pragma unroll
-            for (int u = 0; u < kU; ++u) r[u] = in[j + u * kThreads];
+            for (int u = 0; u < kU; ++u) r[u] = fetch(j + u * kThreads);
 #pragma unroll
             for (int u = 0; u < kU; ++u) store_nt(out + j + u * kThreads, quad(r[u]));
         }
-        for (; j < nq; j += kThreads) store_nt(out + j, quad(in[j]));
+        for (; j < nq; j += kThreads) store_nt(out + j, quad(fetch(j)));
     } else {
         for (int x = tid; x < V; x += kThreads) prow[x] = prob(Elems<BF16>::at(zrow, x));
     }
@@ -819,20 +888,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     gather_pass<BF16, VEC>(zrow, V, c, !kon, &L, Mc, S, nc);  // top-k rows need no row sum
     uint32_t tau = 0u;
     double s_kept = 0.0;
-    bool decided = false;
+    bool decided = false, mapped = false;
     if (!kon && !pon) {  // no filter: the plain softmax
         s_kept = (double)S * ldexp(1.0, fxs);
         decided = true;
     } else {
-        decided = select_thresholds<BF16>(nc, V, c, Mc, fxs, kon, k, pon, pp, (double)S * ldexp(1.0, fxs), &L, tau,
-                                          s_kept);
+        const bool map = VEC && V / 4 <= kMapWords * 32;
+        decided = select_thresholds<BF16>(nc, V, c, Mc, fxs, kon, k, pon, pp, (double)S * ldexp(1.0, fxs), &L, map,
+                                          tau, s_kept, mapped);
     }
     if (!decided) {
         unsigned long long sk = 0;
         radix_thresholds<BF16, VEC>(zrow, V, c, Mc, fxs, kon, k, pon, pp, &L, tau, sk);
         s_kept = (double)sk;
     }
-    write_filtered<BF16, VEC>(zrow, prow, V, c, Mc, fxs, tau, s_kept);
+    write_filtered<BF16, VEC>(zrow, prow, V, c, Mc, fxs, tau, s_kept, mapped ? (const uint32_t*)&L.mass[0][0] : nullptr);
 }
 
 }  // namespace

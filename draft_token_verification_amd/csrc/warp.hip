@@ -40,7 +40,6 @@ constexpr int kUnroll = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCoopMaxG = 64;                       // slices per row the cooperative path accepts
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
