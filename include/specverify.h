@@ -139,10 +139,13 @@ sv_status sv_set_wait_limit(int32_t polls);
  * Kept sets are decided exactly for top-k; top-p decides with fixed-point
  * masses (2^-40 or finer per unit) of fp32 exponentials, so a value within
  * ~1e-5 relative of its threshold may fall either way. Results are bitwise
- * identical run to run. No workspace; one workgroup per live row, two passes
- * over it when the kept ids lie within 20 log2 units of the row maximum
- * (more otherwise). Rows with neither filter are correct but pay the filter
- * machinery: sv_softmax_warp is the faster call for them.
+ * identical run to run. No workspace; one workgroup per live row. When the
+ * kept ids lie within 20 log2 units of the row maximum, the row is read once
+ * and the output written once (for rows of up to 1,048,576 elements with V a
+ * multiple of 8 (bf16) or 4 (fp32) and 16-byte aligned logits and probs);
+ * otherwise the row is read several times. Rows with neither filter are
+ * correct but pay the filter machinery: sv_softmax_warp is the faster call
+ * for them.
  * Errors: as sv_softmax_warp, plus misaligned top_k / top_p.
  */
 sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
