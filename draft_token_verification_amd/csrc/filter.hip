@@ -352,6 +352,26 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
     uint32_t fkey = 0u;               // the wavefront's key floor
     float zf = -INFINITY;             // the logit of the floor's key (-inf: no floor)
     int cnt = 0;                      // entries in buf (wave-uniform)
+    // The wavefronts' floors, published in LDS: a floor bounds the final set
+    // (only keys above the highest floor remain), so each wavefront adopts
+    // the highest published one before it takes elements. Reading a stale,
+    // lower value only lets more elements in.
+    uint32_t* floors = (uint32_t*)L->wcnt;
+    if (lane == 0) floors[wave] = 0u;
+    __syncthreads();
+    auto adopt_floor = [&]() {
+        uint32_t g = lane < kWaves ? __hip_atomic_load(&floors[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                   : 0u;
+        g = max(g, (uint32_t)dpp_i<kDppQuadXor1>((int)g));
+        g = max(g, (uint32_t)dpp_i<kDppQuadXor2>((int)g));
+        g = max(g, (uint32_t)dpp_i<kDppRowHalfMirror>((int)g));
+        g = max(g, (uint32_t)dpp_i<kDppRowMirror>((int)g));  // lanes 0..15 hold the highest floor
+        g = (uint32_t)readlane_i((int)g, 0);
+        if (g > fkey) {
+            fkey = g;
+            zf = value_of<BF16>(g);
+        }
+    };
     // out-of-row elements come in as -inf: never above a threshold
     // running maximum first, so that the test in take() is as tight as possible
     float zlo = -INFINITY;  // the window's lower end for the current step
@@ -385,6 +405,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
                 // raise the floor so that at most 64 entries remain above it
                 fkey = max(fkey, wave_floor<BF16, n>(buf, cnt, kWaveCap / 4, z, want));
                 zf = value_of<BF16>(fkey);
+                if (lane == 0) __hip_atomic_store(&floors[wave], fkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 cnt = wave_compact<BF16>(buf, ibuf, cnt, c, run, fkey);
                 thr = fmaxf(zlo, zf);
                 want = 0u;
@@ -436,6 +457,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
                 for (int u = 0; u < U; ++u) online_addf<E::N>(z + u * E::N, c, om, os);
             }
             update_run(z, std::integral_constant<int, N>{});
+            adopt_floor();
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 take(z + u * E::N, std::integral_constant<int, E::N>{}, (j0 + u * kThreads + tid) * E::N);
@@ -446,6 +468,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
             float z[1] = {in ? E::at(zrow, x0 + tid) : -INFINITY};
             if (stats) online_addf<1>(z, c, om, os);
             update_run(z, std::integral_constant<int, 1>{});
+            adopt_floor();
             take(z, std::integral_constant<int, 1>{}, x0 + tid);
         }
     }
@@ -454,7 +477,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
     if (lane == 0) {
         L->wmax[wave] = stats ? om : run;
         L->wsum_f[wave] = os;
-        L->wcnt[wave] = (int)fkey;
+        __hip_atomic_store(&floors[wave], fkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     om = lane < kWaves ? L->wmax[lane] : -INFINITY;
