@@ -18,6 +18,7 @@ workload on the host's cores.
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -353,7 +354,10 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
     FETCH_SIZE reports about half the bytes a copy reads, WRITE_SIZE all of
     them. The roofline's figure is the warp's fast-path kernel, its two
     launches per step (target rows, draft rows) averaged like ``achieved``;
-    every other library kernel is recorded per launch shape beside it.
+    every other library kernel is recorded per launch shape beside it. A
+    shape's figure is the median over its launches: the run also makes
+    launches outside the step with the same shape but other traffic (the
+    greedy verify over every row, for the stream-read rate).
     """
     import csv
     import re
@@ -378,7 +382,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
         if not warp or not big:
             raise SystemExit(f"{path}: no warp kernel or calibration-copy dispatches with {counter}")
         factor = COPY_BYTES / (sum(big) / len(big))
-        avg = {kg: sum(v) / len(v) * factor for kg, v in per.items()}
+        avg = {kg: statistics.median(v) * factor for kg, v in per.items()}
         per_launch = sum(avg[("warp_coop_kernel", g)] for g in warp) / len(warp)
         return factor, per_launch, avg
 
