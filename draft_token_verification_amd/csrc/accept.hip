@@ -20,8 +20,9 @@
 // probability row is ever written (the sampled verify needs the target
 // distribution only at the positions it examines; blog, section 22).
 //  1. For i = 0, 1, ... in order, one pass over target row i and draft row i
-//     gives each row's log2-domain (max, sum) (online, per lane, merged with
-//     DPP and LDS); p_i(t_i) and q_i(t_i) follow from the two logits at t_i,
+//     gives each row's log2-domain statistics (m, sum of 2^(y - m)), m an
+//     integer at or above the row maximum (online, per lane, merged with DPP
+//     and LDS); p_i(t_i) and q_i(t_i) follow from the two logits at t_i,
 //     and the test u*q < p runs in binary64. The loop stops at the first
 //     rejection, so rows after it are never read.
 //
@@ -471,7 +472,7 @@ struct StatsLds {
     double s[2][kWaves];
 };
 
-// Online (max, sum) of elements [x0, x0 + len) of target row zt and (D) draft
+// Online statistics (m, s) of elements [x0, x0 + len) of target row zt and (D) draft
 // row zd, merged over the NW wavefronts of the workgroup: rt and rd are
 // uniform. For VEC, x0 and len are multiples of 4. Contains barriers.
 template <bool BF16, bool VEC, bool D, int NW, int UD = 4>
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
 // The same procedure as accept_logits_kernel, with the rows of a sequence
 // split into G slices of Ls elements; workgroup (b, g) of 256 lanes owns
 // slice g of every row of sequence b. At each examined position the G
-// workgroups publish their slices' (max, sum) of the target and draft rows
+// workgroups publish their slices' statistics (m, s) of the target and draft rows
 // into sentinel-filled slots of the caller's workspace and merge all G in a
 // fixed order, so every slice takes the same accept decision; for the draw
 // each publishes its slice's total weight, all find the slice holding u * S,
@@ -857,8 +858,8 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
 // sequence's slices together), each slice at least 32768 elements (shorter
 // slices spend more on the exchanges than they save); Ls is a multiple of 1024
 // elements and every slice is non-empty. Measured on MI355X at B = 512,
-// K = 16, V = 256000 (G = 8) for the fused sampled verify: 0.58 ms, against
-// 0.63 (G = 4) and 0.79 (G = 2).
+// K = 16, V = 256000 for the fused sampled verify: G = 8 about 8% faster than
+// G = 4 and 27% faster than G = 2.
 void coop_slice_shape(int B, int V, int& G, int& Ls) {
     int g = 4096 / (B > 0 ? B : 1);
     g = g < 1 ? 1 : (g > kMaxSlices ? kMaxSlices : g);
