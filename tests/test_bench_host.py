@@ -2,8 +2,9 @@
 
 The counters are KiB per dispatch; each is scaled so that the calibration copy
 of COPY_BYTES reads (and writes) COPY_BYTES. Synthetic CSVs with known values
-check the scaling, the per-shape averaging and that only the warp's fast-path
-kernel feeds the roofline figure.
+check the scaling, the per-shape medians (launches outside the timed step, such
+as the greedy verify over every row, share a shape with the step's own) and
+that only the warp's fast-path kernel feeds the roofline figure.
 """
 import csv
 import json
@@ -30,9 +31,11 @@ def test_traffic_from_counters(tmp_path):
     copy_kib = bench.COPY_BYTES / 1024
     coop = "void sv::(anonymous namespace)::warp_coop_kernel<true>(unsigned short const*, int)"
     filt = "void sv::(anonymous namespace)::warp_filter_kernel<true, true>(void const*, int)"
+    greedy = "void sv::(anonymous namespace)::greedy_sliced_kernel<true, false>(void const*, int)"
     copy = "__amd_rocclr_copyBuffer"
     # FETCH_SIZE sees half of every read, WRITE_SIZE all of every write
     fetch = [(coop, 1000, 100.0), (coop, 1000, 110.0), (coop, 2000, 300.0), (filt, 3000, 999.0),
+             (greedy, 4000, 10.0), (greedy, 4000, 10.0), (greedy, 4000, 12.0), (greedy, 4000, 500.0),
              (copy, 64, copy_kib / 2), (copy, 64, copy_kib / 2), (copy, 64, 1.0)]
     write = [(coop, 1000, 50.0), (coop, 1000, 50.0), (coop, 2000, 70.0), (filt, 3000, 5.0),
              (copy, 64, copy_kib), (copy, 64, 2.0)]
@@ -49,5 +52,7 @@ def test_traffic_from_counters(tmp_path):
     assert rec["per_grid"]["1000"] == {"fetch": int(105 * 1024 * 2), "write": 50 * 1024}
     # the filtered warp is recorded on its own, never mixed into the roofline figure
     assert rec["kernels"]["warp_filter_kernel"]["3000"] == {"fetch": int(999 * 1024 * 2), "write": 5 * 1024}
+    # the step's greedy launches, not the one full read that shares their shape
+    assert rec["kernels"]["greedy_sliced_kernel"]["4000"]["fetch"] == int(11.0 * 1024 * 2)
     assert rec["kernel_source_sha"] == bench.kernel_source_sha()
     assert rec["library_source_sha"] == bench.kernel_source_sha(all_sources=True)
