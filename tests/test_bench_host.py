@@ -45,7 +45,7 @@ def test_traffic_from_counters(tmp_path):
     bench.traffic_from_counters(str(fp), str(wp), "wl", str(out))
     rec = json.loads(out.read_text())
     assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
-    # warp: shape 1000 averages 105 KiB fetched, shape 2000 300 KiB; the two shapes averaged, x2
+    # warp: shape 1000 gives 105 KiB fetched (median of 100 and 110), shape 2000 300 KiB; the two shapes averaged, x2
     assert rec["fetch_bytes_per_launch"] == int((105 + 300) / 2 * 1024 * 2)
     assert rec["write_bytes_per_launch"] == int((50 + 70) / 2 * 1024)
     assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
