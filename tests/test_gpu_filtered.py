@@ -117,6 +117,34 @@ def test_filtered_warp_parity_reduced(sv, case):
     check(sv, batch.draft, batch.temperature, batch.lens, 0, tk, tp, case_id(case) + "/draft")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_filtered_warp_kept_ids_at_map_edges(sv, dtype):
+    """Kept ids placed where the kept-quad map has its edges: the first and the
+    last quad of the row, the last quad of one 32-bit map word and the first of
+    the next (ids 124-131), and a long run of kept quads; the rest of each row
+    is far below them. The write pass reads only marked quads, so every kept id
+    must come out right and every other id exactly 0."""
+    g = torch.Generator().manual_seed(31)
+    B, V, T = 6, 4096 * 3, 1.0
+    rows = -20.0 + torch.randn(B, V, generator=g)
+    marks = [
+        [0, 1, 2, 3],                      # the first quad
+        [V - 4, V - 3, V - 2, V - 1],      # the last quad
+        [124, 127, 128, 131],              # both sides of a map word boundary
+        [0, V - 1],                        # first and last element only
+        list(range(512, 1024, 4)),         # 128 quads in a row, one id each
+        list(range(2000, 2064)),           # 16 whole quads
+    ]
+    ks = np.zeros(B, dtype=np.int32)
+    for b, ids in enumerate(marks):
+        rows[b, ids] = 5.0 + torch.arange(len(ids), dtype=torch.float32) * 0.01
+        ks[b] = len(ids)
+    z = rows.reshape(B, 1, V).to(dtype).cuda()
+    for kk, pp in [(ks, np.full(B, 1.0, np.float32)), (ks, np.full(B, 0.999, np.float32)),
+                   (np.zeros(B, np.int32), np.full(B, 0.9, np.float32))]:
+        check(sv, z, T, None, 1, kk, pp, f"map-edges-{dtype}")
+
+
 @pytest.mark.parametrize("k,p", [(50, 1.0), (0, 0.9), (50, 0.9), (1, 1.0), (0, 0.0)])
 def test_filtered_warp_full_size(sv, k, p):
     name = "logits-bf16-b256-k5-v128256"
