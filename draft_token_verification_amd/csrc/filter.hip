@@ -339,9 +339,11 @@ __device__ __forceinline__ uint32_t wave_floor(const uint32_t* buf, int cnt, int
 // The per-element test is one float comparison against the larger of the
 // window's lower end (rounded down by a safe margin, so the gather never
 // misses an id the final set holds) and the value of the floor's key.
+// Without `gather` (a row with neither filter) only the statistics are
+// formed and the list stays empty.
 template <bool BF16, bool VEC>
-__device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bool stats, FilterLds* L, float& Mc,
-                                            float& S, int& nc) {
+__device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bool stats, bool gather, FilterLds* L,
+                                            float& Mc, float& S, int& nc) {
     using E = Elems<BF16>;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     uint32_t* buf = &L->cnt[0][0] + wave * kWaveCap;
@@ -456,6 +458,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
 #pragma unroll
                 for (int u = 0; u < U; ++u) online_addf<E::N>(z + u * E::N, c, om, os);
             }
+            if (!gather) continue;  // a row with neither filter needs only the statistics
             update_run(z, std::integral_constant<int, N>{});
             adopt_floor();
 #pragma unroll
@@ -467,6 +470,7 @@ __device__ __forceinline__ void gather_pass(const void* zrow, int V, float c, bo
             const bool in = x0 + tid < V;
             float z[1] = {in ? E::at(zrow, x0 + tid) : -INFINITY};
             if (stats) online_addf<1>(z, c, om, os);
+            if (!gather) continue;
             update_run(z, std::integral_constant<int, 1>{});
             adopt_floor();
             take(z, std::integral_constant<int, 1>{}, x0 + tid);
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     // pass 1: the statistics and the candidate ids
     float Mc, S;
     int nc;
-    gather_pass<BF16, VEC>(zrow, V, c, !kon, &L, Mc, S, nc);  // top-k rows need no row sum
+    gather_pass<BF16, VEC>(zrow, V, c, !kon, kon || pon, &L, Mc, S, nc);  // top-k rows need no row sum
     uint32_t tau = 0u;
     double s_kept = 0.0;
     bool decided = false, mapped = false;
