@@ -53,8 +53,8 @@ def main():
         traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload, args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(sequences shard across GPUs with no exchange, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(sequences would shard across GPUs with no exchange between them)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
