@@ -20,8 +20,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers are device memory owned by the caller. The library never
- *    allocates, frees or retains them; the one scratch buffer it uses (the
- *    warp's workspace) is passed in by the caller too.
+ *    allocates, frees or retains them; its only scratch memory, the exchange
+ *    slots of sv_softmax_warp, sv_verify_greedy(_margin) and sv_accept_logits
+ *    (their `workspace` arguments), is passed in by the caller too.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
  *    stream) and return. Outputs are valid once the stream reaches them.
  *    Calls keep no state between them; concurrent calls on different streams
@@ -113,8 +114,9 @@ size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
  * partial results of the other workgroups that share its row or sequence
  * before computing them all itself (default 16384), for calls made after
  * this one. It governs sv_softmax_warp's fast path, and sv_accept_logits,
- * sv_verify_greedy and sv_verify_greedy_margin with a workspace. Any value gives the same results; 0 forces the
- * self-computation. Returns SV_ERR_INVALID_ARG for a negative value. */
+ * sv_verify_greedy and sv_verify_greedy_margin with a workspace. Any value
+ * gives the same results; 0 forces the self-computation. Returns
+ * SV_ERR_INVALID_ARG for a negative value. */
 sv_status sv_set_wait_limit(int32_t polls);
 
 /*
@@ -144,8 +146,7 @@ sv_status sv_set_wait_limit(int32_t polls);
  * and the output written once (for rows of up to 1,048,576 elements with V a
  * multiple of 8 (bf16) or 4 (fp32) and 16-byte aligned logits and probs);
  * otherwise the row is read several times. Rows with neither filter are
- * correct but pay the filter machinery: sv_softmax_warp is the faster call
- * for them.
+ * correct but read twice: sv_softmax_warp is the faster call for them.
  * Errors: as sv_softmax_warp, plus misaligned top_k / top_p.
  */
 sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
