@@ -158,19 +158,20 @@ __device__ __forceinline__ int span_argmax(const void* row, int x0, int len, flo
     }
     const typename R::Vec* vrow = (const typename R::Vec*)(span + head * (BF16 ? 2 : 4));
     const int base = x0 + head;
-    int j = tid;
-    if (j < nvec) {
-        R::template scan_first<M>(load_nt(vrow + j), base + j * E, best, bidx, second);
-        j += NT;
-    }
-    for (; j + (U - 1) * NT < nvec; j += U * NT) {
+    // Batches of U vectors per lane, all U loads issued before any is
+    // scanned, the last batch too (its loads past the span are skipped): a
+    // span of n vectors takes ceil(n / (U * NT)) memory round trips. Vectors
+    // are scanned in index order; scan_first also takes a -inf first element
+    // when the lane holds nothing yet (the same as scan otherwise).
+    for (int j = tid; j < nvec; j += U * NT) {
         typename R::Vec w[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = load_nt(vrow + j + u * NT);
+        for (int u = 0; u < U; ++u)
+            if (j + u * NT < nvec) w[u] = load_nt(vrow + j + u * NT);
 #pragma unroll
-        for (int u = 0; u < U; ++u) R::template scan<M>(w[u], base + (j + u * NT) * E, best, bidx, second);
+        for (int u = 0; u < U; ++u)
+            if (j + u * NT < nvec) R::template scan_first<M>(w[u], base + (j + u * NT) * E, best, bidx, second);
     }
-    for (; j < nvec; j += NT) R::template scan<M>(load_nt(vrow + j), base + j * E, best, bidx, second);
     if (tail0 + tid < len) {
         const float v = R::at(span, tail0 + tid);
         if (bidx == INT32_MAX) {
