@@ -412,3 +412,43 @@ def test_warp_cooperative_and_row_paths(sv, case):
                 assert err <= WARP_TOL, (mode, b, r, err)
     print(f"[{name}] coop vs rows max |diff| = "
           f"{float((outs['coop'] - outs['rows']).abs().nan_to_num(0).max()):.3g}", flush=True)
+
+
+@pytest.mark.parametrize("V", [4099, 40000])
+def test_maximum_draft_length(sv, V):
+    """K = SV_MAX_K = 64, one wavefront lane per position: chains that match all
+    the way (the bonus row is row 64), a miss at the last position, a miss at
+    the first, and a ragged length; greedy on logits, the sampled verify from
+    logits and on probabilities with identical draft rows (every position is
+    accepted for u < 1), each against the oracle. V = 4099 takes the unaligned
+    paths, V = 40000 the split ones."""
+    g = torch.Generator().manual_seed(41)
+    B, K = 4, 64
+    zt = torch.randn(B, K + 1, V, generator=g)
+    chain = zt.argmax(-1).to(torch.int32)[:, :K]
+    tok = chain.clone()
+    tok[1, K - 1] = (chain[1, K - 1] + 1) % V
+    tok[2, 0] = (chain[2, 0] + 1) % V
+    lens = torch.tensor([K, K, K, 10], dtype=torch.int32)
+    n, nx = sv.sv_verify_greedy(zt.cuda(), tok.cuda(), lens.cuda())
+    n_o, nx_o = oracle.verify_greedy(zt, tok, lens)
+    np.testing.assert_array_equal(host(n).numpy(), n_o)
+    np.testing.assert_array_equal(host(nx).numpy(), nx_o)
+    assert list(n_o) == [K, K - 1, 0, 10]
+    zd = zt[:, :K].clone()
+    u = torch.rand(B, K + 1, generator=g) * 0.999
+    n2, nx2 = sv.sv_accept_logits(zt.cuda(), zd.cuda(), tok.cuda(), u.cuda(), 1.0, lens.cuda())
+    n2_o, nx2_o, fl = oracle.accept_logits(zt, zd, tok, u, lens, 1.0)
+    np.testing.assert_array_equal(host(n2).numpy(), n2_o)
+    ok = (fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) == 0
+    np.testing.assert_array_equal(host(nx2).numpy()[ok], nx2_o[ok])
+    assert list(n2_o) == [K, K, K, 10]
+    p = torch.softmax(zt.double(), -1).float()
+    q = p[:, :K].clone()
+    n3, nx3 = sv.sv_accept(p.cuda(), q.cuda(), tok.cuda(), u.cuda(), lens.cuda())
+    n3_o, nx3_o, fl3 = oracle.accept(p, q, tok, u, lens)
+    np.testing.assert_array_equal(host(n3).numpy(), n3_o)
+    ok3 = (fl3 & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) == 0
+    np.testing.assert_array_equal(host(nx3).numpy()[ok3], nx3_o[ok3])
+    assert list(n3_o) == [K, K, K, 10]
+    print(f"[K=64, V={V}] greedy n {n_o.tolist()}, sampled n {n2_o.tolist()}", flush=True)
