@@ -201,7 +201,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "K": K, "V": V, "input_dtype": batch.dtype,
-                   "temperature": T, "step": "warp(target)+warp(draft)+accept+greedy"},
+                   "temperature": T,
+                   "step": ("warp(target)+warp(draft)+accept+greedy" if batch.kind == "logits"
+                            else "accept+greedy (inputs are probabilities)")},
     }
     if batch.kind == "logits":
         warp_ms = warp_t_ms + warp_d_ms
@@ -218,8 +220,15 @@ def main():
                            "traffic": traffic,
                            "algorithmic_bytes_per_launch": (warp_bytes_t + warp_bytes_d) // 2,
                            "avg_launch_ms": round(warp_ms / 2, 4)}
+    else:  # probabilities in: the sampled verify is the step's largest kernel
+        achieved = gbs(accept_bytes, accept_ms)
+        out["roofline"] = {"bound": "hbm", "kernel": "accept_kernel", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": None, "algorithmic_bytes_per_launch": int(accept_bytes),
+                           "avg_launch_ms": round(accept_ms, 4)}
     out["kernels"] = {
-        "warp_target_ms": round(warp_t_ms, 4), "warp_draft_ms": round(warp_d_ms, 4),
+        "warp_target_ms": round(warp_t_ms, 4) if batch.kind == "logits" else None,
+        "warp_draft_ms": round(warp_d_ms, 4) if batch.kind == "logits" else None,
         "accept_ms": round(accept_ms, 4), "greedy_ms": round(greedy_ms, 4),
         "warp_GBps": round(gbs(warp_bytes_t + warp_bytes_d, warp_t_ms + warp_d_ms), 1) if batch.kind == "logits"
         else None,
