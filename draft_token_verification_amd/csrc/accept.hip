@@ -640,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
 constexpr int kMaxSlices = kMaxCoopSlices;
+static_assert(kMaxSlices <= 8, "slice partials are merged by a butterfly over 8 lanes");
 
 __device__ __forceinline__ unsigned long long pack_online(const Online& o) {
     return ((unsigned long long)__float_as_uint((float)o.s) << 32) | __float_as_uint(o.m);
@@ -675,13 +676,24 @@ __device__ void sliced_row_stats(unsigned long long* set, int G, int g, int Ls, 
         }
         __syncthreads();
     }
+    // merge the G <= 8 slices' partials in a fixed butterfly over lanes 0-7
+    // of every wavefront (lane k holds slice k), then take lane 0's result
+    const int lane = threadIdx.x & (kWave - 1);
     Online rt{kNoRef, 0.0}, rd{kNoRef, 0.0};
-    for (int k = 0; k < G; ++k) {
-        merge_packed(rt, s_words[2 * k]);
-        if (D) merge_packed(rd, s_words[2 * k + 1]);
+    if (lane < G) {
+        merge_packed(rt, s_words[2 * lane]);
+        if (D) merge_packed(rd, s_words[2 * lane + 1]);
     }
-    st = RowStats{rt.m, 1.0 / rt.s};
-    if (D) sd = RowStats{rd.m, 1.0 / rd.s};
+    online_merge(rt, dpp_f<kDppQuadXor1>(rt.m), dpp_d<kDppQuadXor1>(rt.s));
+    online_merge(rt, dpp_f<kDppQuadXor2>(rt.m), dpp_d<kDppQuadXor2>(rt.s));
+    online_merge(rt, dpp_f<kDppRowHalfMirror>(rt.m), dpp_d<kDppRowHalfMirror>(rt.s));
+    st = RowStats{readlane_f(rt.m, 0), 1.0 / readlane_d(rt.s, 0)};
+    if (D) {
+        online_merge(rd, dpp_f<kDppQuadXor1>(rd.m), dpp_d<kDppQuadXor1>(rd.s));
+        online_merge(rd, dpp_f<kDppQuadXor2>(rd.m), dpp_d<kDppQuadXor2>(rd.s));
+        online_merge(rd, dpp_f<kDppRowHalfMirror>(rd.m), dpp_d<kDppRowHalfMirror>(rd.s));
+        sd = RowStats{readlane_f(rd.m, 0), 1.0 / readlane_d(rd.s, 0)};
+    }
     __syncthreads();  // s_words is reused by the next exchange
 }
 
