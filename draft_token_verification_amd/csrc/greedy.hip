@@ -256,6 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
 constexpr int kSliceUnroll = 6;  // 96 bytes per lane in flight (8 would spill)
+static_assert(kMaxCoopSlices <= 8, "slice results are merged by a butterfly over 8 lanes");
 
 template <bool BF16, bool M>
 __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_sliced_kernel(
@@ -301,17 +302,31 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
             }
             __syncthreads();
         }
-        // merge the slices in slice order (the same in every workgroup)
-        v = __uint_as_float((uint32_t)(s_words[0] >> 32));
-        am = (int)(uint32_t)s_words[0];
-        if (M) s = __uint_as_float((uint32_t)s_words[1]);
-        for (int k = 1; k < G; ++k) {
-            const float vk = __uint_as_float((uint32_t)(s_words[k * W] >> 32));
-            const int ik = (int)(uint32_t)s_words[k * W];
-            if (M)
-                top2_merge(v, am, s, vk, ik, __uint_as_float((uint32_t)s_words[k * W + 1]));
-            else
-                argmax_merge(v, am, vk, ik);
+        // merge the G <= 8 slices: lane k holds slice k, a butterfly over lanes
+        // 0-7 (the (value, index) order is total and the runner-up is a plain
+        // maximum, so every merge order gives the same result), lane 0's result
+        {
+            v = -INFINITY;
+            am = INT32_MAX;
+            s = -INFINITY;
+            if (lane < G) {
+                v = __uint_as_float((uint32_t)(s_words[lane * W] >> 32));
+                am = (int)(uint32_t)s_words[lane * W];
+                if (M) s = __uint_as_float((uint32_t)s_words[lane * W + 1]);
+            }
+            if (M) {
+                top2_merge(v, am, s, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(am), dpp_f<kDppQuadXor1>(s));
+                top2_merge(v, am, s, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(am), dpp_f<kDppQuadXor2>(s));
+                top2_merge(v, am, s, dpp_f<kDppRowHalfMirror>(v), dpp_i<kDppRowHalfMirror>(am),
+                           dpp_f<kDppRowHalfMirror>(s));
+                s = readlane_f(s, 0);
+            } else {
+                argmax_merge(v, am, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(am));
+                argmax_merge(v, am, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(am));
+                argmax_merge(v, am, dpp_f<kDppRowHalfMirror>(v), dpp_i<kDppRowHalfMirror>(am));
+            }
+            v = readlane_f(v, 0);
+            am = readlane_i(am, 0);
         }
         __syncthreads();  // s_words is rewritten by the next position's gather
         // a token outside [0, V) never equals an argmax: it is a miss
