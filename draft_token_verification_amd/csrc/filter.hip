@@ -683,6 +683,45 @@ __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float 
         for (int j = 0; j < kPer; ++j)
             if (valid[j] && key[j] >= kth) cand[off + mine[j]] = key[j];
     }
+    if (ns <= kWave) {
+        // At most 64 survivors (k <= 64, or a short top-p list): every
+        // wavefront sorts them in its lanes and reads the nucleus off a wave
+        // scan, with no barrier. The same keys, masses and decision rule as
+        // the block-wide path below, so the same thresholds.
+        __syncthreads();  // the packed survivors are in cand[]
+        uint32_t kk = lane < ns ? cand[lane] : 0u;  // 0 sorts last
+        for (int size = 2; size <= kWave; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t other = (uint32_t)__shfl_xor((int)kk, stride, kWave);
+                const bool larger_here = ((lane & stride) == 0) == ((lane & size) == 0);
+                kk = larger_here ? max(kk, other) : min(kk, other);
+            }
+        }
+        const unsigned long long mk = lane < ns ? fixed_of(ex2(fmaf(value_of<BF16>(kk), c, -Mc)), fxs) : 0ull;
+        unsigned long long incl = mk;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) incl += shfl_up_u64(incl, d) * (lane >= d);
+        const unsigned long long excl = incl - mk;
+        const unsigned long long H0 = readlane_u64(incl, kWave - 1);  // the survivors' mass
+        double target = (double)pp * (kon ? (double)H0 : S_total);
+        if (!(target > 0.0)) target = 0.5;  // top_p <= 0: keep the largest value only
+        const uint32_t prev = (uint32_t)__shfl_up((int)kk, 1, kWave);
+        int last = (lane > 0 && lane < ns && kk != prev && (double)excl < target) ? lane : 0;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) last = max(last, __shfl_xor(last, d, kWave));
+        tau = (uint32_t)readlane_i((int)kk, last);
+        // every candidate at or above tau is a survivor, so both checks stay in the wavefront
+        const unsigned long long at_or_above = __ballot(lane < ns && kk >= tau);
+        if (!kon && nc < V && __popcll(at_or_above) == nc) return false;
+        unsigned long long m = kk >= tau ? mk : 0ull;
+        m = wave_sum_u64(m);
+        s_kept = (double)m;
+        if (map && tau != 0u) {
+            mark_kept_quads<kPer>(key, valid, tau, L->ids, V / 4, (uint32_t*)&L->mass[0][0]);
+            mapped = true;
+        }
+        return true;
+    }
     int P = 1;
     while (P < ns) P <<= 1;
     for (int i = ns + tid; i < P; i += kThreads) cand[i] = 0u;  // sorts last
