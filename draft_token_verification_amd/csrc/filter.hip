@@ -19,9 +19,11 @@
 // wavefront, collects the keys of the logits within 20 log2 units of its
 // running maximum into LDS.
 //   common path  the k-th largest collected key comes from a bitwise search
-//                with block-wide counts; for top-p the top-k survivors are
-//                sorted (bitonic network) and the nucleus read off their
-//                prefix masses, one decision per group of equal keys. It
+//                with block-wide counts; for top-p, up to 64 top-k survivors
+//                are sorted in a wavefront (bitonic network) and the nucleus
+//                read off their prefix masses, one decision per group of
+//                equal keys; with more, the nucleus's last key comes from a
+//                bitwise search with block-wide masses instead. It
 //                applies when the collected set holds at least k ids and
 //                (top-p alone) the nucleus ends inside it; a wavefront whose
 //                buffer overflows keeps only its largest keys (a key floor),
@@ -536,24 +538,6 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
     return v;
 }
 
-// Sort keys[0 .. P) descending (P a power of two <= kCand), bitonic network.
-__device__ __forceinline__ void sort_desc(uint32_t* keys, int P) {
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (P >> 1); i += kThreads) {
-                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint32_t a = keys[lo], b = keys[hi];
-                if ((a < b) == desc) {
-                    keys[lo] = b;
-                    keys[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 constexpr int kMapWords = kWaves * kBins * 2;  // the kept-quad map: 32-bit words over the mass array
 
 // The map of the quads (4 consecutive elements) that hold a kept id: bit q of
@@ -585,10 +569,12 @@ __device__ __forceinline__ void mark_kept_quads(const uint32_t* key, const bool*
 // ids). Each thread holds up to 4 candidates in registers.
 //   top-k  the k-th largest key: the largest t with at least k candidate keys
 //          >= t, by a bitwise search with block-wide counts.
-//   top-p  the survivors of top-k (keys >= that) are packed and sorted in
-//          LDS; an id is kept iff the survivors strictly above it weigh less
-//          than the target, one decision per group of equal keys, read off the
-//          exclusive prefix masses of the sorted order.
+//   top-p  among the survivors of top-k (keys >= that) an id is kept iff the
+//          survivors strictly above it weigh less than the target, one
+//          decision per group of equal keys: up to 64 survivors are sorted in
+//          a wavefront and the rule read off their exclusive prefix masses;
+//          more give the last kept key by a bitwise search on block-wide
+//          masses (the same key).
 // S_total is the row's mass in fixed-point units (the top-p reference without
 // top-k). Returns false when the candidates cannot decide: fewer than k of
 // them, or (top-p alone) a nucleus that keeps every candidate and may reach
@@ -722,57 +708,26 @@ __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float 
         }
         return true;
     }
-    int P = 1;
-    while (P < ns) P <<= 1;
-    for (int i = ns + tid; i < P; i += kThreads) cand[i] = 0u;  // sorts last
-    __syncthreads();
-    sort_desc(cand, P);
-    // exclusive prefix masses in sorted order: thread t owns entries 4t .. 4t+3
-    unsigned long long* pre = &L->mass[0][0];
-    {
-        unsigned long long part[4], run = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * tid + j;
-            part[j] = run;
-            run += i < ns ? fixed_of(ex2(fmaf(value_of<BF16>(cand[i]), c, -Mc)), fxs) : 0ull;
-        }
-        unsigned long long v = run;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) v += shfl_up_u64(v, d) * (lane >= d);
-        if (lane == kWave - 1) L->wmass[half][wave] = v;
-        __syncthreads();
-        unsigned long long base = v - run;
-        for (int w = 0; w < wave; ++w) base += L->wmass[half][w];
-        half ^= 1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pre[4 * tid + j] = base + part[j];
-    }
-    const unsigned long long H0 = mass_ge(kth);  // the survivors' mass (also orders the writes above)
+    // More survivors: no sort. The kept ids are those whose strictly larger
+    // keys weigh less than the target, which is every key >= T for the
+    // largest T whose mass at or above it still reaches the target (the
+    // masses at or above t fall as t grows, and T is a key: the mass steps
+    // down right after it). T comes from a bitwise search with block-wide
+    // fixed-point sums; it is the key the sorted nucleus ends on, and the
+    // largest key is always kept (its strictly larger mass is 0).
+    const unsigned long long H0 = mass_ge(kth);  // the survivors' mass
     double target = (double)pp * (kon ? (double)H0 : S_total);
     if (!(target > 0.0)) target = 0.5;  // top_p <= 0: keep the largest value only
-    // the last group start whose exclusive prefix is below the target (the
-    // first group is always kept); kept groups are a prefix of the order
-    int last = 0;
-    for (int i = tid; i < ns; i += kThreads)
-        if (i > 0 && cand[i] != cand[i - 1] && (double)pre[i] < target) last = max(last, i);
-    last = max(last, __shfl_xor(last, 1));
-    last = max(last, __shfl_xor(last, 2));
-    last = max(last, __shfl_xor(last, 4));
-    last = max(last, __shfl_xor(last, 8));
-    last = max(last, __shfl_xor(last, 16));
-    last = max(last, __shfl_xor(last, 32));
-    if (lane == 0) L->wnum[half][wave] = last;
-    __syncthreads();
-    int istar = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) istar = max(istar, L->wnum[half][w]);
-    half ^= 1;
-    tau = cand[istar];
+    uint32_t T = 0u;
+    for (int bit = kBits - 1; bit >= 0; --bit) {
+        const uint32_t t = T | (1u << bit);
+        if ((double)mass_ge(t) >= target) T = t;
+    }
+    tau = T;
     // top-p alone: if no candidate is dropped, ids below the cut may belong
     if (!kon && nc < V && count_ge(tau) == nc) return false;
     s_kept = (double)mass_ge(tau);
-    if (map && tau != 0u) {  // the prefix masses in the mass array were last read before istar's barrier
+    if (map && tau != 0u) {
         mark_kept_quads<kPer>(key, valid, tau, L->ids, V / 4, kmap);
         mapped = true;
     }
