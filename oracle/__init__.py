@@ -56,8 +56,8 @@ def load_library(path: str):
     lib.or_icdf.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, i64, f64, f64, ctypes.POINTER(ctypes.c_int32)]
     lib.or_icdf.restype = i64
     lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
-    lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, f64, vp,
-                                     vp, vp]
+    lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, vp, vp,
+                                     vp]
     lib.or_top2_margin.argtypes = [vp, ctypes.c_int, i64]
     lib.or_top2_margin.restype = f64
     lib.or_gate_update.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, f64]
@@ -249,12 +249,11 @@ def accept(p, q, tokens, uniforms, lens=None, rel_window: float = 1e-5, lib=None
     return n, nx, fl
 
 
-def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_window: float = 1e-5,
-                  abs_window: float = 0.0, lib=None):
+def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_window: float = 1e-5, lib=None):
     """Sampled verify from logits: or_accept on softmax(z / T) of the examined rows, in fp64.
 
-    zt [B, K+1, V], zd [B, K, V] logits (same dtype). Returns (n_accepted, next_token, flags).
-    ``abs_window`` adds an absolute floor to the CDF boundary flag.
+    zt [B, K+1, V], zd [B, K, V] logits (same dtype). Returns (n_accepted, next_token, flags),
+    flagged with the same relative ratio and CDF windows as ``accept``.
     """
     ta, dt = _array(zt)
     B, K1, V = ta.shape
@@ -275,7 +274,7 @@ def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_windo
     nx = np.empty(B, dtype=np.int32)
     fl = np.empty(B, dtype=np.int32)
     (lib or _lib()).or_accept_logits(_ptr(ta), _ptr(da), dt, B, K, V, float(T), _ptr(t), _ptr(ln), _ptr(ua), du,
-                                     float(rel_window), float(abs_window), _ptr(n), _ptr(nx), _ptr(fl))
+                                     float(rel_window), _ptr(n), _ptr(nx), _ptr(fl))
     return n, nx, fl
 
 

@@ -249,13 +249,12 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
  * The same procedure as or_accept on p = softmax(z_target / T) and
  * q = softmax(z_draft / T) of each examined row, warped in fp64 with
  * or_warp_row; only the rows the procedure examines are warped. Flags use
- * the relative window plus an absolute floor `abs_window` on the CDF check
- * (the warp's own tolerance), since a kernel that warps in fp32 carries that
- * much absolute error in every p and q. */
+ * the same relative windows as or_accept: a tested u within rel_window * rho
+ * of its ratio, a draw threshold within rel_window * C of a cumulative
+ * weight C. */
 void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
                       const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
-                      double rel_window, double abs_window, int32_t* n_accepted, int32_t* next_token,
-                      int32_t* flags) {
+                      double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags) {
 #pragma omp parallel
     {
         double* p = (double*)malloc((size_t)V * sizeof(double));
@@ -297,19 +296,6 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
             } else {
                 or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);
                 next = or_icdf(p, NULL, OR_F64, 1, V, u_final, rel_window, &f2);
-            }
-            /* absolute floor on the CDF window: recheck the draw's neighbours */
-            if (abs_window > 0.0 && next >= 0) {
-                int kind = (n < kb && !(flag & OR_FLAG_ZERO_RESIDUAL)) ? 0 : 1;
-                double S = or_mass(p, kind == 0 ? q : NULL, OR_F64, kind, V);
-                double thr = u_final * S, c = 0.0;
-                for (int64_t x = 0; x <= next; ++x) {
-                    double w = kind == 0 ? p[x] - q[x] : p[x];
-                    double c_prev = c;
-                    c += w > 0.0 ? w : 0.0;
-                    if (x == next && (fabs(thr - c_prev) <= abs_window || fabs(c - thr) <= abs_window))
-                        f2 |= OR_FLAG_CDF;
-                }
             }
             n_accepted[b] = n;
             next_token[b] = (int32_t)next;

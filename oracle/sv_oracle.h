@@ -51,8 +51,7 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
 
 void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
                       const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
-                      double rel_window, double abs_window, int32_t* n_accepted, int32_t* next_token,
-                      int32_t* flags);
+                      double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags);
 
 double or_top2_margin(const void* row, int dtype, int64_t V);
 void or_gate_update(double* hits, double* trials, int64_t B, int64_t NB, int64_t K, const int32_t* lens,

@@ -1,19 +1,22 @@
 """GPU parity of the sampled verify taken straight from logits (sv_accept_logits)
 against the oracle's fp64 composition softmax(z / T) -> accept.
 
-The kernel forms each examined probability as 2^(z*c - m) * inv with c = log2(e)/T
-rounded to fp32, fp32 exp2 and fp64 sums. Rounding c scales every exponent by
-(1 + d), |d| <= 2^-24, which moves p(x) by at most d * (log2 range of the row)
-relative: under 64 * 6e-8 < 4e-6 for rows whose logits span less than 44 nats
-at T = 1; the exp2 and the fmaf argument add a few 1e-7. Hence:
-  - the ratio p(t)/q(t) is within 1e-5 relative -> RATIO_WINDOW = 2e-5;
-  - a cumulative residual mass (sums of max(0, p - q) or of p, both rows
-    normalised to 1) is within 4e-6 * (1 + 1) absolute -> CDF_WINDOW = 1e-5.
-Decisions and ids must match exactly except on sequences the oracle flags as
-lying within those windows of a boundary (counted). Draws from a residual whose
-total mass is itself ~1e-5 (a draft almost equal to the target, as in the ragged
-workload's low-noise sequences) are flagged almost surely; the flagged fraction
-is bounded per test so that the check never becomes vacuous.
+The bar is the sampled verify's: decisions and ids exact except where the
+oracle finds a uniform within 1e-5 relative of a ratio or CDF boundary
+(tests/sampled_check.py: a ratio flag exempts the sequence, a CDF flag only its
+drawn id; at most 1% of a batch may be flagged).
+
+Why the kernel's errors sit inside those relative windows: it takes every
+probability as 2^(z*c - m) / S with c = log2(e)/T rounded to fp32, i.e. it
+evaluates the softmax at a temperature within 6e-8 relative of T, with fp32
+exponentials and fp64 sums (relative error of S about 1e-7). The accept ratio
+p(t)/q(t) is formed in fp64 from the exact logit difference,
+2^((z_t(t) - z_d(t))*c + m_d - m_t) * S_d / S_t, so its relative error is that
+of S_d / S_t. Each residual weight is p(x) * (1 - q(x)/p(x)) with the ratio
+q(x)/p(x) again from the exact logit difference and 1 - 2^y by a series near
+y = 0, so it carries a relative error of about 1e-7 plus the common error of
+S_t / S_d times p(x) -- about 1e-7 of the target mass below the threshold,
+against a window of 1e-5 times the residual mass below it.
 """
 import numpy as np
 import pytest
@@ -21,11 +24,11 @@ import torch
 
 import oracle
 import synth
+from tests.sampled_check import compare_sampled
 
 pytestmark = pytest.mark.gpu
 
-RATIO_WINDOW = 2e-5
-CDF_WINDOW = 1e-5
+WINDOW = 1e-5  # relative, for ratio and CDF boundaries alike
 SENTINEL = -777
 
 
@@ -56,22 +59,21 @@ def run(sv, zt, zd, tokens, u, lens, T, path="sliced"):
     return host(n).numpy(), host(nx).numpy()
 
 
-def compare(sv, zt, zd, tokens, u, lens, T, label, sample=None, max_flag_frac=0.35, path="sliced"):
+def compare(sv, zt, zd, tokens, u, lens, T, label, sample=None, path="sliced", chunk=64):
+    """GPU result on the whole batch against the oracle on ``sample`` (all sequences when None),
+    the oracle called ``chunk`` sequences at a time."""
     n, nx = run(sv, zt, zd, tokens, u, lens, T, path)
     B = zt.shape[0]
     idx = np.arange(B) if sample is None else np.sort(sample)
-    it = torch.as_tensor(idx, device=zt.device)
-    sel = (lambda x: None if x is None else host(x[it]))
-    n_o, nx_o, fl = oracle.accept_logits(sel(zt), sel(zd), sel(tokens), sel(u), sel(lens), T,
-                                         rel_window=RATIO_WINDOW, abs_window=CDF_WINDOW)
-    flagged = (fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0
-    mism = (n[idx] != n_o) | (nx[idx] != nx_o)
-    hard = np.nonzero(mism & ~flagged)[0]
-    print(f"[{label}] logits verify: {len(idx)} of {B} checked, mean n={n_o.mean():.3f}, "
-          f"flagged={int(flagged.sum())}, mismatched-within-flagged={int((mism & flagged).sum())}", flush=True)
-    assert len(hard) == 0, (f"{label}: mismatch at {len(hard)} unflagged sequences; first b={idx[hard[0]]}: gpu "
-                            f"({n[idx[hard[0]]]}, {nx[idx[hard[0]]]}) oracle ({n_o[hard[0]]}, {nx_o[hard[0]]})")
-    assert flagged.mean() <= max_flag_frac, f"{label}: {flagged.mean():.3f} of sequences flagged"
+    n_o = np.empty(len(idx), np.int32)
+    nx_o = np.empty(len(idx), np.int32)
+    fl = np.empty(len(idx), np.int32)
+    for c0 in range(0, len(idx), chunk):
+        it = torch.as_tensor(idx[c0:c0 + chunk], device=zt.device)
+        sel = (lambda x: None if x is None else host(x[it]))
+        n_o[c0:c0 + chunk], nx_o[c0:c0 + chunk], fl[c0:c0 + chunk] = oracle.accept_logits(
+            sel(zt), sel(zd), sel(tokens), sel(u), sel(lens), T, rel_window=WINDOW)
+    compare_sampled(n[idx], nx[idx], n_o, nx_o, fl, f"{label} ({len(idx)} of {B})")
     V = zt.shape[-1]
     assert (n >= 0).all() and (nx >= 0).all() and (nx < V).all()
     return n, nx, n_o
@@ -106,9 +108,7 @@ def test_accept_logits_parity_reduced(sv, case, path):
 @pytest.mark.parametrize("name", LOGITS)
 def test_accept_logits_full_size(sv, name, path):
     b = synth.generate(name, "cuda", poison=True)
-    sample = np.arange(b.B) if b.B <= 64 else np.random.default_rng(2).choice(b.B, 48, replace=False)
-    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, name + "/full/" + path, sample=sample,
-            path=path)
+    compare(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature, name + "/full/" + path, path=path)
 
 
 def test_accept_logits_matches_two_step_path_in_law(sv):

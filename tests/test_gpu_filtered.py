@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import synth
+from tests.sampled_check import compare_sampled
 
 pytestmark = pytest.mark.gpu
 
@@ -213,12 +214,11 @@ def test_filtered_pipeline_sampled_verify(sv):
     torch.cuda.synchronize()
     n, nx = host(n).numpy(), host(nx).numpy()
     n_o, nx_o, fl = oracle.accept(p_o, q_o, toks, host(batch.uniforms), None)
-    flagged = ((fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0) | (fp & oracle.FLAG_TOPP).any(1) \
-        | (fq & oracle.FLAG_TOPP).any(1)
-    mism = (n != n_o) | (nx != nx_o)
-    print(f"[filtered pipeline] mean n={n_o.mean():.3f} flagged={int(flagged.sum())} "
-          f"mismatched={int(mism.sum())}", flush=True)
-    assert not (mism & ~flagged).any()
+    # a top-p boundary close call may change a whole row: treat it as a ratio flag
+    topp = (fp & oracle.FLAG_TOPP).any(1) | (fq & oracle.FLAG_TOPP).any(1)
+    fl = np.where(topp, fl | oracle.FLAG_RATIO, fl)
+    compare_sampled(n, nx, n_o, nx_o, fl, "filtered pipeline")
+    flagged = (fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0
     # the emitted token always survives the filters of its row
     for b in np.nonzero(~flagged)[0]:
         assert p_o[b, n[b], nx[b]] > 0.0

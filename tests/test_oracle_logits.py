@@ -77,15 +77,46 @@ def test_logits_verify_exact_law():
         np.testing.assert_allclose(emitted_marginal(law, i, V), np.prod(a[:i]) * p[i], atol=1e-12)
 
 
-def test_abs_window_only_adds_flags():
+def test_logits_verify_flags_use_relative_windows():
+    """The boundary flags of the verify from logits are the relative windows of the
+    verify on probabilities: a draw threshold at a cumulative weight C is flagged
+    within 1e-5 * C of it and not beyond, however small C is (a residual of total
+    mass 1e-3 is judged on its own scale), and a realistic batch flags almost
+    nothing."""
+    V = 4
+    # target row 0 and draft row 0 differ only in ids 0 and 1: the residual sits on id 0 alone
+    zt = np.log(np.array([[[0.25, 0.25, 0.25, 0.25], [0.4, 0.3, 0.2, 0.1]]]))
+    zd = np.log(np.array([[[0.2495, 0.2505, 0.25, 0.25]]]))
+    p = np.exp(zt[0, 0]) / np.exp(zt[0, 0]).sum()
+    q = np.exp(zd[0, 0]) / np.exp(zd[0, 0]).sum()
+    rho = p[0] / q[0]
+    w = np.maximum(p - q, 0.0)
+    assert w[0] > 0 and w[1:].sum() == 0  # all residual mass on id 0: a draw can only give 0
+    t = np.array([[0]], dtype=np.int32)
+    for u0, flagged in ((rho * 0.999, False), (rho * (1 - 3e-6), True), (rho * (1 + 3e-6), True),
+                        (min(rho * 1.001, 0.9999), False)):
+        _, _, fl = oracle.accept_logits(zt, zd, t, np.array([[u0, 0.5]]), None, 1.0)
+        assert bool(fl[0] & oracle.FLAG_RATIO) == flagged, (u0, rho)
+    # a residual of mass ~1e-3 split over ids 0 and 2: the boundary C(0) = w0 is
+    # flagged within 1e-5 * w0 (a few 1e-9 absolute), not at 1e-5 absolute
+    zd = np.log(np.array([[[0.2495, 0.2505, 0.2495, 0.2505]]]))
+    q = np.exp(zd[0, 0]) / np.exp(zd[0, 0]).sum()
+    w = np.maximum(p - q, 0.0)
+    S = w.sum()
+    assert w[0] > 0 and w[2] > 0 and 1e-4 < S < 1e-2
+    t = np.array([[1]], dtype=np.int32)  # p/q < 1 at id 1; u = 0.9999 rejects
+    for frac, flagged, want in ((1 - 3e-6, True, 0), (1 + 3e-6, True, 2), (0.999, False, 0), (1.001, False, 2)):
+        uf = w[0] * frac / S
+        n, nx, fl = oracle.accept_logits(zt, zd, t, np.array([[0.9999, uf]]), None, 1.0)
+        assert n[0] == 0 and nx[0] == want, (frac, nx[0])
+        assert bool(fl[0] & oracle.FLAG_CDF) == flagged, frac
+    # the realistic batch: almost nothing flagged
     rng = np.random.default_rng(4)
-    B, K, V = 60, 4, 200
-    zt = rng.standard_normal((B, K + 1, V)).astype(np.float32)
-    zd = (zt[:, :K] + 0.3 * rng.standard_normal((B, K, V))).astype(np.float32)
-    t = rng.integers(0, V, (B, K)).astype(np.int32)
+    B, K, V = 300, 4, 400
+    zt = (3 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    zd = (zt[:, :K] + rng.uniform(0.1, 3.0, (B, 1, 1)) * rng.standard_normal((B, K, V))).astype(np.float32)
+    q = oracle.softmax_warp(zd, None, 0, 1.0)
+    t = np.array([[rng.choice(V, p=q[b, i]) for i in range(K)] for b in range(B)], dtype=np.int32)
     u = rng.random((B, K + 1))
-    n1, x1, f1 = oracle.accept_logits(zt, zd, t, u)
-    n2, x2, f2 = oracle.accept_logits(zt, zd, t, u, abs_window=1e-3)
-    np.testing.assert_array_equal(n1, n2)
-    np.testing.assert_array_equal(x1, x2)
-    assert ((f1 & ~f2) == 0).all() and (f2 & oracle.FLAG_CDF).sum() >= (f1 & oracle.FLAG_CDF).sum()
+    _, _, fl = oracle.accept_logits(zt, zd, t, u, None, 1.0)
+    assert ((fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0).sum() <= 3
