@@ -22,9 +22,12 @@
 //  1. For i = 0, 1, ... in order, one pass over target row i and draft row i
 //     gives each row's log2-domain statistics (m, sum of 2^(y - m)), m an
 //     integer at or above the row maximum (online, per lane, merged with DPP
-//     and LDS); p_i(t_i) and q_i(t_i) follow from the two logits at t_i,
-//     and the test u*q < p runs in binary64. The loop stops at the first
-//     rejection, so rows after it are never read.
+//     and LDS); the ratio p_i(t_i)/q_i(t_i) follows from the difference of
+//     the two logits at t_i and the two rows' statistics, and u < ratio is
+//     tested in binary64. The loop stops at the first rejection, so rows
+//     after it are never read. A residual weight is p(x) * (1 - q(x)/p(x))
+//     with q(x)/p(x) again from the logit difference, so it keeps a small
+//     relative error where the two rows nearly agree.
 //
 // The draw (both kernels):
 //  2. Segment sums (all 16 wavefronts): the one row (pair) the draw needs is
@@ -146,18 +149,73 @@ __device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) 
     return (double)ex2(fmaf(z, c, -st.m)) * st.inv;
 }
 
+// The accept test u < p(t)/q(t) from the two logits at t. The ratio is formed
+// from the logit difference rather than from p and q separately:
+//   rho = 2^e * inv_t / inv_d,  e = (zt - zd) * c + m_d - m_t,
+// with the difference of the two binary32 logits and its product with c
+// taken in binary64 (exact up to one rounding) and the references m
+// integral; 2^e is 2^(e - round(e)) in fp32 (within 2e-7 relative) scaled
+// by an exact power of two. So rho carries about 2e-7 of relative error plus
+// that of the two row masses S = 1/inv. A -inf target logit means p(t) = 0
+// (reject); a -inf draft logit alone means q(t) = 0 < p(t) (accept).
+__device__ __forceinline__ bool accepts(float zt, float zd, float c, const RowStats& st, const RowStats& sd,
+                                        float u) {
+    if (zt == -INFINITY) return false;
+    if (zd == -INFINITY) return true;
+    const double e = fma((double)zt - (double)zd, (double)c, (double)sd.m - (double)st.m);
+    const double ei = rint(fmin(fmax(e, -4096.0), 4096.0));  // beyond the binary64 range either way
+    const double two_e = __builtin_ldexp((double)ex2((float)(e - ei)), (int)ei);
+    return (double)u < two_e * (st.inv / sd.inv);
+}
+
+// 1 - 2^y for y < 0, with a relative error of a few 1e-7 everywhere: a
+// series in t = y ln 2 near 0 (|t| <= 0.18, truncated after t^6 / 6!, whose
+// remainder is below 1e-8 relative) and 1 - exp2(y) below, where the result
+// is at least 0.16.
+__device__ __forceinline__ float one_minus_exp2(float y) {
+    const float t = y * 0.69314718f;
+    float s = 1.0f / 720.0f;
+    s = fmaf(s, t, 1.0f / 120.0f);
+    s = fmaf(s, t, 1.0f / 24.0f);
+    s = fmaf(s, t, 1.0f / 6.0f);
+    s = fmaf(s, t, 0.5f);
+    s = fmaf(s, t, 1.0f);
+    const float near0 = -t * s;
+    return y < -0.25f ? 1.0f - ex2(y) : near0;
+}
+
+// log2(q(x)/p(x)) - (zd(x) - zt(x)) * c = (m_t - m_d) + log2(inv_d / inv_t), one
+// constant per row pair, split into an integral part ki and a fraction kf in
+// [-0.5, 0.5] so that fp32 arithmetic keeps it to within 3e-8 (both exactly 0
+// for two identical rows).
+struct Shift {
+    float ki, kf;
+};
+
+__device__ __forceinline__ Shift residual_shift(const RowStats& st, const RowStats& sd) {
+    const double l = log2(sd.inv / st.inv);
+    const double r = rint(l);
+    return Shift{(float)(((double)st.m - (double)sd.m) + r), (float)(l - r)};
+}
+
 // Logits rows with their statistics: w = max(0, p - q) (residual, D) or
-// max(0, p) (bonus or zero-residual fallback).
+// max(0, p) (bonus or zero-residual fallback). The residual weight is formed
+// as p(x) * (1 - q(x)/p(x)) with log2(q(x)/p(x)) = (zd(x) - zt(x)) * c + k0
+// taken from the exact logit difference, so it keeps a small relative error
+// where p and q nearly agree, instead of the absolute error of a difference of
+// two separately rounded probabilities.
 template <bool BF16, bool VEC, bool D>
 struct LogitSource {
     // segments per wavefront step; with the next step's loads in flight too,
-    // two fp32 pairs would not fit the register budget
-    static constexpr int kUnroll = BF16 ? 2 : 1;
+    // two fp32 pairs, or two bf16 pairs of element-wise loads, would not fit
+    // the register budget
+    static constexpr int kUnroll = BF16 && VEC ? 2 : 1;
     const void* zt;
     const void* zd;  // read only when D
     int V;
     float c;
     RowStats st, sd;
+    Shift k;  // residual_shift(st, sd) when D
     using L = Logit4<BF16>;
     struct Raw {
         typename L::Raw t, d;
@@ -195,17 +253,21 @@ struct LogitSource {
         return r;
     }
     __device__ void weights(const Raw& r, double w[4]) const {
-        // No contraction: p - q must be exactly 0 where the two rows agree;
-        // fma(e_t, inv_t, -(e_d * inv_d)) would leave a product's rounding error.
-#pragma clang fp contract(off)
         float a[4], d[4];
         L::unpack(r.t, a);
         L::unpack(r.d, d);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const double p = prob_of(a[j], c, st);
-            const double v = D ? p - prob_of(d[j], c, sd) : p;
-            w[j] = fmax(v, 0.0);  // a NaN gives 0, as a failed v > 0 test would
+            const float e = ex2(fmaf(a[j], c, -st.m));
+            if (D) {
+                // y = log2(q/p) (the logit difference is exact for bf16 logits);
+                // q >= p (y >= 0), a NaN from two -inf logits or padding, and
+                // p = 0 all give weight 0; q = 0 < p gives y = -inf, weight p
+                const float y = fmaf(d[j] - a[j], c, k.ki) + k.kf;
+                w[j] = y < 0.0f ? (double)(e * one_minus_exp2(y)) * st.inv : 0.0;
+            } else {
+                w[j] = fmax((double)e * st.inv, 0.0);  // a NaN gives 0
+            }
         }
     }
 };
@@ -594,10 +656,7 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
         const void* tr = tbase + (size_t)i * row_bytes;
         const void* dr = dbase + (size_t)i * row_bytes;
         row_stats_pass<BF16, VEC, true>(tr, dr, V, c, &lds, st, sd);
-        const double pt = prob_of(L::at(tr, t), c, st);
-        const double qt = prob_of(L::at(dr, t), c, sd);
-        const double u = uniforms[(int64_t)b * (K + 1) + i];
-        if (!(u * qt < pt)) {
+        if (!accepts(L::at(tr, t), L::at(dr, t), c, st, sd, uniforms[(int64_t)b * (K + 1) + i])) {
             n = i;
             have = true;
             break;
@@ -614,8 +673,9 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
         else
             row_stats_pass<BF16, VEC, false>(zt_row, nullptr, V, c, &lds, st, sd);
     }
-    const LogitSource<BF16, VEC, true> res{zt_row, zd_row, V, c, st, sd};
-    const LogitSource<BF16, VEC, false> bon{zt_row, nullptr, V, c, st, sd};
+    const LogitSource<BF16, VEC, true> res{zt_row, zd_row, V, c, st, sd,
+                                           residual ? residual_shift(st, sd) : Shift{0.f, 0.f}};
+    const LogitSource<BF16, VEC, false> bon{zt_row, nullptr, V, c, st, sd, Shift{0.f, 0.f}};
     const int next = final_draw(res, bon, residual, m, nseg, seg, uniforms[(int64_t)b * (K + 1) + kb]);
     if (threadIdx.x == 0) {
         n_accepted[b] = n;
@@ -761,10 +821,7 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
         const void* dr = dbase + (size_t)i * row_bytes;
         sliced_row_stats<BF16, VEC, true>(my + (size_t)i * 2 * G, G, g, Ls, V, tr, dr, c, &lds, wait_limit, s_words,
                                           &s_ready, st, sd);
-        const double pt = prob_of(L::at(tr, t), c, st);
-        const double qt = prob_of(L::at(dr, t), c, sd);
-        const double u = uniforms[(int64_t)b * (K + 1) + i];
-        if (!(u * qt < pt)) {
+        if (!accepts(L::at(tr, t), L::at(dr, t), c, st, sd, uniforms[(int64_t)b * (K + 1) + i])) {
             n = i;
             have = true;
             break;
@@ -787,10 +844,13 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
     using Res = LogitSource<BF16, VEC, true>;
     using Bon = LogitSource<BF16, VEC, false>;
     auto slice_len = [&](int k) { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); };
+    const Shift k0 = residual ? residual_shift(st, sd) : Shift{0.f, 0.f};
     auto make_res = [&](int k) {
-        return Res{zt_row + (size_t)k * Ls * kElem, zd_row + (size_t)k * Ls * kElem, slice_len(k), c, st, sd};
+        return Res{zt_row + (size_t)k * Ls * kElem, zd_row + (size_t)k * Ls * kElem, slice_len(k), c, st, sd, k0};
     };
-    auto make_bon = [&](int k) { return Bon{zt_row + (size_t)k * Ls * kElem, nullptr, slice_len(k), c, st, sd}; };
+    auto make_bon = [&](int k) {
+        return Bon{zt_row + (size_t)k * Ls * kElem, nullptr, slice_len(k), c, st, sd, Shift{0.f, 0.f}};
+    };
     bool use_bon = !residual;
     if (residual)
         sliced_totals<Res>(draw_sets, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot, make_res);

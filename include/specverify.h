@@ -318,11 +318,13 @@ sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t
  *              the query selects one workgroup per sequence. Results are
  *              identical either way up to the rounding of the partial sums.
  *              Calls that overlap in time must not share a workspace.
- * Accuracy: p and q come from fp32 exponentials with fp64 sums (relative
- * error below ~1e-5 on a ratio, absolute below ~1e-5 on a cumulative weight),
- * and the test and draw weights are compared in binary64, so decisions and
- * ids agree with an exact evaluation except where u lies that close to a
- * ratio or cumulative-weight boundary. Bitwise identical run to run.
+ * Accuracy: the row masses come from fp32 exponentials with fp64 sums
+ * (relative error about 1e-7); the accept ratio p(t)/q(t) and every residual
+ * weight p(x) * (1 - q(x)/p(x)) take q/p from the exact logit difference, so
+ * both carry relative errors of a few 1e-7 and a cumulative weight carries
+ * about 1e-7 of the target mass before it. Decisions and ids agree with an
+ * exact evaluation except where u lies within ~1e-5 relative of a ratio or
+ * cumulative-weight boundary. Bitwise identical run to run.
  * Errors: as sv_accept, plus SV_ERR_INVALID_ARG for a bad dtype or temperature.
  */
 sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,

@@ -213,12 +213,13 @@ def test_filtered_pipeline_sampled_verify(sv):
     sv.sv_accept(p, q, toks_d, batch.uniforms, None, out=(n, nx))
     torch.cuda.synchronize()
     n, nx = host(n).numpy(), host(nx).numpy()
-    n_o, nx_o, fl = oracle.accept(p_o, q_o, toks, host(batch.uniforms), None)
     # a top-p boundary close call may change a whole row: treat it as a ratio flag
     topp = (fp & oracle.FLAG_TOPP).any(1) | (fq & oracle.FLAG_TOPP).any(1)
-    fl = np.where(topp, fl | oracle.FLAG_RATIO, fl)
-    compare_sampled(n, nx, n_o, nx_o, fl, "filtered pipeline")
-    flagged = (fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0
+    u_h = host(batch.uniforms)
+    compare_sampled(n, nx, lambda w: oracle.accept(p_o, q_o, toks, u_h, None, rel_window=w), "filtered pipeline",
+                    extra_ratio=topp)
+    _, _, fl = oracle.accept(p_o, q_o, toks, u_h, None)
+    flagged = ((fl & (oracle.FLAG_RATIO | oracle.FLAG_CDF)) != 0) | topp
     # the emitted token always survives the filters of its row
     for b in np.nonzero(~flagged)[0]:
         assert p_o[b, n[b], nx[b]] > 0.0

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from tests.sampled_check import compare_sampled
+from tests.sampled_check import chunked, compare_sampled
 
 pytestmark = pytest.mark.gpu
 
@@ -71,23 +71,11 @@ def check_greedy(sv, batch, label):
     return n_o
 
 
-def oracle_accept_chunked(p, q, tokens, u, lens, chunk=64):
-    """oracle.accept over a batch of device tensors, ``chunk`` sequences per call."""
-    B = p.shape[0]
-    outs = [np.empty(B, np.int32) for _ in range(3)]
-    for b0 in range(0, B, chunk):
-        sl = slice(b0, min(B, b0 + chunk))
-        r = oracle.accept(host(p[sl]), host(q[sl]) if q is not None else None, host(tokens[sl]) if tokens is not None
-                          else None, host(u[sl]), None if lens is None else host(lens[sl]))
-        for o, v in zip(outs, r):
-            o[sl] = v
-    return outs
-
-
 def check_accept(sv, p, q, tokens, u, lens, label):
     n, nx = run_accept(sv, p, q, tokens, u, lens)
-    n_o, nx_o, fl = oracle_accept_chunked(p, q, tokens, u, lens)
-    compare_sampled(n, nx, n_o, nx_o, fl, label)
+    sel = (lambda x, sl: None if x is None else host(x[sl]))
+    compare_sampled(n, nx, lambda w: chunked(lambda sl: oracle.accept(
+        sel(p, sl), sel(q, sl), sel(tokens, sl), sel(u, sl), sel(lens, sl), rel_window=w), p.shape[0]), label)
     return n, nx
 
 
@@ -233,14 +221,10 @@ def test_full_size_pipeline_end_to_end(sv, name):
     q = sv.sv_softmax_warp(batch.draft, T, batch.lens, 0)
     n, nx = run_accept(sv, p, q, batch.tokens, batch.uniforms, batch.lens)
     del p, q
-    B = batch.B
-    n_o, nx_o, fl = (np.empty(B, np.int32) for _ in range(3))
-    for b0 in range(0, B, 64):
-        sl = slice(b0, min(B, b0 + 64))
-        n_o[sl], nx_o[sl], fl[sl] = oracle.accept_logits(
-            host(batch.target[sl]), host(batch.draft[sl]), host(batch.tokens[sl]), host(batch.uniforms[sl]),
-            None if batch.lens is None else host(batch.lens[sl]), T)
-    compare_sampled(n, nx, n_o, nx_o, fl, f"{name}/warp->accept end to end")
+    sel = (lambda x, sl: None if x is None else host(x[sl]))
+    compare_sampled(n, nx, lambda w: chunked(lambda sl: oracle.accept_logits(
+        sel(batch.target, sl), sel(batch.draft, sl), sel(batch.tokens, sl), sel(batch.uniforms, sl),
+        sel(batch.lens, sl), T, rel_window=w), batch.B), f"{name}/warp->accept end to end")
 
 
 def test_single_sequence_rounds_follow_acceptance_law(sv):
@@ -251,10 +235,14 @@ def test_single_sequence_rounds_follow_acceptance_law(sv):
     for r in range(600):
         b = synth.generate(name, "cuda", round_index=r)
         n, nx = run_accept(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens)
-        n_o, nx_o, fl = oracle.accept(host(b.target), host(b.draft), host(b.tokens), host(b.uniforms))
-        rounds.append((n[0], nx[0], n_o[0], nx_o[0], fl[0]))
+        rounds.append((n[0], nx[0], host(b.tokens), host(b.uniforms)))
         ns.append(int(n[0]))
-    compare_sampled(*(np.array(c) for c in zip(*rounds)), "600 rounds")
+    p_h, q_h = host(b.target), host(b.draft)  # the same p and q every round; fresh tokens and uniforms
+
+    def oracle_at(w):
+        res = [oracle.accept(p_h, q_h, t, u, rel_window=w) for _, _, t, u in rounds]
+        return tuple(np.array([r[k][0] for r in res]) for k in range(3))
+    compare_sampled(np.array([r[0] for r in rounds]), np.array([r[1] for r in rounds]), oracle_at, "600 rounds")
     p = host(b.target)[0].double().numpy()
     q = host(b.draft)[0].double().numpy()
     a = np.minimum(p[:4], q).sum(-1)
@@ -383,8 +371,7 @@ def test_accept_unaligned_and_tiny_rows(sv):
         t = rng.integers(0, V, size=(B, K)).astype(np.int32)
         u = rng.random((B, K + 1)).astype(np.float32)
         n, nx = run_accept(sv, dev(p), dev(q), dev(t), dev(u), None)
-        n_o, nx_o, fl = oracle.accept(p, q, t, u)
-        compare_sampled(n, nx, n_o, nx_o, fl, f"tiny V={V}")
+        compare_sampled(n, nx, lambda w: oracle.accept(p, q, t, u, rel_window=w), f"tiny V={V}")
 
 
 def test_bitwise_determinism(sv):
@@ -489,13 +476,14 @@ def test_maximum_draft_length(sv, V):
     zd = zt[:, :K].clone()
     u = torch.rand(B, K + 1, generator=g) * 0.999
     n2, nx2 = sv.sv_accept_logits(zt.cuda(), zd.cuda(), tok.cuda(), u.cuda(), 1.0, lens.cuda())
-    n2_o, nx2_o, fl = oracle.accept_logits(zt, zd, tok, u, lens, 1.0)
-    compare_sampled(host(n2).numpy(), host(nx2).numpy(), n2_o, nx2_o, fl, f"K=64 V={V} from logits")
+    n2_o, _ = compare_sampled(host(n2).numpy(), host(nx2).numpy(),
+                              lambda w: oracle.accept_logits(zt, zd, tok, u, lens, 1.0, rel_window=w),
+                              f"K=64 V={V} from logits")
     assert list(n2_o) == [K, K, K, 10]
     p = torch.softmax(zt.double(), -1).float()
     q = p[:, :K].clone()
     n3, nx3 = sv.sv_accept(p.cuda(), q.cuda(), tok.cuda(), u.cuda(), lens.cuda())
-    n3_o, nx3_o, fl3 = oracle.accept(p, q, tok, u, lens)
-    compare_sampled(host(n3).numpy(), host(nx3).numpy(), n3_o, nx3_o, fl3, f"K=64 V={V} probabilities")
+    n3_o, _ = compare_sampled(host(n3).numpy(), host(nx3).numpy(),
+                              lambda w: oracle.accept(p, q, tok, u, lens, rel_window=w), f"K=64 V={V} probabilities")
     assert list(n3_o) == [K, K, K, 10]
     print(f"[K=64, V={V}] greedy n {n_o.tolist()}, sampled n {n2_o.tolist()}", flush=True)
