@@ -36,7 +36,7 @@ class GateParams(ctypes.Structure):
                 ("verify_slope_ms", ctypes.c_double), ("plain_ms", ctypes.c_double), ("margin", ctypes.c_double),
                 ("min_draft", ctypes.c_int32), ("margin_threshold", ctypes.c_float)]
 SV_MAX_K = 64
-_STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_HIP"}
+_STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_HIP", 4: "SV_ERR_WORKSPACE"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -89,7 +89,7 @@ def _load():
     lib.sv_accept_logits_workspace_bytes.argtypes = [i32, i32, i64]
     lib.sv_accept_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_accept_logits.restype = c_int
-    if lib.sv_abi_version() != 2:
+    if lib.sv_abi_version() != 3:
         raise ImportError("libspecverify ABI version mismatch")
     return lib
 
@@ -155,16 +155,26 @@ def _out(shape, device, out: Optional[torch.Tensor], dtype, what) -> torch.Tenso
 
 
 _WORKSPACES = {}
+_RETIRED = []  # superseded workspaces, kept alive for the life of the process
 
 
 def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
     """A workspace of at least nbytes, kept per (device, stream) so that calls
-    on one stream reuse it and calls on different streams never share one."""
+    on one stream reuse it and calls on different streams never share one.
+
+    A workspace is never freed: a HIP graph captured earlier holds its raw
+    address, and a replay after the buffer went back to the allocator would
+    write exchange slots into another tensor's memory. When a call needs more
+    bytes, the old buffer is retired (kept alive) and the new one is at least
+    twice its size, so a stream keeps O(log(largest size)) buffers."""
     if nbytes == 0:
         return None
     key = (device.index, stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _RETIRED.append(ws)
+            nbytes = max(nbytes, 2 * ws.numel())
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws

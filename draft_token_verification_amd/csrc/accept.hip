@@ -970,7 +970,8 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
         segment_shape(Ls, m, nseg);
         const int64_t words = (int64_t)(need / sizeof(unsigned long long));
         unsigned long long* slots = (unsigned long long*)workspace;
-        launch_fill_empty(slots, words, stream);
+        const hipError_t fe = launch_fill_empty(slots, words, stream);
+        if (fe != hipSuccess) return fe;  // without the fill, stale slots would read as published
         const size_t lds = 2 * (size_t)nseg * sizeof(double);
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
         const int wl = get_wait_limit();

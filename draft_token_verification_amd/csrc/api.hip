@@ -63,6 +63,17 @@ sv_status check_sizes(const char* fn, int32_t B, int32_t K, int64_t V) {
     return SV_OK;
 }
 
+// A workspace of workspace_bytes > 0 must hold at least `need` bytes and be
+// 8-byte aligned; workspace_bytes == 0 (or a null pointer) means none.
+sv_status check_workspace(const char* fn, const void* workspace, size_t workspace_bytes, size_t need) {
+    if (workspace == nullptr || workspace_bytes == 0) return SV_OK;
+    if (workspace_bytes < need)
+        return fail(SV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed (pass 0 bytes for none)", fn,
+                    workspace_bytes, need);
+    if (!aligned(workspace, 8)) return fail(SV_ERR_INVALID_ARG, "%s: workspace not 8-byte aligned", fn);
+    return SV_OK;
+}
+
 sv_status launched(const char* fn, hipError_t e) {
     if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
@@ -82,6 +93,8 @@ sv_status greedy_common(const char* fn, const void* target, int dtype, int32_t B
         (draft_tokens && !aligned(draft_tokens, 4)) || (draft_lens && !aligned(draft_lens, 4)) ||
         (top2_margin && !aligned(top2_margin, 4)))
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_workspace(fn, workspace, workspace_bytes, sv::greedy_workspace_bytes(B, K, (int)V))) != SV_OK)
+        return st;
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_greedy(target, dtype == SV_BF16, B, K, (int)V, draft_tokens, draft_lens, n_accepted,
                                           next_token, top2_margin, workspace, workspace_bytes, (hipStream_t)stream));
@@ -101,6 +114,7 @@ const char* sv_status_string(int status) {
     case SV_ERR_INVALID_ARG: return "SV_ERR_INVALID_ARG: an argument is out of range, null or misaligned";
     case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: the current device is not gfx950";
     case SV_ERR_HIP: return "SV_ERR_HIP: the HIP runtime reported an error";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: the workspace is smaller than the call needs";
     default: return "unknown sv_status";
     }
 }
@@ -136,6 +150,8 @@ sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, i
     if (!logits || !probs) return fail(SV_ERR_INVALID_ARG, "%s: null logits or probs", fn);
     if (!aligned(logits, dtype_bytes(dtype)) || !aligned(probs, 4) || (draft_lens && !aligned(draft_lens, 4)))
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_workspace(fn, workspace, workspace_bytes, sv::warp_workspace_bytes(B, R, (int)V))) != SV_OK)
+        return st;
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_warp(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows, temperature,
                                         probs, workspace, workspace_bytes, (hipStream_t)stream));
@@ -298,6 +314,9 @@ sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, 
         !aligned(n_accepted, 4) || !aligned(next_token, 4) || (draft_tokens && !aligned(draft_tokens, 4)) ||
         (draft_lens && !aligned(draft_lens, 4)))
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if ((st = check_workspace(fn, workspace, workspace_bytes, sv::accept_logits_workspace_bytes(B, K, (int)V))) !=
+        SV_OK)
+        return st;
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_accept_logits(target_logits, draft_logits, dtype == SV_BF16, B, K, (int)V,
                                                  temperature, draft_tokens, draft_lens, uniforms, n_accepted,

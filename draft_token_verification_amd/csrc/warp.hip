@@ -364,6 +364,8 @@ hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const
         const int64_t nslots = (int64_t)B * R * G;
         hipLaunchKernelGGL(fill_slots, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, stream,
                            (unsigned long long*)workspace, nslots);
+        const hipError_t fe = hipGetLastError();
+        if (fe != hipSuccess) return fe;  // without the fill, stale slots would read as published
         const dim3 grid((unsigned)((int64_t)B * R * G));
         if (bf16)
             hipLaunchKernelGGL((warp_coop_kernel<true>), grid, dim3(kThreads), 0, stream, logits, R, V, G, lens,

@@ -31,6 +31,12 @@
  *    order.
  *  - Host-side argument checks return an error before anything is enqueued;
  *    sv_last_error() then describes it. A launch failure returns SV_ERR_HIP.
+ *  - Workspaces: a call that takes one accepts either none (a null pointer
+ *    or 0 bytes: a path that needs no exchange slots runs instead, with the
+ *    same results) or at least the bytes its *_workspace_bytes query returns
+ *    for the same sizes, 8-byte aligned; anything in between is
+ *    SV_ERR_WORKSPACE, so an undersized buffer never silently selects the
+ *    slower path.
  *  - Data-dependent conditions are defined behaviour, not errors: a draft
  *    token outside [0, V) is a greedy miss and a sampled rejection and is
  *    never dereferenced; draft_lens are clamped. Rows, tokens and uniforms a
@@ -47,14 +53,15 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 #define SV_MAX_K 64 /* draft lengths up to 64, one wavefront lane per position */
 
 typedef enum {
     SV_OK = 0,
     SV_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer, bad dtype */
     SV_ERR_UNSUPPORTED = 2, /* the current device is not gfx950 */
-    SV_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+    SV_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+    SV_ERR_WORKSPACE = 4    /* a workspace of more than 0 bytes is smaller than its query returns */
 } sv_status;
 
 typedef enum {
@@ -92,7 +99,8 @@ const char* sv_last_error(void);
  *              R, V) bytes, 8-byte aligned, owned by the caller, contents
  *              irrelevant (the call initialises it on `stream`); it holds the
  *              per-row partial statistics the workgroups of a row exchange.
- *              NULL (or too small) selects a slower path that needs none.
+ *              NULL or 0 bytes selects a slower path that needs none;
+ *              fewer bytes than the query returns is SV_ERR_WORKSPACE.
  *              Calls that overlap in time must not share a workspace.
  * Accuracy: |probs - exact| <= 1e-5 absolute per element (fp32 arithmetic,
  * exp2 with a folded log2(e)/T scale, fixed-order sums); results are bitwise
@@ -100,7 +108,7 @@ const char* sv_last_error(void);
  * timing.
  * Errors: SV_ERR_INVALID_ARG for a null logits/probs, B < 0, R < 1,
  * extra_rows not in [0, R], V < 1 or V > INT32_MAX, B*R > INT32_MAX, a bad
- * dtype or temperature, or misaligned pointers.
+ * dtype or temperature, or misaligned pointers; SV_ERR_WORKSPACE as above.
  */
 sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
                           const int32_t* draft_lens, int32_t extra_rows, float temperature,
@@ -173,7 +181,8 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
  *              and are scratch afterwards. With it, each sequence's rows are
  *              split over up to 8 workgroups that exchange partial argmaxes
  *              (a long chain of matches is read by several compute units);
- *              NULL (or too small) selects one workgroup per sequence. The
+ *              NULL or 0 bytes selects one workgroup per sequence (fewer
+ *              bytes than the query returns is SV_ERR_WORKSPACE). The
  *              results are identical either way.
  * Result: n_accepted[b] in [0, K_b], next_token[b] in [0, V); bit-exact.
  * Errors: SV_ERR_INVALID_ARG for null required pointers, B < 0, K < 0,
@@ -314,9 +323,11 @@ sv_status sv_accept(const float* target_probs, const float* draft_probs, int32_t
  *              workgroups sharing a sequence's rows exchange partial
  *              statistics. With it each sequence's rows are split over
  *              several workgroups (a long chain of accepted positions runs on
- *              several compute units); NULL, too small, or a size of 0 from
- *              the query selects one workgroup per sequence. Results are
- *              identical either way up to the rounding of the partial sums.
+ *              several compute units); NULL or 0 bytes (and any workspace
+ *              when the query returns 0) selects one workgroup per sequence;
+ *              fewer bytes than the query returns is SV_ERR_WORKSPACE.
+ *              Results are identical either way up to the rounding of the
+ *              partial sums.
  *              Calls that overlap in time must not share a workspace.
  * Accuracy: the row masses come from fp32 exponentials with fp64 sums
  * (relative error about 1e-7); the accept ratio p(t)/q(t) and every residual

@@ -51,10 +51,11 @@ def test_library_exports_every_declared_symbol(sv):
 
 def test_constants_match_header(sv):
     text = open(HEADER).read()
-    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 2
+    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 3
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
     assert re.search(r"SV_F32 = 0", text) and re.search(r"SV_BF16 = 1", text)
-    for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARG"), (2, "SV_ERR_UNSUPPORTED"), (3, "SV_ERR_HIP")]:
+    for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARG"), (2, "SV_ERR_UNSUPPORTED"), (3, "SV_ERR_HIP"),
+                       (4, "SV_ERR_WORKSPACE")]:
         assert re.search(rf"{name} = {code}", text)
         assert sv._lib.sv_status_string(code).decode().startswith(name)
 
@@ -252,3 +253,30 @@ def test_verify_greedy_workspace_size(sv):
     assert sv.sv_verify_greedy_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
     assert sv.sv_verify_greedy_workspace_bytes(0, 4, 256000) == 0
     assert sv.sv_verify_greedy_workspace_bytes(8, 65, 256000) == 0
+
+
+ALIGNED = ctypes.c_void_p(0x2000)
+
+
+def test_undersized_workspace_is_an_error(sv):
+    """A workspace of more than 0 bytes but fewer than the query returns is
+    SV_ERR_WORKSPACE (never a silent switch to the slower path); 0 bytes means
+    none; a misaligned one is SV_ERR_INVALID_ARG. All checked before any device
+    is looked for."""
+    lib = sv._lib
+    need = sv.sv_softmax_warp_workspace_bytes(4, 17, 256000)
+    assert need > 0
+    assert lib.sv_softmax_warp(FAKE, 1, 4, 17, 256000, None, 1, 1.0, FAKE, ALIGNED, need - 8, None) == 4
+    assert "workspace" in lib.sv_last_error().decode() and str(need) in lib.sv_last_error().decode()
+    assert lib.sv_softmax_warp(FAKE, 1, 4, 17, 256000, None, 1, 1.0, FAKE, ODD, need, None) == 1
+    assert "aligned" in lib.sv_last_error().decode()
+    need = sv.sv_verify_greedy_workspace_bytes(64, 4, 256000)
+    assert need > 0
+    assert lib.sv_verify_greedy(FAKE, 1, 64, 4, 256000, FAKE, None, FAKE, FAKE, ALIGNED, 16, None) == 4
+    assert lib.sv_verify_greedy_margin(FAKE, 1, 64, 4, 256000, FAKE, None, FAKE, FAKE, FAKE, ALIGNED, need - 1,
+                                       None) == 4
+    need = sv.sv_accept_logits_workspace_bytes(64, 4, 256000)
+    assert need > 0
+    assert lib.sv_accept_logits(FAKE, FAKE, 1, 64, 4, 256000, 1.0, FAKE, None, FAKE, FAKE, FAKE, ALIGNED, need // 2,
+                                None) == 4
+    assert sv._lib.sv_status_string(4).decode().startswith("SV_ERR_WORKSPACE")

@@ -87,3 +87,40 @@ def test_captured_round_replays_like_eager(sv, case):
             assert torch.equal(a, e), f"{name}: replay {rep}: {nm} differs from the eager call"
         print(f"[{name}] replay {rep}: all outputs equal the eager round "
               f"(greedy mean n {eager_out[2].float().mean().item():.2f})", flush=True)
+
+
+def test_replay_after_the_stream_needs_a_larger_workspace(sv):
+    """A call on the capture stream that needs a larger workspace than the
+    captured round must not free the buffer the graph holds: the replay after
+    it still equals the eager round bit for bit (the binding retires the old
+    buffer instead of returning it to the allocator, where a new tensor could
+    take its memory)."""
+    name = "logits-bf16-b512-k16-v256000-zipf"
+    dev = torch.device("cuda", 0)
+    small = synth.generate(name, dev, B=8)
+    big = synth.generate(name, dev, B=64, seed=77)
+    T = small.temperature
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = new_outputs(small, dev)
+    with torch.cuda.stream(s):
+        round_calls(sv, small, small.tokens, small.uniforms, outs, T)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        round_calls(sv, small, small.tokens, small.uniforms, outs, T)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # needs larger workspaces on the same stream
+        big_outs = new_outputs(big, dev)
+        round_calls(sv, big, big.tokens, big.uniforms, big_outs, T)
+        filler = [torch.full((1 << 20,), 3.0, device=dev) for _ in range(8)]  # memory the allocator hands out now
+    torch.cuda.synchronize()
+    eager = new_outputs(small, dev)
+    round_calls(sv, small, small.tokens, small.uniforms, eager, T)
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, e in zip(outs, eager):
+            assert torch.equal(a, e), f"replay {rep} after a larger call differs from the eager round"
+        assert all(bool((f == 3.0).all()) for f in filler), "a replay wrote into memory the allocator reused"
+    print(f"[graph + larger workspace] 2 replays equal the eager round; fillers intact", flush=True)
