@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
-__all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_set_wait_limit", "sv_verify_greedy",
+__all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_softmax_warp_noalloc",
+           "SV_NOALLOC_SCRATCH_BYTES", "sv_set_wait_limit", "sv_verify_greedy",
            "sv_verify_greedy_workspace_bytes", "sv_accept",
            "sv_accept_logits", "sv_accept_logits_workspace_bytes", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
            "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder",
@@ -64,6 +65,8 @@ def _load():
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_softmax_warp.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.sv_softmax_warp_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.sv_softmax_warp_noalloc.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp]
+    lib.sv_softmax_warp_noalloc.restype = c_int
     lib.sv_verify_greedy_margin.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sv_verify_greedy_margin.restype = c_int
     lib.sv_gate_update.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_double, vp]
@@ -234,6 +237,32 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
         st = _lib.sv_softmax_warp(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens), int(extra_rows),
                                   float(temperature), _ptr(probs), _ptr(workspace), ws_bytes, stream)
     _check("sv_softmax_warp", st)
+    return probs
+
+
+SV_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def sv_softmax_warp_noalloc(logits: torch.Tensor, temperature: float, draft_lens: Optional[torch.Tensor],
+                            extra_rows: int, out: torch.Tensor) -> torch.Tensor:
+    """sv_softmax_warp without a workspace or any allocation: the library's fixed
+    per-device scratch array holds the exchange slots. ``out`` (fp32 [B, R, V]) is
+    required; calls that overlap in time on one device must not be issued (they
+    share the array)."""
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dev = logits.device
+    if draft_lens is not None:
+        _dev(draft_lens, "draft_lens")
+        if draft_lens.dtype != torch.int32 or tuple(draft_lens.shape) != (B,) or draft_lens.device != dev:
+            raise ValueError("draft_lens must be int32 [B] on the logits' device")
+    probs = _out((B, R, V), dev, out, torch.float32, "out")
+    with torch.cuda.device(dev):
+        st = _lib.sv_softmax_warp_noalloc(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(draft_lens),
+                                          int(extra_rows), float(temperature), _ptr(probs), _stream(dev))
+    _check("sv_softmax_warp_noalloc", st)
     return probs
 
 

@@ -157,6 +157,38 @@ sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, i
                                         probs, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
+sv_status sv_softmax_warp_noalloc(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
+                                  const int32_t* draft_lens, int32_t extra_rows, float temperature, float* probs,
+                                  void* stream) {
+    static_assert(sv::kStaticScratchBytes == SV_NOALLOC_SCRATCH_BYTES, "header and library disagree on the scratch size");
+    const char* fn = "sv_softmax_warp_noalloc";
+    sv_status st;
+    if ((st = check_dtype(dtype)) != SV_OK) return st;
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (R < 1) return fail(SV_ERR_INVALID_ARG, "%s: R = %d < 1", fn, R);
+    if (extra_rows < 0 || extra_rows > R)
+        return fail(SV_ERR_INVALID_ARG, "%s: extra_rows = %d not in [0, R]", fn, extra_rows);
+    if (V < 1 || V > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: V = %lld not in [1, 2^31-1]", fn, (long long)V);
+    if ((int64_t)B * R > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*R exceeds 2^31-1 rows", fn);
+    if (!(temperature > 0.0f) || !std::isfinite(temperature))
+        return fail(SV_ERR_INVALID_ARG, "%s: temperature %g must be finite and > 0", fn, (double)temperature);
+    if (B == 0) return ok();
+    if (!logits || !probs) return fail(SV_ERR_INVALID_ARG, "%s: null logits or probs", fn);
+    if (!aligned(logits, dtype_bytes(dtype)) || !aligned(probs, 4) || (draft_lens && !aligned(draft_lens, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    const size_t need = sv::warp_workspace_bytes(B, R, (int)V);
+    if (need > sv::kStaticScratchBytes)
+        return fail(SV_ERR_WORKSPACE, "%s: %d x %d rows of %lld need %zu bytes of exchange slots; the static scratch "
+                    "holds %zu (use sv_softmax_warp with a workspace)", fn, B, R, (long long)V, need,
+                    sv::kStaticScratchBytes);
+    if ((st = check_device()) != SV_OK) return st;
+    void* scratch = nullptr;
+    const hipError_t e = sv::static_scratch(&scratch);
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: hipGetSymbolAddress: %s", fn, hipGetErrorString(e));
+    return launched(fn, sv::launch_warp(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows, temperature,
+                                        probs, scratch, sv::kStaticScratchBytes, (hipStream_t)stream));
+}
+
 sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
                                    const int32_t* draft_lens, int32_t extra_rows, float temperature,
                                    const int32_t* top_k, const float* top_p, float* probs, void* stream) {

@@ -68,6 +68,12 @@ hipError_t launch_commit(int32_t* seq, int32_t* seq_len, int32_t* done, int B, i
 // Workspace the cooperative warp path needs (0: that path does not apply to V).
 size_t warp_workspace_bytes(int B, int R, int V);
 
+// The device array that serves as the warp's workspace for callers that cannot
+// allocate (SV_NOALLOC_SCRATCH_BYTES bytes), and its address on the current
+// device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Polls a cooperative warp workgroup makes before it recomputes its row alone
 // (applies to launches made after the call, on every device).
 void set_wait_limit(int tries);

@@ -27,6 +27,7 @@
 //   loads, then the normalised write reading the row again.
 // Rows past a sequence's live count exit at once in both.
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -395,5 +396,37 @@ hipError_t launch_warp(const void* logits, bool bf16, int B, int R, int V, const
 }
 
 int get_wait_limit() { return g_wait_limit.load(); }
+
+// ---- exchange slots without a caller's workspace ---------------------------
+// The cooperative warp's slots in a fixed device array, for callers that
+// cannot allocate: one copy per device, alive until the process ends, shared
+// by every call on that device (so calls that overlap on one device race; the
+// fill kernel resets the slots at the start of each call). In host code the
+// array's name stands for a host shadow, never a device address: the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) unsigned long long scratch[kStaticScratchBytes / sizeof(unsigned long long)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 }  // namespace sv

@@ -118,6 +118,26 @@ sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, i
  * does not apply: V not a multiple of 4, or V above about 2 million). */
 size_t sv_softmax_warp_workspace_bytes(int32_t B, int32_t R, int64_t V);
 
+/*
+ * sv_softmax_warp_noalloc -- sv_softmax_warp for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It calls no allocating routine; the
+ * exchange slots that sv_softmax_warp takes from a caller's workspace live in
+ * a fixed device array of SV_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (one per device, held until the process ends).
+ * Arguments, results (bitwise those of sv_softmax_warp with a workspace) and
+ * errors as sv_softmax_warp, plus SV_ERR_WORKSPACE when the call needs more
+ * slots than the array holds, i.e. sv_softmax_warp_workspace_bytes(B, R, V)
+ * > SV_NOALLOC_SCRATCH_BYTES (up to 131072 row slices: 8704 rows of 256000).
+ * Every call on a device shares that device's array and leaves its slots
+ * behind (each call resets them on its stream first), so calls that overlap
+ * in time on one device race: serialise them on one stream.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES 1048576
+sv_status sv_softmax_warp_noalloc(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
+                                  const int32_t* draft_lens, int32_t extra_rows, float temperature, float* probs,
+                                  void* stream);
+
 /* Diagnostic control, process-wide: how many times a workgroup polls for the
  * partial results of the other workgroups that share its row or sequence
  * before computing them all itself (default 16384), for calls made after

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                                     "sv_commit", "sv_gate_choose",
                                     "sv_gate_update",
                                     "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
-                                    "sv_softmax_warp_workspace_bytes", "sv_status_string", "sv_verify_greedy",
+                                    "sv_softmax_warp_noalloc", "sv_softmax_warp_workspace_bytes", "sv_status_string",
+                                    "sv_verify_greedy",
                                     "sv_verify_greedy_margin", "sv_verify_greedy_workspace_bytes"]
 
 
@@ -280,3 +281,21 @@ def test_undersized_workspace_is_an_error(sv):
     assert lib.sv_accept_logits(FAKE, FAKE, 1, 64, 4, 256000, 1.0, FAKE, None, FAKE, FAKE, FAKE, ALIGNED, need // 2,
                                 None) == 4
     assert sv._lib.sv_status_string(4).decode().startswith("SV_ERR_WORKSPACE")
+
+
+def test_noalloc_warp_host_checks(sv):
+    """sv_softmax_warp_noalloc validates like sv_softmax_warp and refuses, before
+    looking for a device, a call that needs more exchange slots than its static
+    scratch holds."""
+    lib = sv._lib
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SV_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1)) == sv.SV_NOALLOC_SCRATCH_BYTES
+    assert sv.sv_softmax_warp_workspace_bytes(512, 17, 256000) <= sv.SV_NOALLOC_SCRATCH_BYTES
+    assert sv.sv_softmax_warp_workspace_bytes(2048, 17, 256000) > sv.SV_NOALLOC_SCRATCH_BYTES
+    assert lib.sv_softmax_warp_noalloc(FAKE, 1, 2048, 17, 256000, None, 1, 1.0, FAKE, None) == 4
+    assert "static scratch" in lib.sv_last_error().decode()
+    assert lib.sv_softmax_warp_noalloc(FAKE, 1, 2, 0, 100, None, 0, 1.0, FAKE, None) == 1
+    assert lib.sv_softmax_warp_noalloc(FAKE, 1, 2, 3, 100, None, 1, 0.0, FAKE, None) == 1
+    assert lib.sv_softmax_warp_noalloc(None, 1, 2, 3, 100, None, 1, 1.0, FAKE, None) == 1
+    assert lib.sv_softmax_warp_noalloc(ODD, 0, 2, 3, 100, None, 1, 1.0, FAKE, None) == 1
+    assert lib.sv_softmax_warp_noalloc(None, 1, 0, 3, 100, None, 1, 1.0, None, None) == 0
