@@ -161,7 +161,7 @@ _WORKSPACES = {}
 _RETIRED = []  # superseded workspaces, kept alive for the life of the process
 
 
-def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, device, stream, kind: str = "fill") -> Optional[torch.Tensor]:
     """A workspace of at least nbytes, kept per (device, stream) so that calls
     on one stream reuse it and calls on different streams never share one.
 
@@ -169,25 +169,33 @@ def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
     address, and a replay after the buffer went back to the allocator would
     write exchange slots into another tensor's memory. When a call needs more
     bytes, the old buffer is retired (kept alive) and the new one is at least
-    twice its size, so a stream keeps O(log(largest size)) buffers."""
+    twice its size, so a stream keeps O(log(largest size)) buffers.
+
+    ``kind`` "zero" is the greedy verify's workspace, kept apart from the others:
+    it must hold zeros before its first use and only the greedy verify may
+    write it (every call leaves it zero); the others reset their slots
+    themselves at each call."""
     if nbytes == 0:
         return None
-    key = (device.index, stream)
+    key = (device.index, stream, kind)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         if ws is not None:
             _RETIRED.append(ws)
             nbytes = max(nbytes, 2 * ws.numel())
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if kind == "zero":
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        else:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
 
-def _workspace_arg(workspace: Optional[torch.Tensor], need: int, device, stream, what: str):
+def _workspace_arg(workspace: Optional[torch.Tensor], need: int, device, stream, what: str, kind: str = "fill"):
     """(pointer, bytes) of the caller's workspace, or of the one kept per
     device and stream when none is given."""
     if workspace is None:
-        workspace = _workspace(need, device, stream)
+        workspace = _workspace(need, device, stream, kind)
     elif workspace.device != device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous uint8 tensor on the {what}' device")
     return _ptr(workspace), 0 if workspace is None else workspace.numel()
@@ -291,7 +299,7 @@ def sv_verify_greedy_margin(target: torch.Tensor, draft_tokens: Optional[torch.T
     with torch.cuda.device(dev):
         stream = _stream(dev)
         ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
-                                      stream.value, "target")
+                                      stream.value, "target", "zero")
         st = _lib.sv_verify_greedy_margin(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
                                           _ptr(n), _ptr(nx), _ptr(mg), ws, ws_bytes, stream)
     _check("sv_verify_greedy_margin", st)
@@ -427,7 +435,9 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
     """Greedy verify of target [B, K+1, V] (fp32/bf16 logits or probs) -> (n_accepted[B], next_token[B]).
 
     ``workspace`` (uint8 device tensor) defaults to one kept per device and stream, sized by
-    sv_verify_greedy_workspace_bytes; a zero-size one selects one workgroup per sequence.
+    sv_verify_greedy_workspace_bytes; a zero-size one selects one workgroup per sequence. A
+    workspace of your own must hold zeros before its first use and serve only the greedy verify
+    (every call leaves it zero).
     """
     _dev(target, "target")
     if target.dim() != 3:
@@ -446,7 +456,7 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
     with torch.cuda.device(dev):
         stream = _stream(dev)
         ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
-                                      stream.value, "target")
+                                      stream.value, "target", "zero")
         st = _lib.sv_verify_greedy(_ptr(target), _dtype_code(target, "target"), B, K, V, _ptr(toks), _ptr(lens),
                                    _ptr(n), _ptr(nx), ws, ws_bytes, stream)
     _check("sv_verify_greedy", st)

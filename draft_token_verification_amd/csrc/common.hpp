@@ -168,7 +168,8 @@ constexpr unsigned long long kEmptySlot = ~0ull;  // a NaN pattern: never a publ
 // Wavefront 0 polls words set[0 .. nw) (bounded) and copies them to LDS;
 // returns whether all were published (uniform after the barrier).
 __device__ __forceinline__ bool gather_words(const unsigned long long* set, int nw, int wait_limit,
-                                             unsigned long long* s_words, int* s_ready) {
+                                             unsigned long long* s_words, int* s_ready,
+                                             unsigned long long empty = kEmptySlot) {
     const int tid = threadIdx.x;
     if (tid < kWave) {
         bool ready = false;
@@ -176,7 +177,7 @@ __device__ __forceinline__ bool gather_words(const unsigned long long* set, int 
             bool mine = true;
             for (int k = tid; k < nw; k += kWave) {
                 const unsigned long long v = __hip_atomic_load(set + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (v == kEmptySlot)
+                if (v == empty)
                     mine = false;
                 else
                     s_words[k] = v;

@@ -128,6 +128,39 @@ struct RowReader<false> {
     }
 };
 
+// Merge of the lanes' (best, bidx, second) over a workgroup of NW wavefronts:
+// the wave-wide merge, then the NW wave results through LDS buffer `slot`,
+// merged again by every wavefront, so the result (index returned, maximum and
+// runner-up in vmax / vsecond) is uniform. Contains one barrier.
+template <bool M, int NW>
+__device__ __forceinline__ int block_merge(float best, int bidx, float second, float (*lds_v)[NW], int (*lds_i)[NW],
+                                           float (*lds_s)[NW], int slot, float& vmax, float& vsecond) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (M) {
+        wave_top2(best, bidx, second);
+    } else {
+        wave_argmax(best, bidx);
+    }
+    if (lane == 0) {
+        lds_v[slot][wave] = best;
+        lds_i[slot][wave] = bidx;
+        if (M) lds_s[slot][wave] = second;
+    }
+    __syncthreads();
+    float v = lane < NW ? lds_v[slot][lane] : -INFINITY;
+    int i = lane < NW ? lds_i[slot][lane] : INT32_MAX;
+    if (M) {
+        float s = lane < NW ? lds_s[slot][lane] : -INFINITY;
+        wave_top2(v, i, s);
+        vmax = v;
+        vsecond = s;
+    } else {
+        wave_argmax(v, i);
+        vmax = v;
+    }
+    return i;
+}
+
 // Argmax of elements [x0, x0 + len) of a row (len >= 1), over a workgroup of
 // NW wavefronts. Returns the wave-uniform index (and, with M, the maximum and
 // runner-up values in vmax / vsecond); every lane of the workgroup must call
@@ -182,29 +215,7 @@ __device__ __forceinline__ int span_argmax(const void* row, int x0, int len, flo
         }
     }
 
-    if (M) {
-        wave_top2(best, bidx, second);
-    } else {
-        wave_argmax(best, bidx);
-    }
-    if (lane == 0) {
-        lds_v[slot][wave] = best;
-        lds_i[slot][wave] = bidx;
-        if (M) lds_s[slot][wave] = second;
-    }
-    __syncthreads();
-    float v = lane < NW ? lds_v[slot][lane] : -INFINITY;
-    int i = lane < NW ? lds_i[slot][lane] : INT32_MAX;
-    if (M) {
-        float s = lane < NW ? lds_s[slot][lane] : -INFINITY;
-        wave_top2(v, i, s);
-        vmax = v;
-        vsecond = s;
-    } else {
-        wave_argmax(v, i);
-        vmax = v;
-    }
-    return i;
+    return block_merge<M, NW>(best, bidx, second, lds_v, lds_i, lds_s, slot, vmax, vsecond);
 }
 
 // M: also write top2_margin[b] = max - runner-up of the row next_token comes
@@ -246,27 +257,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 //
 // The same walk with the rows of a sequence split into G slices of Ls
 // elements; workgroup (b, g) of 256 lanes owns slice g of every row of
-// sequence b. At each position every slice publishes its (value, index) --
-// and, with M, its runner-up value -- into sentinel-filled slots of the
-// caller's workspace, and every workgroup merges all G in slice order, so all
-// take the same decision. A long chain of matches thus reads each row with G
-// compute units instead of one. Every wait is bounded: a workgroup that gives
-// up computes the missing slices itself with the same code and lane mapping,
-// so the result is the same either way.
+// sequence b and reads it in one batch of loads (a 32 KB slice: one memory
+// round trip per position). At each position every slice publishes its
+// (value, index) -- and, with M, its runner-up value -- into slots of the
+// caller's workspace, and every workgroup merges all G, so all take the same
+// decision. A long chain of matches thus reads each row with G compute units
+// instead of one. Every wait is bounded: a workgroup that gives up computes
+// the missing slices itself, so the result is the same either way.
+//
+// The workspace needs no fill before a launch: an empty slot is a zero word
+// (a published word never is: it carries index + 1, or a set low bit), and
+// every launch leaves the workspace all zero again. When a workgroup is done
+// with its sequence (every slot access finished) it counts itself out on the
+// sequence's departure counter; the last of the G clears every slot word the
+// sequence used and the counter. So a workspace must hold zeros before its
+// first use, and the next launch finds it so.
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
-constexpr int kSliceUnroll = 6;  // 96 bytes per lane in flight (8 would spill)
-static_assert(kMaxCoopSlices <= 8, "slice results are merged by a butterfly over 8 lanes");
+constexpr int kSliceUnroll = 8;  // 128 bytes per lane in flight: a 32 KB slice in one batch
+constexpr int kMarginUnroll = 6;  // with the runner-up values (8 would spill): the slice in two batches
+constexpr int kMaxGreedySlices = kWave;  // slice results are merged across one wavefront
+
+// Wavefront 0 counts the workgroup out of its sequence once it has made its
+// last slot access; the last of the sequence's G workgroups clears the
+// sequence's `nwords` slot words and the counter, returning them to zero.
+// The count needs no fence in the common case: every gather polls the
+// workgroup's own word too, through the same device-coherent loads as the
+// others, so a workgroup's published words are visible before it counts
+// itself out, and its loads have all returned. Only a workgroup that gave up
+// waiting (`waited_out`) may still have a word in flight: it releases first.
+__device__ __forceinline__ void depart(unsigned long long* counter, unsigned long long* words, int nwords, int G,
+                                       bool waited_out) {
+    if (threadIdx.x >= kWave) return;
+    if (waited_out) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    unsigned long long prev = 0;
+    if (threadIdx.x == 0) prev = __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(prev, 0, kWave) != (unsigned long long)(G - 1)) return;
+    for (int k = threadIdx.x; k < nwords; k += kWave)
+        __hip_atomic_store(words + k, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <bool BF16, bool M>
 __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void greedy_sliced_kernel(
     const void* __restrict__ target, int K, int V, int G, int Ls, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ lens, int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token,
-    float* __restrict__ top2_margin, unsigned long long* __restrict__ slots, int wait_limit) {
+    float* __restrict__ top2_margin, unsigned long long* __restrict__ departed, unsigned long long* __restrict__ slots,
+    int wait_limit) {
     __shared__ float lds_v[2][kSliceWaves];
     __shared__ int lds_i[2][kSliceWaves];
     __shared__ float lds_s[M ? 2 : 1][kSliceWaves];
-    __shared__ unsigned long long s_words[2 * kMaxCoopSlices];
+    __shared__ unsigned long long s_words[2 * kMaxGreedySlices];
     __shared__ int s_ready;
     constexpr int W = M ? 2 : 1;  // words per slice and position
     const int b = blockIdx.x / G, g = blockIdx.x - b * G;
@@ -276,107 +317,131 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
     const size_t row_bytes = (size_t)V * (BF16 ? 2 : 4);
     const char* base = (const char*)target + (size_t)b * (size_t)(K + 1) * row_bytes;
     auto slice_len = [&](int k) { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); };
+    // never zero: the low half holds index + 1 (index < V <= INT32_MAX), or a set bit
     auto pack = [](float v, int i) {
-        return ((unsigned long long)__float_as_uint(v) << 32) | (unsigned long long)(uint32_t)i;
+        return ((unsigned long long)__float_as_uint(v) << 32) | (unsigned long long)((uint32_t)i + 1u);
     };
+    auto pack2 = [](float s) { return ((unsigned long long)__float_as_uint(s) << 32) | 1ull; };
     int parity = 0;
-    for (int i = 0;; ++i) {
+    int i = 0;
+    float v, s = -INFINITY;
+    int am;
+    bool waited_out = false;
+    for (;; ++i) {
         const char* row = base + (size_t)i * row_bytes;
         unsigned long long* set = slots + ((size_t)b * (K + 1) + i) * (size_t)(G * W);
-        float v, s = -INFINITY;
-        int am = span_argmax<BF16, M, kSliceWaves, kSliceUnroll>(row, g * Ls, slice_len(g), lds_v, lds_i, lds_s, parity, v, s);
+        s = -INFINITY;
+        am = span_argmax<BF16, M, kSliceWaves, M ? kMarginUnroll : kSliceUnroll>(row, g * Ls, slice_len(g), lds_v, lds_i,
+                                                                                 lds_s, parity, v, s);
         parity ^= 1;
         publish_word(set + g * W, pack(v, am));
-        if (M) publish_word(set + g * W + 1, (unsigned long long)__float_as_uint(s));
-        if (!gather_words(set, G * W, wait_limit, s_words, &s_ready)) {
+        if (M) publish_word(set + g * W + 1, pack2(s));
+        if (!gather_words(set, G * W, wait_limit, s_words, &s_ready, 0ull)) {
             // bounded wait ran out: every slice's result, computed here alike
+            // (two vectors per lane in flight: a rare path, kept small)
+            waited_out = true;
             for (int k = 0; k < G; ++k) {
                 float vk, sk = -INFINITY;
-                const int ik =
-                    span_argmax<BF16, M, kSliceWaves, kSliceUnroll>(row, k * Ls, slice_len(k), lds_v, lds_i, lds_s, parity, vk, sk);
+                const int ik = span_argmax<BF16, M, kSliceWaves, 2>(row, k * Ls, slice_len(k), lds_v, lds_i, lds_s,
+                                                                    parity, vk, sk);
                 parity ^= 1;
                 if (threadIdx.x == 0) {
                     s_words[k * W] = pack(vk, ik);
-                    if (M) s_words[k * W + 1] = (unsigned long long)__float_as_uint(sk);
+                    if (M) s_words[k * W + 1] = pack2(sk);
                 }
             }
             __syncthreads();
         }
-        // merge the G <= 8 slices: lane k holds slice k, a butterfly over lanes
-        // 0-7 (the (value, index) order is total and the runner-up is a plain
-        // maximum, so every merge order gives the same result), lane 0's result
+        // merge the G <= 64 slices: lane k holds slice k, the wave-wide merge
+        // (the (value, index) order is total and the runner-up is a plain
+        // maximum, so every merge order gives the same result)
         {
             v = -INFINITY;
             am = INT32_MAX;
             s = -INFINITY;
             if (lane < G) {
                 v = __uint_as_float((uint32_t)(s_words[lane * W] >> 32));
-                am = (int)(uint32_t)s_words[lane * W];
-                if (M) s = __uint_as_float((uint32_t)s_words[lane * W + 1]);
+                am = (int)((uint32_t)s_words[lane * W] - 1u);
+                if (M) s = __uint_as_float((uint32_t)(s_words[lane * W + 1] >> 32));
             }
-            if (M) {
-                top2_merge(v, am, s, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(am), dpp_f<kDppQuadXor1>(s));
-                top2_merge(v, am, s, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(am), dpp_f<kDppQuadXor2>(s));
-                top2_merge(v, am, s, dpp_f<kDppRowHalfMirror>(v), dpp_i<kDppRowHalfMirror>(am),
-                           dpp_f<kDppRowHalfMirror>(s));
-                s = readlane_f(s, 0);
-            } else {
-                argmax_merge(v, am, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(am));
-                argmax_merge(v, am, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(am));
-                argmax_merge(v, am, dpp_f<kDppRowHalfMirror>(v), dpp_i<kDppRowHalfMirror>(am));
-            }
-            v = readlane_f(v, 0);
-            am = readlane_i(am, 0);
+            if (M)
+                wave_top2(v, am, s);
+            else
+                wave_argmax(v, am);
         }
         __syncthreads();  // s_words is rewritten by the next position's gather
         // a token outside [0, V) never equals an argmax: it is a miss
-        if (i == kb || readlane_i(my_tok, i) != am) {
-            if (g == 0 && threadIdx.x == 0) {
-                n_accepted[b] = i;
-                next_token[b] = am;
-                if (M) top2_margin[b] = v - s;
-            }
-            return;
-        }
+        if (i == kb || readlane_i(my_tok, i) != am) break;
     }
+    if (g == 0 && threadIdx.x == 0) {
+        n_accepted[b] = i;
+        next_token[b] = am;
+        if (M) top2_margin[b] = v - s;
+    }
+    depart(departed + b, slots + (size_t)b * (K + 1) * (size_t)(G * W), (i + 1) * G * W, G, waited_out);
 }
 
 }  // namespace
 
-size_t greedy_workspace_bytes(int B, int K, int V) {
-    int G, Ls;
-    coop_slice_shape(B, V, G, Ls);
-    if (G < 2) return 0;
-    return (size_t)B * (size_t)(K + 1) * 2 * (size_t)G * sizeof(unsigned long long);
+// Slices of the split greedy verify: each 256-lane workgroup reads its slice
+// of a row with one batch of kSliceUnroll 16-byte loads per lane (one memory
+// round trip per position), so a row of V elements of s bytes takes
+// G = V*s / (256 * 16 * kSliceUnroll) slices (24 KB each), at most 64 (longer
+// rows get longer slices). Rows of at most 128 KB use one 1024-lane
+// workgroup per sequence instead: that is one round trip too, without an
+// exchange.
+void greedy_slice_shape(int V, bool bf16, int& G, int& Ls) {
+    const int64_t per = (int64_t)kSliceThreads * kSliceUnroll * (bf16 ? 8 : 4);
+    const int64_t row_bytes = (int64_t)V * (bf16 ? 2 : 4);
+    if (row_bytes <= 128 * 1024) {
+        G = 1;
+        Ls = V;
+        return;
+    }
+    int64_t ls = per;
+    if (((int64_t)V + ls - 1) / ls > kMaxGreedySlices) ls = ((int64_t)V + kMaxGreedySlices - 1) / kMaxGreedySlices;
+    ls = (ls + 63) / 64 * 64;
+    G = (int)(((int64_t)V + ls - 1) / ls);
+    Ls = (int)ls;
 }
+
+// B departure counters, then 2 words per slice and position of every sequence.
+size_t greedy_dtype_workspace_bytes(int B, int K, int V, bool bf16) {
+    int G, Ls;
+    greedy_slice_shape(V, bf16, G, Ls);
+    if (G < 2) return 0;
+    return ((size_t)B + (size_t)B * (size_t)(K + 1) * 2 * (size_t)G) * sizeof(unsigned long long);
+}
+
+// The larger of the two dtypes' needs (fp32 rows are split into more slices),
+// so that one size serves either.
+size_t greedy_workspace_bytes(int B, int K, int V) { return greedy_dtype_workspace_bytes(B, K, V, false); }
 
 hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, const int32_t* tokens,
                          const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const size_t need = greedy_workspace_bytes(B, K, V);
+    const size_t need = greedy_dtype_workspace_bytes(B, K, V, bf16);
     if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
         int G, Ls;
-        coop_slice_shape(B, V, G, Ls);
-        unsigned long long* slots = (unsigned long long*)workspace;
-        const int64_t words = (int64_t)B * (K + 1) * (top2_margin ? 2 : 1) * G;
-        hipError_t e = launch_fill_empty(slots, words, stream);
-        if (e != hipSuccess) return e;
+        greedy_slice_shape(V, bf16, G, Ls);
+        unsigned long long* departed = (unsigned long long*)workspace;  // zero between launches
+        unsigned long long* slots = departed + B;
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
         const int wl = get_wait_limit();
         if (top2_margin) {
             if (bf16)
                 hipLaunchKernelGGL((greedy_sliced_kernel<true, true>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
             else
                 hipLaunchKernelGGL((greedy_sliced_kernel<false, true>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
         } else {
             if (bf16)
                 hipLaunchKernelGGL((greedy_sliced_kernel<true, false>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
             else
                 hipLaunchKernelGGL((greedy_sliced_kernel<false, false>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
         }
         return hipGetLastError();
     }

@@ -14,7 +14,8 @@ hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, con
                          const int32_t* lens, int32_t* n_accepted, int32_t* next_token, float* top2_margin,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-// 0 when one workgroup per sequence is used regardless (short rows).
+// 0 when one workgroup per sequence is used regardless (short rows); the size
+// covers fp32 and bf16 rows alike.
 size_t greedy_workspace_bytes(int B, int K, int V);
 
 hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, const int32_t* tokens,

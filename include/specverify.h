@@ -22,7 +22,8 @@
  *  - Pointers are device memory owned by the caller. The library never
  *    allocates, frees or retains them; its only scratch memory, the exchange
  *    slots of sv_softmax_warp, sv_verify_greedy(_margin) and sv_accept_logits
- *    (their `workspace` arguments), is passed in by the caller too.
+ *    (their `workspace` arguments), is passed in by the caller too (the one
+ *    exception is sv_softmax_warp_noalloc's fixed array, below).
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
  *    stream) and return. Outputs are valid once the stream reaches them.
  *    Calls keep no state between them; concurrent calls on different streams
@@ -197,16 +198,21 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
  * workspace    device memory of at least
  *              sv_verify_greedy_workspace_bytes(B, K, V) bytes, 8-byte
  *              aligned, owned by the caller, not used by another call that
- *              may run at the same time; its contents need no preparation
- *              and are scratch afterwards. With it, each sequence's rows are
- *              split over up to 8 workgroups that exchange partial argmaxes
- *              (a long chain of matches is read by several compute units);
- *              NULL or 0 bytes selects one workgroup per sequence (fewer
- *              bytes than the query returns is SV_ERR_WORKSPACE). The
+ *              may run at the same time. Unlike the other workspaces it must
+ *              hold ZEROS before its first use (e.g. hipMemset to 0) and be
+ *              written by nothing but sv_verify_greedy and
+ *              sv_verify_greedy_margin: every call leaves it all zero again,
+ *              so no reset has to run before a launch. With it, each
+ *              sequence's rows are split over workgroups (one 32 KB slice of
+ *              each row per workgroup, up to 64) that exchange partial
+ *              argmaxes, so a long chain of matches is read by many compute
+ *              units; NULL or 0 bytes selects one workgroup per sequence
+ *              (fewer bytes than the query returns is SV_ERR_WORKSPACE). The
  *              results are identical either way.
  * Result: n_accepted[b] in [0, K_b], next_token[b] in [0, V); bit-exact.
  * Errors: SV_ERR_INVALID_ARG for null required pointers, B < 0, K < 0,
- * K > SV_MAX_K, V < 1 or V > INT32_MAX, a bad dtype, misaligned pointers.
+ * K > SV_MAX_K, V < 1 or V > INT32_MAX, a bad dtype, misaligned pointers;
+ * SV_ERR_WORKSPACE for an undersized workspace.
  */
 sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, int64_t V,
                            const int32_t* draft_tokens, const int32_t* draft_lens,
@@ -214,8 +220,9 @@ sv_status sv_verify_greedy(const void* target, int dtype, int32_t B, int32_t K, 
                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes the split path of sv_verify_greedy and
- * sv_verify_greedy_margin uses for these sizes (0 when one workgroup per
- * sequence is used regardless: V up to 32768, or invalid sizes). */
+ * sv_verify_greedy_margin uses for these sizes, for fp32 or bf16 rows alike
+ * (0 when one workgroup per sequence is used regardless: rows of at most
+ * 128 KB, i.e. V up to 32768, or invalid sizes). */
 size_t sv_verify_greedy_workspace_bytes(int32_t B, int32_t K, int64_t V);
 
 /*

@@ -246,12 +246,15 @@ def test_accept_logits_workspace_size(sv):
 
 
 def test_verify_greedy_workspace_size(sv):
-    # B * (K + 1) * 2 * G 8-byte slots (two words per slice and position); G as for the fused sampled verify
-    assert sv.sv_verify_greedy_workspace_bytes(512, 16, 256000) == 512 * 17 * 2 * 8 * 8
-    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 70000) == 64 * 5 * 2 * 3 * 8
-    assert sv.sv_verify_greedy_workspace_bytes(1024, 7, 152064) == 1024 * 8 * 2 * 4 * 8
-    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 32768) == 0     # short rows: one workgroup per sequence
-    assert sv.sv_verify_greedy_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
+    # B departure counters + B * (K + 1) * 2 * G 8-byte slots (two words per slice and position), with
+    # G = ceil(V / 8192) slices of 32 KB of fp32 (bf16 rows use half as many, in the same size)
+    w = lambda B, K, G: (B + B * (K + 1) * 2 * G) * 8
+    assert sv.sv_verify_greedy_workspace_bytes(512, 16, 256000) == w(512, 16, 32)
+    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 70000) == w(64, 4, 9)
+    assert sv.sv_verify_greedy_workspace_bytes(1024, 7, 152064) == w(1024, 7, 19)
+    assert sv.sv_verify_greedy_workspace_bytes(4096, 4, 256000) == w(4096, 4, 32)
+    assert sv.sv_verify_greedy_workspace_bytes(1, 0, 64 * 8192 + 1) == w(1, 0, 64)  # at most 64 slices
+    assert sv.sv_verify_greedy_workspace_bytes(64, 4, 32768) == 0     # rows of 128 KB: one workgroup per sequence
     assert sv.sv_verify_greedy_workspace_bytes(0, 4, 256000) == 0
     assert sv.sv_verify_greedy_workspace_bytes(8, 65, 256000) == 0
 

@@ -90,8 +90,8 @@ def test_paths_on_workloads(sv, case):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_paths_ties_across_slices(sv, dtype, offset):
-    B, K, V = 10, 4, 100_003   # 4 slices, the last one short
-    G_ls = 25_600              # the slice length the split path uses for these sizes (Ls rounds up to 1024)
+    B, K, V = 10, 4, 100_003   # 7 (bf16) or 13 (fp32) slices, the last one short
+    G_ls = 16_384 if dtype == torch.bfloat16 else 8_192  # the split path's slice: 32 KB of the row
     g = torch.Generator().manual_seed(11)
     tgt = torch.randn((B, K + 1, V), generator=g).to(dtype)
     for b in range(B):
@@ -131,3 +131,36 @@ def test_paths_full_size(sv):
     toks = b.tokens.clone()
     toks[::4] = chain[::4]   # a quarter of the sequences match all the way
     check(sv, b.target, toks.contiguous(), b.lens, name + "/full")
+
+
+@pytest.mark.parametrize("polls", [DEFAULT_POLLS, 0])
+def test_workspace_is_left_zero(sv, polls):
+    """The split path needs no reset before a launch: a workspace that holds
+    zeros is all zero again after every call (the last workgroup of each
+    sequence clears the words the sequence used), also when every workgroup
+    gives up waiting and computes the other slices itself. Several calls in a
+    row on one workspace, with and without the margin, stay equal to the
+    oracle."""
+    name = "logits-bf16-b512-k16-v256000-zipf"
+    b = synth.generate(name, "cuda", B=24)
+    chain = b.target.argmax(-1).to(torch.int32)[:, :b.K]
+    toks = b.tokens.clone()
+    toks[::3] = chain[::3]
+    toks = toks.contiguous()
+    n_o, nx_o = oracle.verify_greedy(host(b.target), host(toks), None)
+    ws = torch.zeros(sv.sv_verify_greedy_workspace_bytes(b.B, b.K, b.V), dtype=torch.uint8, device="cuda")
+    sv.sv_set_wait_limit(polls)
+    try:
+        for rep in range(3):
+            for margin in (False, True):
+                if margin:
+                    n, nx, _ = sv.sv_verify_greedy_margin(b.target, toks, None, workspace=ws)
+                else:
+                    n, nx = sv.sv_verify_greedy(b.target, toks, None, workspace=ws)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(host(n).numpy(), n_o)
+                np.testing.assert_array_equal(host(nx).numpy(), nx_o)
+                assert int(ws.count_nonzero()) == 0, f"rep {rep} margin {margin}: workspace not left zero"
+    finally:
+        sv.sv_set_wait_limit(DEFAULT_POLLS)
+    print(f"[workspace left zero] polls={polls}: 6 calls, mean n {n_o.mean():.2f}", flush=True)
