@@ -25,7 +25,7 @@ import numpy as np
 __all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", "accept_logits", "icdf", "mass",
            "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
            "FLAG_NO_MASS", "FLAG_TOPP", "warp_row_filtered", "softmax_warp_filtered", "top2_margin", "gate_update",
-           "gate_choose", "GATE_DEFAULTS", "library_path",
+           "gate_choose", "GATE_DEFAULTS", "penalize_row", "apply_penalties", "library_path",
            "load_library"]
 
 F32, BF16, F64 = 0, 1, 2
@@ -58,6 +58,9 @@ def load_library(path: str):
     lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
     lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, vp, vp,
                                      vp]
+    f32 = ctypes.c_float
+    lib.or_penalize_row.argtypes = [vp, ctypes.c_int, i64, vp, i64, f32, f32, f32, vp]
+    lib.or_apply_penalties.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, i64, vp, i64, vp, vp, vp, vp]
     lib.or_top2_margin.argtypes = [vp, ctypes.c_int, i64]
     lib.or_top2_margin.restype = f64
     lib.or_gate_update.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, f64]
@@ -164,6 +167,45 @@ def softmax_warp_filtered(logits, lens=None, extra_rows: int = 0, T: float = 1.0
     (lib or _lib()).or_softmax_warp_filtered(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), float(T), _ptr(tk),
                                              _ptr(tp), float(window), _ptr(out), _ptr(flags))
     return out, flags
+
+
+def penalize_row(z, history, theta: float = 1.0, presence: float = 0.0, frequency: float = 0.0, lib=None):
+    """Repetition, presence and frequency penalties of one logit row given its token history -> fp32 row."""
+    a, dt = _array(z)
+    h = _i32(history)
+    h = np.zeros(0, np.int32) if h is None else h.ravel()
+    out = np.empty(a.shape[-1], dtype=np.float32)
+    (lib or _lib()).or_penalize_row(_ptr(a), dt, a.shape[-1], _ptr(h), h.size, float(theta), float(presence),
+                                    float(frequency), _ptr(out))
+    return out
+
+
+def _f32(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def apply_penalties(logits, lens=None, extra_rows: int = 0, seq=None, seq_len=None, tokens=None, theta=None,
+                    presence=None, frequency=None, lib=None):
+    """Penalties of the live rows of logits [B, R, V]: row r of sequence b takes the history
+    seq[b, :seq_len[b]] + tokens[b, :r]. Per-sequence theta / presence / frequency [B] (None: off).
+    Returns fp32 [B, R, V] with NaN in rows that are not live."""
+    a, dt = _array(logits)
+    B, R, V = a.shape
+    out = np.full((B, R, V), np.nan, dtype=np.float32)
+    ln = _i32(lens)
+    sq = _i32(seq)
+    sl = _i32(seq_len)
+    tk = _i32(tokens)
+    cap = 0 if sq is None else sq.shape[1]
+    K = 0 if tk is None else tk.shape[1]
+    (lib or _lib()).or_apply_penalties(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), _ptr(sq), _ptr(sl), cap,
+                                       _ptr(tk), K, _ptr(_f32(theta)), _ptr(_f32(presence)), _ptr(_f32(frequency)),
+                                       _ptr(out))
+    return out
 
 
 def top2_margin(row, lib=None) -> float:

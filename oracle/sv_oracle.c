@@ -306,6 +306,73 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
     }
 }
 
+/* ---- sampler penalties: the pipeline's first stage [BLOG s.38, s.39] ----
+ * The sampler turns raw logits into the effective distribution as
+ * penalties -> temperature -> top-k -> top-p -> normalise; the penalties are
+ * stateful (they depend on the tokens so far), and under speculation their
+ * state must follow the speculative branch: the history of verify row r is
+ * the committed sequence followed by the draft tokens before position r.
+ * Readings (the pages name the stage, not its formulas):
+ *  R24 repetition penalty theta, as the transformers library applies it: an
+ *      id present in the history has its logit z replaced by z * theta when
+ *      z < 0, else by z / theta (theta = 1: off).
+ *  R25 presence and frequency penalties (the usual serving-API form): an id
+ *      with c > 0 occurrences in the history loses frequency * c + presence.
+ *  R26 repetition first, then presence and frequency; ids outside [0, V) in
+ *      the history are ignored.
+ *  R27 the stage is defined in fp32, one rounding per operation, so that
+ *      every later decision (top-k keys, argmax) sees identical values:
+ *        z1 = z < 0 ? z * theta : z / theta       (c > 0)
+ *        d  = fmaf(frequency, c, presence)
+ *        z' = z1 - d                              (c > 0; z' = z otherwise) */
+void or_penalize_row(const void* z, int dtype, int64_t V, const int32_t* hist, int64_t nh, float theta,
+                     float presence, float frequency, float* out) {
+    int32_t* count = (int32_t*)calloc((size_t)V, sizeof(int32_t));
+    for (int64_t j = 0; j < nh; ++j)
+        if (hist[j] >= 0 && hist[j] < V) count[hist[j]] += 1;
+    for (int64_t x = 0; x < V; ++x) {
+        float v = (float)elem(z, dtype, x); /* exact: the input is fp32 or bf16 */
+        if (count[x] > 0) {
+            float z1 = v < 0.0f ? v * theta : v / theta;
+            float d = fmaf(frequency, (float)count[x], presence);
+            v = z1 - d;
+        }
+        out[x] = v;
+    }
+    free(count);
+}
+
+/* Live rows r < clamp(lens[b], 0, R - extra) + extra of logits [B, R, V]:
+ * history = seq[b, :clamp(seq_len[b], 0, cap)] (none when seq is NULL), then
+ * draft tokens tokens[b, 0 .. r-1] (none when tokens is NULL); per-sequence
+ * theta / presence / frequency (NULL: 1, 0, 0). Other rows are untouched. */
+void or_apply_penalties(const void* logits, int dtype, int64_t B, int64_t R, int64_t V, const int32_t* lens,
+                        int32_t extra_rows, const int32_t* seq, const int32_t* seq_len, int64_t cap,
+                        const int32_t* tokens, int64_t K, const float* theta, const float* presence,
+                        const float* frequency, float* out) {
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t live = (int64_t)clamp_len(lens, b, R - extra_rows) + extra_rows;
+            if (r >= (live < R ? live : R)) continue;
+            int64_t n0 = 0;
+            if (seq) {
+                n0 = seq_len[b];
+                if (n0 < 0) n0 = 0;
+                if (n0 > cap) n0 = cap;
+            }
+            int64_t np = tokens ? r : 0;
+            int32_t* hist = (int32_t*)malloc((size_t)(n0 + np + 1) * sizeof(int32_t));
+            for (int64_t j = 0; j < n0; ++j) hist[j] = seq[b * cap + j];
+            for (int64_t j = 0; j < np; ++j) hist[n0 + j] = tokens[b * K + j];
+            or_penalize_row(row_ptr(logits, dtype, b * R + r, V), dtype, V, hist, n0 + np, theta ? theta[b] : 1.0f,
+                            presence ? presence[b] : 0.0f, frequency ? frequency[b] : 0.0f,
+                            out + (size_t)(b * R + r) * V);
+            free(hist);
+        }
+    }
+}
+
 /* ---- filtered warp: temperature, top-k, top-p, normalise [BLOG §38] ---
  * The sampler pipeline turns logits into the effective distribution in the
  * order: temperature, top-k, top-p, renormalisation (penalties and other

@@ -53,6 +53,13 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
                       const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
                       double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags);
 
+void or_penalize_row(const void* z, int dtype, int64_t V, const int32_t* hist, int64_t nh, float theta,
+                     float presence, float frequency, float* out);
+void or_apply_penalties(const void* logits, int dtype, int64_t B, int64_t R, int64_t V, const int32_t* lens,
+                        int32_t extra_rows, const int32_t* seq, const int32_t* seq_len, int64_t cap,
+                        const int32_t* tokens, int64_t K, const float* theta, const float* presence,
+                        const float* frequency, float* out);
+
 double or_top2_margin(const void* row, int dtype, int64_t V);
 void or_gate_update(double* hits, double* trials, int64_t B, int64_t NB, int64_t K, const int32_t* lens,
                     const int32_t* n_accepted, const int32_t* buckets, double decay);

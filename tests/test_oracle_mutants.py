@@ -197,8 +197,22 @@ def check_gate(lib):
     assert oracle.top2_margin(np.array([1.0, 3.0, 2.5], np.float32), lib=lib) == 0.5
 
 
+def check_penalties(lib):
+    z = np.array([2.0, -1.0, 0.0, 3.0, -0.5, 1.5], np.float32)
+    np.testing.assert_array_equal(oracle.penalize_row(z, [0, 0, 1, 4, 4, 4, 7, -1, 6], 2.0, 0.5, 0.25, lib=lib),
+                                  np.array([0.0, -2.75, 0.0, 3.0, -2.25, 1.5], np.float32))
+    # the speculative branch: the prefix of draft tokens before the row, from the committed length on
+    zz = np.tile(np.array([1.0, -2.0, 4.0, 0.5], np.float32), (1, 3, 1))     # [1, K + 1 = 3, V = 4]
+    seq = np.array([[3, 0, 0, 0]], np.int32)                                # seq_len 1: only id 3 counts
+    t = np.array([[2, 2]], np.int32)
+    out = oracle.apply_penalties(zz, None, 1, seq, np.array([1], np.int32), t, [2.0], [0.0], [1.0], lib=lib)
+    np.testing.assert_array_equal(out[0, 0], [1.0, -2.0, 4.0, 0.25 - 1.0])    # history (3)
+    np.testing.assert_array_equal(out[0, 1], [1.0, -2.0, 2.0 - 1.0, -0.75])   # history (3, 2)
+    np.testing.assert_array_equal(out[0, 2], [1.0, -2.0, 2.0 - 2.0, -0.75])   # history (3, 2, 2)
+
+
 ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits,
-              check_filtered, check_gate]
+              check_filtered, check_gate, check_penalties]
 
 # (what goes wrong, exact source text, planted replacement)
 MUTANTS = [
@@ -248,6 +262,13 @@ MUTANTS = [
     ("gate verify cost without the per-token slope", "verify_slope_ms * (double)n);", "verify_slope_ms);"),
     ("top-2 margin drops every copy of a tied maximum", "if (x != am && elem(row, dtype, x) > v2)",
      "if (elem(row, dtype, x) < v1 && elem(row, dtype, x) > v2)"),
+    ("penalties ignore the draft prefix", "int64_t np = tokens ? r : 0;", "int64_t np = 0;"),
+    ("penalty prefix one token short", "int64_t np = tokens ? r : 0;", "int64_t np = tokens && r > 0 ? r - 1 : 0;"),
+    ("repetition penalty sign rule inverted", "float z1 = v < 0.0f ? v * theta : v / theta;",
+     "float z1 = v < 0.0f ? v / theta : v * theta;"),
+    ("frequency penalty ignores the count", "float d = fmaf(frequency, (float)count[x], presence);",
+     "float d = frequency + presence;"),
+    ("penalty history ignores seq_len", "n0 = seq_len[b];", "n0 = cap;"),
 ]
 
 
