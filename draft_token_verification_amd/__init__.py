@@ -24,11 +24,19 @@ __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_softmax_war
            "SV_NOALLOC_SCRATCH_BYTES", "sv_set_wait_limit", "sv_verify_greedy",
            "sv_verify_greedy_workspace_bytes", "sv_accept",
            "sv_accept_logits", "sv_accept_logits_workspace_bytes", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
-           "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder",
+           "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder", "sv_apply_penalties",
+           "sv_apply_penalties_workspace_bytes",
            "verify_greedy", "accept", "library_path",
            "SV_F32", "SV_BF16", "SV_MAX_K", "SpecVerifyError", "abi_version"]
 
 SV_F32, SV_BF16 = 0, 1
+
+
+class Penalties(ctypes.Structure):
+    """sv_penalties of include/specverify.h (device pointers, host struct)."""
+    _fields_ = [("seq", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("cap", ctypes.c_int32),
+                ("draft_tokens", ctypes.c_void_p), ("K", ctypes.c_int32), ("repetition", ctypes.c_void_p),
+                ("presence", ctypes.c_void_p), ("frequency", ctypes.c_void_p)]
 
 
 class GateParams(ctypes.Structure):
@@ -75,6 +83,11 @@ def _load():
     lib.sv_gate_choose.restype = c_int
     lib.sv_commit.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, i32, vp]
     lib.sv_commit.restype = c_int
+    lib.sv_apply_penalties.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.POINTER(Penalties), vp, vp,
+                                       ctypes.c_size_t, vp]
+    lib.sv_apply_penalties.restype = c_int
+    lib.sv_apply_penalties_workspace_bytes.argtypes = [i32, i32]
+    lib.sv_apply_penalties_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_softmax_warp_filtered.argtypes = [vp, c_int, i32, i32, i64, vp, i32, ctypes.c_float, vp, vp, vp, vp]
     lib.sv_softmax_warp_filtered.restype = c_int
     lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
@@ -399,6 +412,58 @@ def _per_sequence(v, B: int, dtype: torch.dtype, dev: torch.device, name: str) -
             raise ValueError(f"{name} must be [B] = {(B,)}")
         return v.to(device=dev, dtype=dtype).contiguous()
     return torch.full((B,), v, dtype=dtype, device=dev)
+
+
+def sv_apply_penalties_workspace_bytes(B: int, cap: int) -> int:
+    return int(_lib.sv_apply_penalties_workspace_bytes(B, cap))
+
+
+def sv_apply_penalties(logits: torch.Tensor, draft_lens: Optional[torch.Tensor] = None, extra_rows: int = 0,
+                       seq: Optional[torch.Tensor] = None, seq_len: Optional[torch.Tensor] = None,
+                       draft_tokens: Optional[torch.Tensor] = None, repetition=None, presence=None, frequency=None,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Repetition / presence / frequency penalties of the live rows of logits [B, R, V] -> fp32 [B, R, V].
+
+    Row r of sequence b is penalised with the history seq[b, :seq_len[b]] + draft_tokens[b, :r]
+    (seq [B, cap] and draft_tokens [B, K] int32 device tensors, either may be None). The
+    per-sequence parameters are None (off), a number, or a [B] tensor. Rows that are not live
+    are left as they were in ``out``.
+    """
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    B, R, V = logits.shape
+    dev = logits.device
+    lens = _int32(draft_lens, "draft_lens", dev)
+    if lens is not None and tuple(lens.shape) != (B,):
+        raise ValueError("draft_lens must be [B]")
+    sq = _int32(seq, "seq", dev)
+    sl = _int32(seq_len, "seq_len", dev)
+    if sq is not None:
+        sq = sq.contiguous()
+        if sq.dim() != 2 or sq.shape[0] != B:
+            raise ValueError("seq must be [B, cap]")
+        if sl is None or tuple(sl.shape) != (B,):
+            raise ValueError("seq_len must be [B] with seq")
+    tk = _int32(draft_tokens, "draft_tokens", dev)
+    if tk is not None:
+        tk = tk.contiguous()
+        if tk.dim() != 2 or tk.shape[0] != B:
+            raise ValueError("draft_tokens must be [B, K]")
+    params = [_per_sequence(v, B, torch.float32, dev, n) for v, n in
+              ((repetition, "repetition"), (presence, "presence"), (frequency, "frequency"))]
+    o = _out((B, R, V), dev, out, torch.float32, "out")
+    pen = Penalties(None if sq is None else sq.data_ptr(), None if sl is None else sl.data_ptr(),
+                    0 if sq is None else sq.shape[1], None if tk is None else tk.data_ptr(),
+                    0 if tk is None else tk.shape[1], *[None if t is None else t.data_ptr() for t in params])
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = sv_apply_penalties_workspace_bytes(B, sq.shape[1]) if (sq is not None and B > 0) else 0
+        ws, ws_bytes = _workspace_arg(workspace, need, dev, stream.value, "logits", "penalty")
+        st = _lib.sv_apply_penalties(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens),
+                                     int(extra_rows), ctypes.byref(pen), _ptr(o), ws, ws_bytes, stream)
+    _check("sv_apply_penalties", st)
+    return o
 
 
 def sv_softmax_warp_filtered(logits: torch.Tensor, temperature: float = 1.0, draft_lens: Optional[torch.Tensor] = None,

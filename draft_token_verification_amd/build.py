@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libspecverify.so")
 RESOURCES = os.path.join(HERE, "libspecverify.resources.json")
-SOURCES = ["api.hip", "greedy.hip", "accept.hip", "warp.hip", "filter.hip", "gate.hip", "commit.hip"]
+SOURCES = ["api.hip", "greedy.hip", "accept.hip", "warp.hip", "filter.hip", "penalty.hip", "gate.hip", "commit.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -103,6 +103,7 @@ sv_status greedy_common(const char* fn, const void* target, int dtype, int32_t B
 }  // namespace
 
 static_assert(sizeof(sv_gate_params) == 48, "sv_gate_params layout: five doubles, an int32 and a float");
+static_assert(sizeof(sv_penalties) == 64, "sv_penalties layout: pointers and two int32 strides");
 
 extern "C" {
 
@@ -211,6 +212,47 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_warp_filtered(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows,
                                                  temperature, top_k, top_p, probs, (hipStream_t)stream));
+}
+
+size_t sv_apply_penalties_workspace_bytes(int32_t B, int32_t cap) { return sv::penalty_workspace_bytes(B, cap); }
+
+sv_status sv_apply_penalties(const void* logits, int dtype, int32_t B, int32_t R, int64_t V, const int32_t* draft_lens,
+                             int32_t extra_rows, const sv_penalties* pen, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const char* fn = "sv_apply_penalties";
+    sv_status st;
+    if ((st = check_dtype(dtype)) != SV_OK) return st;
+    if (B < 0) return fail(SV_ERR_INVALID_ARG, "%s: B = %d < 0", fn, B);
+    if (R < 1) return fail(SV_ERR_INVALID_ARG, "%s: R = %d < 1", fn, R);
+    if (extra_rows < 0 || extra_rows > R)
+        return fail(SV_ERR_INVALID_ARG, "%s: extra_rows = %d not in [0, R]", fn, extra_rows);
+    if (V < 1 || V > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: V = %lld not in [1, 2^31-1]", fn, (long long)V);
+    if ((int64_t)B * R > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*R exceeds 2^31-1 rows", fn);
+    if (!pen) return fail(SV_ERR_INVALID_ARG, "%s: null pen", fn);
+    const sv_penalties& p = *pen;
+    if (p.seq && !p.seq_len) return fail(SV_ERR_INVALID_ARG, "%s: seq without seq_len", fn);
+    if (p.seq && p.cap < 1) return fail(SV_ERR_INVALID_ARG, "%s: cap = %d < 1", fn, p.cap);
+    if (p.seq && (int64_t)B * p.cap > INT32_MAX) return fail(SV_ERR_INVALID_ARG, "%s: B*cap exceeds 2^31-1", fn);
+    if (p.draft_tokens && (p.K < R - 1 || p.K > SV_MAX_K))
+        return fail(SV_ERR_INVALID_ARG, "%s: K = %d must be in [R - 1, %d] with draft_tokens", fn, p.K, SV_MAX_K);
+    if (B == 0) return ok();
+    if (!logits || !out) return fail(SV_ERR_INVALID_ARG, "%s: null logits or out", fn);
+    if (!aligned(logits, dtype_bytes(dtype)) || !aligned(out, 4) || (draft_lens && !aligned(draft_lens, 4)) ||
+        (p.seq && !aligned(p.seq, 4)) || (p.seq_len && !aligned(p.seq_len, 4)) ||
+        (p.draft_tokens && !aligned(p.draft_tokens, 4)) || (p.repetition && !aligned(p.repetition, 4)) ||
+        (p.presence && !aligned(p.presence, 4)) || (p.frequency && !aligned(p.frequency, 4)))
+        return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (p.seq) {
+        const size_t need = sv::penalty_workspace_bytes(B, p.cap);
+        if (!workspace || workspace_bytes < need)
+            return fail(SV_ERR_WORKSPACE, "%s: the history tables need %zu bytes of workspace, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 4)) return fail(SV_ERR_INVALID_ARG, "%s: workspace not 4-byte aligned", fn);
+    }
+    if ((st = check_device()) != SV_OK) return st;
+    return launched(fn, sv::launch_penalties(logits, dtype == SV_BF16, B, R, (int)V, draft_lens, extra_rows, p.seq,
+                                             p.seq_len, p.cap, p.draft_tokens, p.K, p.repetition, p.presence,
+                                             p.frequency, out, workspace, (hipStream_t)stream));
 }
 
 size_t sv_verify_greedy_workspace_bytes(int32_t B, int32_t K, int64_t V) {

@@ -49,6 +49,15 @@ hipError_t launch_warp_filtered(const void* logits, bool bf16, int B, int R, int
                                 int extra_rows, float temperature, const int32_t* top_k, const float* top_p,
                                 float* probs, hipStream_t stream);
 
+// The penalty stage: workspace bytes for B sequences with histories of up to
+// `cap` tokens (hash tables of the committed histories), and the launcher
+// (seq may be null: no committed history; tokens may be null: no draft prefix).
+size_t penalty_workspace_bytes(int B, int cap);
+hipError_t launch_penalties(const void* logits, bool bf16, int B, int R, int V, const int32_t* lens, int extra_rows,
+                            const int32_t* seq, const int32_t* seq_len, int cap, const int32_t* tokens, int K,
+                            const float* theta, const float* presence, const float* frequency, float* out,
+                            void* workspace, hipStream_t stream);
+
 // Draft-length gate parameters as the kernels take them (by value).
 struct GateCosts {
     double draft_ms, verify_base_ms, verify_slope_ms, plain_ms, margin;

@@ -183,6 +183,66 @@ sv_status sv_softmax_warp_filtered(const void* logits, int dtype, int32_t B, int
                                    const int32_t* top_k, const float* top_p, float* probs, void* stream);
 
 /*
+ * sv_apply_penalties -- the sampler pipeline's first stage: repetition,
+ * presence and frequency penalties of the live logit rows, each row with its
+ * own token history (llmstudio blog "Как работает speculative decoding и MTP
+ * при инференсе LLM", section 38: raw logits -> penalties -> temperature ->
+ * top-k -> top-p -> normalise; section 39: a stateful sampler's state must
+ * follow the speculative branch).
+ *
+ * The history of row r of sequence b is seq[b, :clamp(seq_len[b], 0, cap)]
+ * followed by draft_tokens[b, 0 .. r-1]; ids outside [0, V) in it are
+ * ignored. An id with c > 0 occurrences gets, in fp32 with one rounding per
+ * operation,
+ *     z1 = z < 0 ? z * theta : z / theta,   z' = z1 - fmaf(frequency, c, presence)
+ * (the repetition penalty as the transformers library applies it, then the
+ * usual presence and frequency penalties); every other id keeps z. The rest
+ * of the pipeline runs on the output: sv_softmax_warp_filtered (or
+ * sv_softmax_warp) for the sampled verify, sv_verify_greedy for greedy.
+ *
+ * logits       [B, R, V] of `dtype`, element-aligned; rows and live-row rule
+ *              as sv_softmax_warp (draft_lens, extra_rows).
+ * pen          host pointer to the parameters below (read during the call):
+ *   seq          [B, cap] int32 token buffers (sv_commit's), or NULL: no
+ *                committed history;
+ *   seq_len      [B] int32, required with seq;
+ *   cap          row stride of seq, >= 1 with seq;
+ *   draft_tokens [B, K] int32, or NULL: no draft prefix; with it K >= R - 1;
+ *   K            row stride of draft_tokens;
+ *   repetition, presence, frequency   [B] fp32 per-sequence parameters, or
+ *                NULL (1, 0, 0: off). theta must be finite and > 0 and the
+ *                others finite; other values are outside the contract.
+ * out          [B, R, V] fp32, 4-byte aligned, not overlapping logits; live
+ *              rows are written, the others left untouched.
+ * workspace    with seq: at least sv_apply_penalties_workspace_bytes(B, cap)
+ *              bytes, 4-byte aligned, contents irrelevant (the call builds
+ *              its tables in it); not needed without seq.
+ * Result: bitwise the fp32 values above.
+ * Errors: SV_ERR_INVALID_ARG for null logits/out/pen, bad sizes (as
+ * sv_softmax_warp), seq without seq_len, cap < 1 with seq, K < R - 1 with
+ * draft_tokens, misaligned pointers; SV_ERR_WORKSPACE when seq is given and
+ * the workspace is missing or too small.
+ */
+typedef struct {
+    const int32_t* seq;
+    const int32_t* seq_len;
+    int32_t cap;
+    const int32_t* draft_tokens;
+    int32_t K;
+    const float* repetition;
+    const float* presence;
+    const float* frequency;
+} sv_penalties;
+
+sv_status sv_apply_penalties(const void* logits, int dtype, int32_t B, int32_t R, int64_t V,
+                             const int32_t* draft_lens, int32_t extra_rows, const sv_penalties* pen, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sv_apply_penalties needs for B sequences with token buffers
+ * of cap tokens (0 for invalid sizes). */
+size_t sv_apply_penalties_workspace_bytes(int32_t B, int32_t cap);
+
+/*
  * sv_verify_greedy -- temperature-0 verification.
  *
  * Accept draft token t_i while it equals argmax(target row i); at the first

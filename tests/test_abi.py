@@ -31,6 +31,7 @@ def sv():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_accept_logits_workspace_bytes",
+                                    "sv_apply_penalties", "sv_apply_penalties_workspace_bytes",
                                     "sv_commit", "sv_gate_choose",
                                     "sv_gate_update",
                                     "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
@@ -302,3 +303,25 @@ def test_noalloc_warp_host_checks(sv):
     assert lib.sv_softmax_warp_noalloc(None, 1, 2, 3, 100, None, 1, 1.0, FAKE, None) == 1
     assert lib.sv_softmax_warp_noalloc(ODD, 0, 2, 3, 100, None, 1, 1.0, FAKE, None) == 1
     assert lib.sv_softmax_warp_noalloc(None, 1, 0, 3, 100, None, 1, 1.0, None, None) == 0
+
+
+def test_apply_penalties_host_checks(sv):
+    """Argument checks of sv_apply_penalties, before any device is looked for."""
+    lib = sv._lib
+    P = sv.Penalties
+    seq = ctypes.c_void_p(0x3000)
+    ok = P(seq, seq, 100, None, 0, None, None, None)
+    need = sv.sv_apply_penalties_workspace_bytes(4, 100)
+    assert need == 4 * (4 * 256 + 4) * 4  # tables of 256 slots (a power of two >= 2 * cap): keys, counts, pairs
+    assert sv.sv_apply_penalties_workspace_bytes(4, 0) == 0
+    call = lambda pen, ws=ALIGNED, nb=need, R=3, extra=1, B=4: lib.sv_apply_penalties(
+        FAKE, 0, B, R, 1000, None, extra, None if pen is None else ctypes.byref(pen), FAKE, ws, nb, None)
+    assert call(None) == 1 and "null pen" in lib.sv_last_error().decode()
+    assert call(P(seq, None, 100, None, 0, None, None, None)) == 1 and "seq_len" in lib.sv_last_error().decode()
+    assert call(P(seq, seq, 0, None, 0, None, None, None)) == 1 and "cap" in lib.sv_last_error().decode()
+    assert call(P(None, None, 0, seq, 1, None, None, None)) == 1 and "K = 1" in lib.sv_last_error().decode()
+    assert call(ok, None, 0) == 4 and "workspace" in lib.sv_last_error().decode()
+    assert call(ok, ALIGNED, need - 4) == 4
+    assert call(P(ODD, seq, 100, None, 0, None, None, None)) == 1 and "misaligned" in lib.sv_last_error().decode()
+    assert call(ok, R=0) == 1
+    assert call(ok, B=0) == 0  # an empty call

@@ -24,7 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 KERNELS = ["accept_kernel", "accept_logits_kernel", "accept_logits_sliced_kernel", "commit_kernel", "fill_empty",
            "fill_slots", "gate_choose_kernel", "gate_update_kernel", "greedy_kernel", "greedy_sliced_kernel",
            "warp_coop_kernel",
-           "warp_filter_kernel", "warp_rows_kernel"]
+           "warp_filter_kernel", "warp_rows_kernel", "penalty_table_kernel", "penalty_rows_kernel"]
 
 
 @pytest.fixture(scope="module")
