@@ -20,13 +20,30 @@ may be None); in sampling mode both are fp32 probabilities, warped alike.
 
 ``generate`` returns the prompt followed by the generated tokens: a 1-D int64
 tensor for a 1-D prompt, else ``(seq, seq_len)`` int32 device tensors.
+
+With ``sampler`` (a dict: temperature, top_k, top_p, repetition, presence,
+frequency; each optional) the callbacks return raw logits instead and the
+decoder applies the sampler pipeline of the llmstudio blog (section 38:
+penalties -> temperature -> top-k -> top-p -> normalise) to the target and
+draft rows alike, with the penalties' history following the speculative
+branch (section 39: the committed tokens, then the draft tokens before each
+position). The draft loop is then the decoder's own, so that every draft token
+is drawn from the same pipeline's draft distribution:
+    draft_step(seq [B, cap], seq_len [B], drafted [B, i]) -> logits [B, V]
+        (the draft model's logits for the next position after `drafted`)
+    target_step(seq, seq_len, proposed [B, k]) -> logits [B, k + 1, V]
+Greedy mode takes the argmax of the penalised rows (temperature and the
+filters do not move it); sampling mode warps and filters them and verifies
+with sv_accept. The batched form only.
 """
 from typing import Callable, Optional
 
 import torch
 
-from . import (GATE_DEFAULTS, sv_accept, sv_commit, sv_gate_choose, sv_gate_update, sv_verify_greedy,
-               sv_verify_greedy_margin)
+from . import (GATE_DEFAULTS, sv_accept, sv_apply_penalties, sv_commit, sv_gate_choose, sv_gate_update,
+               sv_softmax_warp, sv_softmax_warp_filtered, sv_verify_greedy, sv_verify_greedy_margin)
+
+SAMPLER_KEYS = ("temperature", "top_k", "top_p", "repetition", "presence", "frequency")
 
 
 class SpeculativeDecoder:
@@ -44,13 +61,22 @@ class SpeculativeDecoder:
                (a positive margin_threshold also skips drafting after an
                uncertain committed token, greedy mode only).
     eos        stop a sequence right after it commits this token.
+    sampler    callbacks return logits and the decoder applies the sampler
+               pipeline (keys of SAMPLER_KEYS; see the module notes).
     """
 
     def __init__(self, draft_step: Callable, target_step: Callable, k: int = 4, greedy: bool = True,
                  generator: Optional[torch.Generator] = None, gate: bool = False, gate_params: Optional[dict] = None,
-                 decay: float = 0.9, eos: Optional[int] = None):
+                 decay: float = 0.9, eos: Optional[int] = None, sampler: Optional[dict] = None):
         if not 1 <= int(k) <= 64:
             raise ValueError("k must be in [1, 64]")
+        if sampler is not None:
+            unknown = set(sampler) - set(SAMPLER_KEYS)
+            if unknown:
+                raise ValueError(f"unknown sampler keys {sorted(unknown)}")
+            if not greedy and float(sampler.get("temperature", 1.0)) <= 0.0:
+                raise ValueError("sampling needs a positive temperature (greedy=True is temperature 0)")
+        self.sampler = None if sampler is None else dict(sampler)
         self.draft_step = draft_step
         self.target_step = target_step
         self.k = int(k)
@@ -90,9 +116,23 @@ class SpeculativeDecoder:
         self.rounds = 0
         if max_new <= 0:
             return self._result(single, seq, seq_len)
+        if self.sampler is not None:
+            if single:
+                raise ValueError("the sampler pipeline takes the batched callbacks")
+            seq_draft = torch.zeros((B, cap + K), dtype=torch.int32, device=dev)
         # every round commits at least one token to each live sequence
         for _ in range(int(max_new)):
             lens_now = dlens * (1 - done)  # finished sequences verify nothing
+            if self.sampler is not None:
+                n, nx, tok = self._round_with_sampler(seq, seq_len, seq_draft, lens_now, B, dev)
+                sv_commit(seq, seq_len, done, tok, n, nx, limit, self.eos)
+                if self.gate:
+                    sv_gate_update(hits, trials, K, lens_now, n, decay=self.decay)
+                    dlens = sv_gate_choose(hits, trials, K, **self.gate_params)
+                self.rounds += 1
+                if bool(done.all()):
+                    break
+                continue
             if single:
                 n0 = int(seq_len[0])
                 tok, q = self.draft_step(seq[0, :n0], K)
@@ -119,6 +159,52 @@ class SpeculativeDecoder:
             if bool(done.all()):
                 break
         return self._result(single, seq, seq_len)
+
+    def _pipeline(self, logits, lens, extra_rows, seq, seq_len, prefix):
+        """(penalised fp32 logits, probabilities or None in greedy mode) of the live rows."""
+        sm = self.sampler
+        pen = any(sm.get(x) is not None for x in ("repetition", "presence", "frequency"))
+        z = (sv_apply_penalties(logits, lens, extra_rows, seq, seq_len, prefix, sm.get("repetition"),
+                                sm.get("presence"), sm.get("frequency")) if pen else logits)
+        if self.greedy:
+            return z, None
+        T = float(sm.get("temperature", 1.0))
+        if sm.get("top_k") is None and sm.get("top_p") is None:
+            return z, sv_softmax_warp(z, T, lens, extra_rows)
+        return z, sv_softmax_warp_filtered(z, T, lens, extra_rows, sm.get("top_k"), sm.get("top_p"))
+
+    def _round_with_sampler(self, seq, seq_len, seq_draft, lens_now, B, dev):
+        """One round in logits mode: the draft loop through the pipeline, the
+        target rows through the same pipeline, then the verify."""
+        K = self.k
+        cap = seq.shape[1]
+        seq_draft[:, :cap] = seq
+        ar = torch.arange(B, device=dev)
+        toks = torch.zeros((B, K), dtype=torch.int32, device=dev)
+        qs = []
+        for i in range(K):
+            z = self.draft_step(seq, seq_len, toks[:, :i]).reshape(B, 1, -1).contiguous()
+            # the draft's history for position i: the committed tokens, then the i drafted ones
+            zp, q = self._pipeline(z, None, 1, seq_draft, seq_len + i, None)
+            if self.greedy:
+                t = zp[:, 0].argmax(-1).to(torch.int32)
+            else:
+                t = torch.multinomial(q[:, 0], 1, generator=self._draft_generator(dev)).squeeze(1).to(torch.int32)
+                qs.append(q[:, 0])
+            toks[:, i] = t
+            seq_draft[ar, (seq_len + i).long()] = t
+        zt = self.target_step(seq, seq_len, toks).contiguous()
+        zp, p = self._pipeline(zt, lens_now, 1, seq, seq_len, toks)
+        if self.greedy:
+            n, nx = sv_verify_greedy(zp.contiguous(), toks, lens_now)
+        else:
+            q = torch.stack(qs, 1).contiguous()
+            n, nx = sv_accept(p, q, toks, self._uniforms(B, dev), lens_now)
+        return n, nx, toks
+
+    def _draft_generator(self, dev):
+        g = self.generator
+        return g if g is not None and g.device == dev else None
 
     @staticmethod
     def _result(single, seq, seq_len):

@@ -49,6 +49,16 @@ class Markov:
             return torch.stack(toks, 1).to(torch.int32), torch.stack(probs, 1)
         return step
 
+    # ---- callbacks of the decoder's sampler mode (raw logits) ---------------
+    def draft_logits(self):
+        def step(seq, seq_len, drafted):
+            prev = drafted[:, -1].long() if drafted.shape[1] else self.last(seq, seq_len)
+            return self.W[prev]
+        return step
+
+    def target_logits(self):
+        return self.target_step(greedy=True)
+
     # ---- references ----------------------------------------------------------
     def greedy_chain(self, start: int, n: int, eos=None):
         """Plain greedy decoding from token `start` (lowest id on ties), CPU float32 logits."""
@@ -59,4 +69,16 @@ class Markov:
             out.append(prev)
             if eos is not None and prev == eos:
                 break
+        return out
+
+    def greedy_chain_with(self, prompt, n: int, row_fn):
+        """Plain greedy decoding of the rows row_fn(logits, history) (lowest id on
+        ties): the history is the prompt followed by the tokens generated so far."""
+        W = self.W.cpu().numpy()
+        hist = [int(x) for x in prompt]
+        out = []
+        for _ in range(n):
+            z = row_fn(W[hist[-1]], np.array(hist))
+            out.append(int(np.argmax(z)))
+            hist.append(out[-1])
         return out
