@@ -935,7 +935,7 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
 void coop_slice_shape(int B, int V, int& G, int& Ls) {
     int g = 4096 / (B > 0 ? B : 1);
     g = g < 1 ? 1 : (g > kMaxSlices ? kMaxSlices : g);
-    const int gv = (V + 32767) / 32768;
+    const int gv = (int)(((int64_t)V + 32767) / 32768);  // V may be INT32_MAX
     g = g < gv ? g : (gv > 1 ? gv : 1);
     int64_t ls = ((int64_t)V + g - 1) / g;
     ls = (ls + 1023) / 1024 * 1024;
