@@ -145,10 +145,6 @@ struct RowStats {
     double inv;
 };
 
-__device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) {
-    return (double)ex2(fmaf(z, c, -st.m)) * st.inv;
-}
-
 // The accept test u < p(t)/q(t) from the two logits at t. The ratio is formed
 // from the logit difference rather than from p and q separately:
 //   rho = 2^e * inv_t / inv_d,  e = (zt - zd) * c + m_d - m_t,

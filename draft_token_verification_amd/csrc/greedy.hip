@@ -173,7 +173,6 @@ __device__ __forceinline__ int span_argmax(const void* row, int x0, int len, flo
     constexpr int E = R::kPerVec;
     constexpr int NT = NW * kWave;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
     const char* span = (const char*)row + (size_t)x0 * (BF16 ? 2 : 4);
 
     // Elements before the first 16-byte boundary, one per lane.

@@ -37,7 +37,9 @@ _LOCK = threading.Lock()
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "liboracle.so")
+    """The oracle build to load: ``liboracle.so`` beside this file, or the build
+    named by SV_ORACLE_LIBRARY (the sanitized build the pins also run on)."""
+    return os.environ.get("SV_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 
 def load_library(path: str):

@@ -3,6 +3,9 @@ report fatal):
 
   - the fp64 oracle, driven through every entry point on small inputs with
     edge cases (tests/sanitize/oracle_checks.c);
+  - the oracle's whole pin suite (tests/test_oracle_*.py but the mutants, which
+    load builds of their own) run on a sanitized build of the oracle library,
+    the sanitizer runtimes preloaded into the test process;
   - the host side of libspecverify's C ABI, built from the same sources as the
     library (device code for gfx950, sanitizers on the host pass only) and
     driven through every documented argument error and every workspace-size
@@ -11,6 +14,7 @@ report fatal):
 import os
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -37,6 +41,29 @@ def test_oracle_under_asan_ubsan(tmp_path):
         str(tmp_path), 300)
     out = run([exe], str(tmp_path), 300, SAN_ENV)
     assert "oracle checks clean" in out
+
+
+def _runtime(name):
+    path = subprocess.run(["gcc", f"-print-file-name={name}"], stdout=subprocess.PIPE, text=True).stdout.strip()
+    return path if os.path.isabs(path) and os.path.exists(path) else None
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or _runtime("libasan.so") is None or _runtime("libubsan.so") is None,
+                    reason="no gcc sanitizer runtimes")
+@pytest.mark.skipif(bool(os.environ.get("LD_PRELOAD")), reason="the environment already preloads a library")
+def test_oracle_pins_on_a_sanitized_oracle(tmp_path):
+    lib = str(tmp_path / "liboracle_san.so")
+    run(["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+         os.path.join(ROOT, "oracle", "sv_oracle.c"), "-lm", "-o", lib], str(tmp_path), 300)
+    pins = sorted(os.path.join("tests", f) for f in os.listdir(os.path.join(ROOT, "tests"))
+                  if f.startswith("test_oracle_") and f.endswith(".py") and "mutants" not in f)
+    env = dict(SAN_ENV, SV_ORACLE_LIBRARY=lib, ASAN_OPTIONS="detect_leaks=0",  # the interpreter's own leaks
+               LD_PRELOAD=f"{_runtime('libasan.so')} {_runtime('libubsan.so')}")
+    out = run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-p", "no:xdist", "-m", "not gpu"] + pins,
+              ROOT, 900, env)
+    assert " passed" in out and "failed" not in out
+    print(out.strip().splitlines()[-1])
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="no hipcc")
