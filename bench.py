@@ -2,18 +2,27 @@
 """Benchmark of the speculative-decoding verify step on one MI355X.
 
 One step = one verify round over the whole batch, through every kernel of the
-hot path, on inputs already resident in HBM:
+hot path, on inputs already in HBM:
   sv_softmax_warp(target logits) + sv_softmax_warp(draft logits)
-  + sv_accept(p, q, tokens, uniforms) + sv_verify_greedy(target logits).
-Default workload: B = 512 sequences, K = 16 draft tokens, V = 256000, bf16
-logits (target ~ N(0, 5^2) with a Zipf(1.1) rank bias, draft = target +
-N(0, 1)), seeded synthetic data.
+  + sv_accept(p, q, tokens, uniforms) + sv_verify_greedy(target logits)
+(probability workloads: the two verifies). Default workload: B = 512
+sequences, K = 16 draft tokens, V = 256000, bf16 logits (target ~ N(0, 5^2)
+with a Zipf(1.1) rank bias, draft = target + N(0, 1)), seeded synthetic data.
 
-Prints ONE JSON line. ``value`` is verify rounds/s; ``roofline`` reports the
-dominant kernel (the warp) against MI355X's 8 TB/s HBM peak on algorithmic
-bytes, timed with HIP events on the stream the kernels run on;
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload on the host's cores.
+Every mode is timed twice with HIP events on the stream the kernels run on:
+"hbm", cycling through n >= 4 copies of the inputs of more than 1 GiB
+together, so that no call finds its inputs in the L2 caches or the MALL; and
+"resident", calling on one copy over and over. ``value`` is the whole step's
+hbm rounds/s. ``modes`` gives rounds/s per mode (greedy round, sampled round
+through the warps, sampled round fused from logits, the filtered warps and the
+penalty stage), each with its bytes needed (what the method must move) and,
+when rocprofv3 counters of these sources are on file, its bytes read, both as
+GB/s and as fractions of MI355X's 8 TB/s. ``roofline`` is the dominant
+kernel (the warp) on algorithmic bytes. ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same workload with every host thread and
+with one (medians over repeats).
+
+Prints ONE JSON line.
 """
 import argparse
 import json
@@ -47,6 +56,48 @@ def parse():
     return ap.parse_args()
 
 
+class Rotation:
+    """Copies of the batch's inputs in HBM: copy 0 is the batch itself, the rest
+    clones, so that consecutive calls can read different copies. With n copies
+    of more than 1 GiB together (and n >= 4) every call of a cycle reads inputs
+    that the n - 1 calls before it have pushed out of the L2 caches and the
+    256 MB MALL: the "hbm" timings. Timing copy 0 over and over gives the
+    "resident" ones."""
+
+    def __init__(self, batch, min_total=1 << 30, min_copies=4):
+        import torch
+        t, d = batch.target, batch.draft
+        per = t.numel() * t.element_size() + d.numel() * d.element_size() + batch.tokens.numel() * 4 \
+            + batch.uniforms.numel() * 4
+        self.n = max(min_copies, -(-min_total // per) + 1)
+        self.bytes_per_copy = per
+        extra = self.n - 1
+
+        def stack(x):
+            if x is None:
+                return [None] * self.n
+            more = x.unsqueeze(0).expand((extra,) + tuple(x.shape)).clone() if extra else None
+            return [x] + ([more[i] for i in range(extra)] if extra else [])
+        self.target, self.draft = stack(t), stack(d)
+        self.tokens, self.uniforms = stack(batch.tokens), stack(batch.uniforms)
+        self.lens = stack(batch.lens)
+        torch.cuda.synchronize()
+
+
+def timed(fn, indices, stream):
+    """Milliseconds per call of fn(i) over the indices, HIP events on `stream`."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in indices:
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / len(indices)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -65,136 +116,156 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
     batch = synth.generate(args.workload, dev)
     B, K, V = batch.B, batch.K, batch.V
     T = batch.temperature
     elem = 2 if batch.dtype == "bf16" else 4
-    lens = batch.lens
-
-    if batch.kind == "logits":
-        p = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
-        q = torch.empty((B, K, V), dtype=torch.float32, device=dev)
-    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
-    nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    n_gr = torch.empty(B, dtype=torch.int32, device=dev)
-    nx_gr = torch.empty(B, dtype=torch.int32, device=dev)
+    logits = batch.kind == "logits"
+    rot = Rotation(batch)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        if batch.kind == "logits":
-            sv.sv_softmax_warp(batch.target, T, lens, 1, out=p)
-            if ev:
-                ev[1].record(stream)
-            sv.sv_softmax_warp(batch.draft, T, lens, 0, out=q)
-            pp, qq = p, q
-        else:
-            if ev:
-                ev[1].record(stream)
-            pp, qq = batch.target, batch.draft
-        if ev:
-            ev[2].record(stream)
-        sv.sv_accept(pp, qq, batch.tokens, batch.uniforms, lens, out=(n_acc, nxt))
-        if ev:
-            ev[3].record(stream)
-        sv.sv_verify_greedy(batch.target, batch.tokens, lens, out=(n_gr, nx_gr))
-        if ev:
-            ev[4].record(stream)
+    p = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev) if logits else None
+    q = torch.empty((B, K, V), dtype=torch.float32, device=dev) if logits else None
+    o = {m: (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+         for m in ("greedy", "sampled", "fused")}
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # the modes, each a function of the input copy it reads
+    def greedy(c):
+        sv.sv_verify_greedy(rot.target[c], rot.tokens[c], rot.lens[c], out=o["greedy"])
 
-    # whole-step timing: K back-to-back steps between two events
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_per_step = total_ms / args.steps
+    def warp_t(c):
+        sv.sv_softmax_warp(rot.target[c], T, rot.lens[c], 1, out=p)
 
-    # per-kernel timing: the same steps with events between the launches
+    def warp_d(c):
+        sv.sv_softmax_warp(rot.draft[c], T, rot.lens[c], 0, out=q)
+
+    def accept(c):
+        pp, qq = (p, q) if logits else (rot.target[c], rot.draft[c])
+        sv.sv_accept(pp, qq, rot.tokens[c], rot.uniforms[c], rot.lens[c], out=o["sampled"])
+
+    def sampled_warps(c):
+        if logits:
+            warp_t(c)
+            warp_d(c)
+        accept(c)
+
+    def fused(c):
+        sv.sv_accept_logits(rot.target[c], rot.draft[c], rot.tokens[c], rot.uniforms[c], T, rot.lens[c],
+                            out=o["fused"])
+
+    def step(c):  # one pass of the whole hot path: both warps, the sampled verify, the greedy verify
+        sampled_warps(c)
+        greedy(c)
+
+    W, S, n = args.warmup, args.steps, rot.n
+    hbm = [(W + i) % n for i in range(S)]      # each call a different copy from the last n - 1
+    resident = [0] * S
+
+    def measure(fn):
+        for i in range(W):
+            fn(i % n)
+        h = timed(fn, hbm, stream)
+        for _ in range(W):
+            fn(0)
+        r = timed(fn, resident, stream)
+        return h, r
+
+    modes = {"step": step, "greedy": greedy, "sampled_warps": sampled_warps}
+    if logits:
+        modes["sampled_fused"] = fused
+    ms = {m: measure(fn) for m, fn in modes.items()}
+
+    # the step's kernels one by one (HBM copies): events between the launches
     per = np.zeros(4)
-    for _ in range(args.steps):
+    for i in hbm:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        step(ev)
+        ev[0].record(stream)
+        if logits:
+            warp_t(i)
+        ev[1].record(stream)
+        if logits:
+            warp_d(i)
+        ev[2].record(stream)
+        accept(i)
+        ev[3].record(stream)
+        greedy(i)
+        ev[4].record(stream)
         torch.cuda.synchronize()
-        per += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-    per /= args.steps
+        per += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+    per /= len(hbm)
     warp_t_ms, warp_d_ms, accept_ms, greedy_ms = per
 
-    # the fused sampled path: the accept test and the draw straight from logits
-    fused_ms = None
-    if batch.kind == "logits":
-        n_fu = torch.empty(B, dtype=torch.int32, device=dev)
-        nx_fu = torch.empty(B, dtype=torch.int32, device=dev)
-        fused = lambda: sv.sv_accept_logits(batch.target, batch.draft, batch.tokens, batch.uniforms, T, lens,
-                                            out=(n_fu, nx_fu))
-        for _ in range(args.warmup):
-            fused()
-        f0 = torch.cuda.Event(enable_timing=True)
-        f1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for _ in range(args.steps):
-            fused()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        fused_ms = f0.elapsed_time(f1) / args.steps
-
-    # the filtered warp (temperature, top-k, top-p) of target and draft rows
-    filt_ms = None
-    if batch.kind == "logits":
-        tk = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
-        tp = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
-
-        def filtered():
-            sv.sv_softmax_warp_filtered(batch.target, T, lens, 1, tk, tp, out=p)
-            sv.sv_softmax_warp_filtered(batch.draft, T, lens, 0, tk, tp, out=q)
-
-        for _ in range(args.warmup):
-            filtered()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        g0.record(stream)
-        for _ in range(args.steps):
-            filtered()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        filt_ms = g0.elapsed_time(g1) / args.steps
-
     # algorithmic bytes of each kernel (what the method must move)
-    kb = lens.cpu().numpy() if lens is not None else np.full(B, K)
-    n_s = n_acc.cpu().numpy().astype(np.int64)
-    n_g = n_gr.cpu().numpy().astype(np.int64)
-    rows_t = int((kb + 1).sum())
-    rows_d = int(kb.sum())
+    kb = batch.lens.cpu().numpy() if batch.lens is not None else np.full(B, K)
+    n_s = o["sampled"][0].cpu().numpy().astype(np.int64)
+    n_g = o["greedy"][0].cpu().numpy().astype(np.int64)
+    rows_t, rows_d = int((kb + 1).sum()), int(kb.sum())
     warp_bytes_t = rows_t * V * (elem + 4)
     warp_bytes_d = rows_d * V * (elem + 4)
     greedy_bytes = int(((n_g + 1) * V * elem).sum()) + 4 * B * K + 8 * B
-    accept_bytes = int((8 * np.minimum(n_s + 1, kb) + np.where(n_s < kb, 2 * V * 4, V * 4)).sum()) + 4 * B * (K + 1) \
-        + 8 * B
-    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9 if ms > 0 else None
-    if fused_ms is not None:
-        n_f = n_fu.cpu().numpy().astype(np.int64)
+    accept_bytes = int((8 * np.minimum(n_s + 1, kb) + np.where(n_s < kb, 2 * V * 4, V * 4)).sum()) \
+        + 4 * B * (K + 1) + 8 * B
+    gbs = lambda nbytes, t_ms: nbytes / (t_ms * 1e-3) / 1e9 if t_ms and t_ms > 0 else None
+    frac = lambda x: None if x is None else round(x / HBM_PEAK_GBS, 4)
+    r1 = lambda x, d=1: None if x is None else round(x, d)
+
+    # bytes the kernels read (rocprofv3 FETCH_SIZE, scaled; from the traffic file when it matches these sources)
+    traffic = {}
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == args.workload and tr.get("library_source_sha") == kernel_source_sha(True):
+            traffic = tr
+
+    def read_bytes(kernel, launches=1):
+        """FETCH bytes of one call's launches of `kernel`: its recorded launch
+        shapes, which must number `launches` (one per launch of the call)."""
+        grids = traffic.get("kernels", {}).get(kernel, {})
+        if len(grids) != launches:
+            return None
+        return sum(g["fetch"] for g in grids.values())
+
+    def mode_record(name, t_hbm, t_res, needed=None, read=None, **extra):
+        rec = {"hbm_ms": round(t_hbm, 4), "resident_ms": round(t_res, 4),
+               "hbm_rounds_per_s": round(1000.0 / t_hbm, 3), "resident_rounds_per_s": round(1000.0 / t_res, 3)}
+        if needed is not None:
+            g = gbs(needed, t_hbm)
+            rec.update({"needed_bytes": int(needed), "needed_GBps": r1(g), "needed_frac": frac(g)})
+        if read is not None:
+            g = gbs(read, t_hbm)
+            rec.update({"read_bytes": int(read), "read_GBps": r1(g), "read_frac": frac(g)})
+        rec.update(extra)
+        return rec
+
+    modes_out = {}
+    modes_out["greedy"] = mode_record("greedy", *ms["greedy"], needed=greedy_bytes,
+                                      read=read_bytes("greedy_sliced_kernel") or read_bytes("greedy_kernel"),
+                                      mean_n=round(float(n_g.mean()), 4))
+    sw_needed = accept_bytes + (warp_bytes_t + warp_bytes_d if logits else 0)
+    rd_acc = read_bytes("accept_kernel")
+    rd_warp = read_bytes("warp_coop_kernel", 2) if logits else 0
+    modes_out["sampled_warps"] = mode_record(
+        "sampled_warps", *ms["sampled_warps"], needed=sw_needed,
+        read=None if rd_acc is None or rd_warp is None else rd_acc + rd_warp, mean_n=round(float(n_s.mean()), 4))
+    if logits:
+        n_f = o["fused"][0].cpu().numpy().astype(np.int64)
         # target rows 0..n and draft rows 0..min(n, kb-1), each read once
         fused_bytes = int(((n_f + 1 + np.minimum(n_f + 1, kb)) * V * elem).sum()) + 4 * B * (2 * K + 1) + 8 * B
+        modes_out["sampled_fused"] = mode_record(
+            "sampled_fused", *ms["sampled_fused"], needed=fused_bytes,
+            read=read_bytes("accept_logits_sliced_kernel") or read_bytes("accept_logits_kernel"),
+            mean_n=round(float(n_f.mean()), 4))
+    step_hbm, step_res = ms["step"]
+    modes_out["step"] = mode_record("step", step_hbm, step_res, needed=sw_needed + greedy_bytes)
 
     out = {
         "metric": "verify rounds/s and achieved HBM GB/s (% of peak) for [B,K+1,V] verify",
-        "value": round(1000.0 / ms_per_step, 3),
+        "value": round(1000.0 / step_hbm, 3),
         "unit": "rounds/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(step_hbm, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -202,68 +273,69 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "K": K, "V": V, "input_dtype": batch.dtype,
                    "temperature": T,
-                   "step": ("warp(target)+warp(draft)+accept+greedy" if batch.kind == "logits"
-                            else "accept+greedy (inputs are probabilities)")},
+                   "step": ("warp(target)+warp(draft)+accept+greedy" if logits
+                            else "accept+greedy (inputs are probabilities)"),
+                   "inputs": f"{n} rotating copies of {rot.bytes_per_copy / 1e9:.3f} GB; value is the hbm timing"},
     }
-    if batch.kind == "logits":
+    if logits:
         warp_ms = warp_t_ms + warp_d_ms
-        warp_bytes = warp_bytes_t + warp_bytes_d
-        achieved = gbs(warp_bytes, warp_ms)
-        traffic = None
-        if os.path.exists(args.traffic):
-            with open(args.traffic) as f:
-                tr = json.load(f)
-            if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_source_sha():
-                traffic = tr.get("bytes_per_launch")
+        achieved = gbs(warp_bytes_t + warp_bytes_d, warp_ms)
+        wt = traffic.get("bytes_per_launch") if traffic.get("kernel_source_sha") == kernel_source_sha() else None
         out["roofline"] = {"bound": "hbm", "kernel": "warp_coop_kernel", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": traffic,
+                           "traffic": wt,
                            "algorithmic_bytes_per_launch": (warp_bytes_t + warp_bytes_d) // 2,
                            "avg_launch_ms": round(warp_ms / 2, 4)}
     else:  # probabilities in: the sampled verify is the step's largest kernel
         achieved = gbs(accept_bytes, accept_ms)
         out["roofline"] = {"bound": "hbm", "kernel": "accept_kernel", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": None, "algorithmic_bytes_per_launch": int(accept_bytes),
+                           "traffic": read_bytes("accept_kernel"), "algorithmic_bytes_per_launch": int(accept_bytes),
                            "avg_launch_ms": round(accept_ms, 4)}
+    out["modes"] = modes_out
     out["kernels"] = {
-        "warp_target_ms": round(warp_t_ms, 4) if batch.kind == "logits" else None,
-        "warp_draft_ms": round(warp_d_ms, 4) if batch.kind == "logits" else None,
+        "warp_target_ms": round(warp_t_ms, 4) if logits else None,
+        "warp_draft_ms": round(warp_d_ms, 4) if logits else None,
         "accept_ms": round(accept_ms, 4), "greedy_ms": round(greedy_ms, 4),
-        "warp_GBps": round(gbs(warp_bytes_t + warp_bytes_d, warp_t_ms + warp_d_ms), 1) if batch.kind == "logits"
-        else None,
-        "accept_GBps_needed": round(gbs(accept_bytes, accept_ms), 1),
-        "greedy_GBps_needed": round(gbs(greedy_bytes, greedy_ms), 1),
-        "mean_n_sampled": round(float(n_s.mean()), 4), "mean_n_greedy": round(float(n_g.mean()), 4),
+        "warp_GBps": r1(gbs(warp_bytes_t + warp_bytes_d, warp_t_ms + warp_d_ms)) if logits else None,
+        "accept_GBps_needed": r1(gbs(accept_bytes, accept_ms)),
+        "greedy_GBps_needed": r1(gbs(greedy_bytes, greedy_ms)),
     }
-    if filt_ms is not None:
-        out["kernels"].update({
-            "filtered_warp_ms": round(filt_ms, 4),
-            "filtered_warp_GBps": round(gbs(warp_bytes_t + warp_bytes_d, filt_ms), 1),
-            "filtered_warp_top_k": args.top_k, "filtered_warp_top_p": args.top_p,
-        })
-    if fused_ms is not None:
-        out["kernels"].update({
-            "accept_logits_ms": round(fused_ms, 4),
-            "accept_logits_GBps_needed": round(gbs(fused_bytes, fused_ms), 1),
-            "mean_n_accept_logits": round(float(n_f.mean()), 4),
-            "fused_sampled_rounds_per_s": round(1000.0 / (fused_ms + greedy_ms), 3),
-        })
 
-    # per-round latency, eager and replayed from a HIP graph (torch.cuda.CUDAGraph): the
-    # greedy round alone and the sampled round alone (probabilities: sv_accept; logits:
-    # the fused sv_accept_logits)
+    if logits:
+        # the filtered warp (temperature, top-k, top-p) of target and draft rows
+        tk = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
+        tp = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
+
+        def filtered(c):
+            sv.sv_softmax_warp_filtered(rot.target[c], T, rot.lens[c], 1, tk, tp, out=p)
+            sv.sv_softmax_warp_filtered(rot.draft[c], T, rot.lens[c], 0, tk, tp, out=q)
+        fh, fr = measure(filtered)
+        modes_out["filtered_warps"] = mode_record("filtered_warps", fh, fr, needed=warp_bytes_t + warp_bytes_d,
+                                                  top_k=args.top_k, top_p=args.top_p)
+
+        # the penalty stage of the target rows: a committed history of up to
+        # 2048 tokens per sequence plus each row's draft prefix
+        cap = 2048
+        g = torch.Generator(device=dev).manual_seed(7)
+        seq = torch.randint(0, V, (B, cap), generator=g, device=dev, dtype=torch.int32)
+        seq_len = torch.randint(cap // 2, cap + 1, (B,), generator=g, device=dev, dtype=torch.int32)
+        ws = torch.empty(sv.sv_apply_penalties_workspace_bytes(B, cap), dtype=torch.uint8, device=dev)
+
+        def penalties(c):
+            sv.sv_apply_penalties(rot.target[c], rot.lens[c], 1, seq, seq_len, rot.tokens[c], 1.2, 0.3, 0.1,
+                                  out=p, workspace=ws)
+        ph, pr = measure(penalties)
+        pen_bytes = warp_bytes_t + int(seq_len.sum().item()) * 4
+        modes_out["penalties_target"] = mode_record("penalties_target", ph, pr, needed=pen_bytes,
+                                                    history_cap=cap)
+        del seq, seq_len, ws
+
+    # per-round latency, eager and replayed from a HIP graph (torch.cuda.CUDAGraph), resident inputs
     def latency_us(fn, reps=50):
         fn()
         torch.cuda.synchronize()
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for _ in range(reps):
-            fn()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        eager = a0.elapsed_time(a1) / reps * 1e3
+        eager = timed(lambda _: fn(), range(reps), stream) * 1e3
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -276,71 +348,22 @@ def main():
             fn()
         graph.replay()
         torch.cuda.synchronize()
-        a0.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        return {"eager": round(eager, 2), "graph": round(a0.elapsed_time(a1) / reps * 1e3, 2)}
+        return {"eager": round(eager, 2), "graph": round(timed(lambda _: graph.replay(), range(reps), stream) * 1e3, 2)}
 
-    lat = {"greedy_round": latency_us(lambda: sv.sv_verify_greedy(batch.target, batch.tokens, lens, out=(n_gr, nx_gr)))}
-    if batch.kind == "logits":
-        lat["sampled_round_fused"] = latency_us(lambda: sv.sv_accept_logits(batch.target, batch.draft, batch.tokens,
-                                                                           batch.uniforms, T, lens, out=(n_fu, nx_fu)))
-    else:
-        lat["sampled_round"] = latency_us(lambda: sv.sv_accept(batch.target, batch.draft, batch.tokens, batch.uniforms,
-                                                               lens, out=(n_acc, nxt)))
+    lat = {"greedy_round": latency_us(lambda: greedy(0))}
+    lat["sampled_round_fused" if logits else "sampled_round"] = latency_us(lambda: (fused if logits else accept)(0))
     out["latency_us"] = lat
 
     # a measured stream-read rate: the greedy verify with draft tokens equal to
     # the target's argmax chain, so every live row of every sequence is read
-    # (the argmax kernel streaming with no early exit)
     chain = batch.target.argmax(-1).to(torch.int32)[:, :K].contiguous()
     n_ch = torch.empty(B, dtype=torch.int32, device=dev)
     nx_ch = torch.empty(B, dtype=torch.int32, device=dev)
-    sv.sv_verify_greedy(batch.target, chain, lens, out=(n_ch, nx_ch))
-    torch.cuda.synchronize()
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for _ in range(5):
-        sv.sv_verify_greedy(batch.target, chain, lens, out=(n_ch, nx_ch))
-    r1.record(stream)
-    torch.cuda.synchronize()
-    read_bytes = int(((n_ch.cpu().numpy().astype(np.int64) + 1) * V * elem).sum())
-    out["kernels"]["stream_read_GBps"] = round(gbs(read_bytes, r0.elapsed_time(r1) / 5), 1)
+    sv.sv_verify_greedy(batch.target, chain, batch.lens, out=(n_ch, nx_ch))
+    t_ch = timed(lambda _: sv.sv_verify_greedy(batch.target, chain, batch.lens, out=(n_ch, nx_ch)), range(5), stream)
+    out["kernels"]["stream_read_GBps"] = r1(gbs(int(((n_ch.cpu().numpy().astype(np.int64) + 1) * V * elem).sum()),
+                                                t_ch))
     del chain, n_ch, nx_ch
-
-    # bytes read by the round's kernels (rocprofv3 FETCH_SIZE, scaled, from the
-    # traffic file when it matches these sources) over the round time
-    if batch.kind == "logits" and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        ks = tr.get("kernels", {})
-        if tr.get("workload") == args.workload and tr.get("library_source_sha") == kernel_source_sha(True) and ks:
-            rd = lambda name: sum(x["fetch"] for x in ks.get(name, {}).values())
-            per_step = rd("warp_coop_kernel") + rd("accept_kernel") + rd("greedy_sliced_kernel") + rd("greedy_kernel")
-            out["kernels"]["round_bytes_read"] = per_step
-            out["kernels"]["round_read_GBps"] = round(gbs(per_step, ms_per_step), 1)
-
-    # practical reference for the warp's stream: torch's own bf16/fp32 -> fp32
-    # conversion copy of one target-row launch's worth of logits (read s,
-    # write 4 bytes per element), timed the same way
-    if batch.kind == "logits":
-        src = batch.target.reshape(-1)[: rows_t * V]
-        dst = p.reshape(-1)[: rows_t * V]
-        for _ in range(2):
-            dst.copy_(src)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        c0.record(stream)
-        for _ in range(5):
-            dst.copy_(src)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        out["kernels"]["torch_convert_copy_GBps"] = round(gbs(rows_t * V * (elem + 4), c0.elapsed_time(c1) / 5), 1)
-        del src, dst
 
     if args.copy_calibrate:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -373,7 +396,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
 
     kernel_re = re.compile(r"\b(warp_coop_kernel|warp_rows_kernel|warp_filter_kernel|accept_kernel|"
                            r"accept_logits_kernel|accept_logits_sliced_kernel|greedy_kernel|greedy_sliced_kernel|"
-                           r"fill_slots|fill_empty)\b")
+                           r"penalty_table_kernel|penalty_rows_kernel|fill_slots|fill_empty)\b")
 
     def load(path, counter):
         per, copy = {}, []
@@ -427,28 +450,27 @@ def kernel_source_sha(all_sources=False):
 
 
 def cpu_baseline(batch, seconds):
-    """The fp64 CPU oracle, as it stands, on a bounded sample of sequences of the
-    same workload: warp of the live target and draft rows, sampled verify on the
-    oracle's own fp64 probabilities, greedy verify on the logits. The sample is
-    repeated until about ``seconds`` of work, then scaled to rounds/s of the
-    full batch."""
+    """The fp64 CPU oracle, as it stands, on a bounded sample of the workload's
+    sequences: warp of the live target and draft rows, sampled verify on the
+    oracle's own fp64 probabilities, greedy verify on the logits (probability
+    workloads: the two verifies). Timed with every host thread and with one,
+    each as the median over repeats of its sample (about half of ``seconds``
+    each), scaled by B / sample to rounds/s of the whole batch."""
     import numpy as np
     import oracle
 
     B, K, V = batch.B, batch.K, batch.V
     affinity = len(os.sched_getaffinity(0))
     threads = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity)))
-    # keep the sample's fp64 probability arrays under ~4 GB
-    cap = max(1, int(4e9 // ((2 * K + 1) * V * 8)))
-    n = min(B, cap, max(threads, 1) * 4)
-    sel = np.random.default_rng(0).permutation(B)[:n].tolist()
-    tgt = batch.target[sel].cpu()
-    drf = batch.draft[sel].cpu()
-    tok = batch.tokens[sel].cpu()
-    uni = batch.uniforms[sel].cpu()
-    ln = None if batch.lens is None else batch.lens[sel].cpu()
+    cap = max(1, int(4e9 // ((2 * K + 1) * V * 8)))  # the sample's fp64 probability rows under ~4 GB
+    order = np.random.default_rng(0).permutation(B).tolist()
 
-    def run():
+    def sample(n):
+        sel = order[:n]
+        return (batch.target[sel].cpu(), batch.draft[sel].cpu(), batch.tokens[sel].cpu(), batch.uniforms[sel].cpu(),
+                None if batch.lens is None else batch.lens[sel].cpu())
+
+    def run(tgt, drf, tok, uni, ln):
         t0 = time.perf_counter()
         if batch.kind == "logits":
             p = np.nan_to_num(oracle.softmax_warp(tgt, ln, 1, batch.temperature))
@@ -459,14 +481,25 @@ def cpu_baseline(batch, seconds):
         oracle.verify_greedy(tgt, tok, ln)
         return time.perf_counter() - t0
 
-    total, reps = 0.0, 0
-    while total < seconds or reps < 1:
-        total += run()
-        reps += 1
-    per_round = total / reps * B / n
-    return {"value": round(1.0 / per_round, 6), "unit": "rounds/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {B} sequences x {reps} repeats ({total:.1f} s): warp of the live rows, sampled "
-                      f"verify on the oracle's fp64 probs, greedy on the logits; scaled by B/{n}"}
+    def leg(nthreads, n, budget):
+        used = oracle.set_threads(nthreads)
+        data = sample(n)
+        times = [run(*data)]
+        while sum(times) < budget or len(times) < 3:
+            times.append(run(*data))
+        med = statistics.median(times)
+        return {"value": round(n / (med * B), 6), "unit": "rounds/s", "cores": used, "kind": "oracle",
+                "sample": f"{n} of {B} sequences ({100.0 * n / B:.1f}%), median of {len(times)} repeats "
+                          f"({med:.3f} s each), scaled by B/{n}"}
+
+    n_all = min(B, cap, max(threads, 1) * 4)
+    all_core = leg(threads, n_all, seconds / 2)
+    single = leg(1, max(1, min(n_all, 2)), seconds / 2)
+    oracle.set_threads(threads)
+    all_core["what"] = ("warp of the live target and draft rows, sampled verify on the oracle's fp64 probs, greedy "
+                        "on the logits" if batch.kind == "logits" else "sampled and greedy verify of the probs")
+    all_core["single_thread"] = single
+    return all_core
 
 
 if __name__ == "__main__":

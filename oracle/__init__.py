@@ -26,7 +26,7 @@ __all__ = ["warp_row", "softmax_warp", "argmax_row", "verify_greedy", "accept", 
            "overlap", "F32", "BF16", "F64", "FLAG_RATIO", "FLAG_CDF", "FLAG_ZERO_RESIDUAL",
            "FLAG_NO_MASS", "FLAG_TOPP", "warp_row_filtered", "softmax_warp_filtered", "top2_margin", "gate_update",
            "gate_choose", "GATE_DEFAULTS", "penalize_row", "apply_penalties", "library_path",
-           "load_library"]
+           "load_library", "set_threads"]
 
 F32, BF16, F64 = 0, 1, 2
 FLAG_RATIO, FLAG_CDF, FLAG_ZERO_RESIDUAL, FLAG_NO_MASS, FLAG_TOPP = 1, 2, 4, 8, 16
@@ -69,8 +69,15 @@ def load_library(path: str):
     lib.or_gate_choose.argtypes = [vp, vp, i64, i64, i64, vp, vp, f64, f64, f64, f64, f64, i32, f64, vp]
     lib.or_overlap.argtypes = [vp, vp, ctypes.c_int, i64]
     lib.or_overlap.restype = f64
+    lib.or_set_threads.argtypes = [ctypes.c_int]
+    lib.or_set_threads.restype = ctypes.c_int
     assert lib.or_abi_version() == 1
     return lib
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's row loops use from now on; returns the count in effect (timing only)."""
+    return int(_lib().or_set_threads(int(n)))
 
 
 def _lib():

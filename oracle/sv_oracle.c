@@ -44,6 +44,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #include "sv_oracle.h"
 
@@ -563,3 +566,15 @@ double or_overlap(const void* p, const void* q, int dtype, int64_t V) {
 }
 
 int or_abi_version(void) { return 1; }
+
+/* Threads the parallel loops over rows use from now on (n >= 1); returns the
+ * count in effect. Timing only: results do not depend on it. */
+int or_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}

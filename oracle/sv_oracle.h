@@ -26,6 +26,7 @@ enum {
 };
 
 int or_abi_version(void);
+int or_set_threads(int n); /* threads of the row loops (timing only); returns the count in effect */
 
 void or_warp_row(const void* z, int dtype, int64_t V, double T, double* p);
 void or_softmax_warp(const void* logits, int dtype, int64_t B, int64_t R, int64_t V,

@@ -56,3 +56,15 @@ def test_traffic_from_counters(tmp_path):
     assert rec["kernels"]["greedy_sliced_kernel"]["4000"]["fetch"] == int(11.0 * 1024 * 2)
     assert rec["kernel_source_sha"] == bench.kernel_source_sha()
     assert rec["library_source_sha"] == bench.kernel_source_sha(all_sources=True)
+
+
+def test_cpu_baseline_reports_all_core_and_single_thread_medians():
+    import synth
+    for name in ("logits-bf16-b256-k5-v128256", "probs-b64-k4-v32000"):
+        batch = synth.generate(name, "cpu", B=6, V=640)
+        rec = bench.cpu_baseline(batch, 0.2)
+        st = rec["single_thread"]
+        assert rec["kind"] == st["kind"] == "oracle" and rec["unit"] == st["unit"] == "rounds/s"
+        assert st["cores"] == 1 and rec["cores"] >= 1
+        assert rec["value"] > 0 and st["value"] > 0
+        assert "median of" in rec["sample"] and "of 6 sequences" in st["sample"]
