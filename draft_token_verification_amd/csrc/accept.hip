@@ -681,194 +681,523 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
 
 // ---- accept_logits_sliced_kernel: each sequence over G workgroups ----------
 //
-// The same procedure as accept_logits_kernel, with the rows of a sequence
-// split into G slices of Ls elements; workgroup (b, g) of 256 lanes owns
-// slice g of every row of sequence b. At each examined position the G
-// workgroups publish their slices' statistics (m, s) of the target and draft rows
-// into sentinel-filled slots of the caller's workspace and merge all G in a
-// fixed order, so every slice takes the same accept decision; for the draw
-// each publishes its slice's total weight, all find the slice holding u * S,
-// and that one locates the id inside it. A long chain of accepted positions
-// thus runs on G compute units instead of one. Every wait is bounded: a
-// workgroup that gives up recomputes the missing slices' values itself with
+// The procedure of accept_logits_kernel with the rows of a sequence split
+// into G slices; workgroup (b, g) of 256 lanes owns slice g of every row of
+// sequence b. A slice is kSliceVecs 16-byte vectors per lane and row (12288
+// bf16 or 6144 fp32 logits), so at each examined position the workgroup
+// issues its whole share of the target and draft rows as one batch of loads;
+// the target share stays in registers and the draft share is parked in LDS.
+// The kernel is bound by its arithmetic (two exponentials per element pair,
+// and per position the reductions, the exchange and the accept test), not by
+// memory: measured on MI355X at B = 512, K = 16, V = 256000 it runs about as
+// fast with its slice loads removed. Six vectors per lane (G = 21 slices of
+// 24 KB per row there) beat four by 4% and eight (which spills) by 30%.
+// The slice's statistics, the accept test, the weights of the draw and the
+// locate of the drawn id all come from those copies, so every byte the
+// method needs is fetched once. At each position the G workgroups publish
+// their slices' statistics (m, s) of both rows into slots of the caller's
+// workspace (filled with the empty marker before the launch) and each merges
+// all G in one fixed order, so every slice takes the same decision; for the
+// draw each publishes its slice's total weight, all find the slice holding
+// u * S, and that one locates the id. Every wait is bounded: a workgroup that
+// gives up loads the missing slices and computes their values itself with
 // the same code and lane mapping, so results are bitwise identical either way.
 
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
-constexpr int kMaxSlices = kMaxCoopSlices;
-static_assert(kMaxSlices <= 8, "slice partials are merged by a butterfly over 8 lanes");
+constexpr int kSliceVecs = 6;      // 16-byte vectors per lane and row: one batch of loads per position
+constexpr int kMaxSlices = kWave;  // slice partials are merged across one wavefront
+constexpr int kChunks = kSliceVecs * kSliceWaves;
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 buffer descriptor: raw 32-bit data, no swizzle
+
+// 16 bytes of a row: 8 bf16 or 4 fp32 logits.
+template <bool BF16>
+struct Vec16 {
+    static constexpr int E = BF16 ? 8 : 4;
+    __device__ static u32x4 neg_inf() {
+        const uint32_t w = BF16 ? 0xFF80FF80u : 0xFF800000u;
+        return u32x4{w, w, w, w};
+    }
+};
+
+// Elements 4h .. 4h + 3 of a 16-byte vector (h < E / 4).
+template <bool BF16>
+__device__ __forceinline__ void quad_of(const u32x4& r, int h, float z[4]) {
+    if (BF16) {
+        z[0] = bf16_lo(r[2 * h]);
+        z[1] = bf16_hi(r[2 * h]);
+        z[2] = bf16_lo(r[2 * h + 1]);
+        z[3] = bf16_hi(r[2 * h + 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) z[k] = __uint_as_float(r[k]);
+    }
+}
+
+// The lane's share of elements [x0, x0 + len) of a row: vector u holds
+// elements x0 + (u * 256 + lane) * E ... + E - 1 (lane = threadIdx.x), so
+// each load instruction covers 4 KB of consecutive logits; vectors at or past
+// x0 + len read as -inf (only a row's last slice is partial). VEC: buffer
+// loads of 16 bytes (V a multiple of E, rows 16-byte aligned); otherwise
+// element by element.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load_slice(const char* row, int64_t x0, int len, u32x4 (&r)[kSliceVecs]) {
+    using W = Vec16<BF16>;
+    constexpr int E = W::E;
+    constexpr int es = BF16 ? 2 : 4;
+    const int tid = threadIdx.x;
+    if (VEC) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row) + x0 * es, 0, len * es, kBufferWord3);
+#pragma unroll
+        for (int u = 0; u < kSliceVecs; ++u)
+            r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, u * kSliceThreads * 16, 0);
+        if (len < kSliceThreads * kSliceVecs * E) {  // the row's last slice: past its end reads -inf
+#pragma unroll
+            for (int u = 0; u < kSliceVecs; ++u)
+                if ((u * kSliceThreads + tid) * E >= len) r[u] = W::neg_inf();
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSliceVecs; ++u) {
+            const int xi = (u * kSliceThreads + tid) * E;
+            float z[E];
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const bool in = xi + j < len;
+                const float v = Logit4<BF16>::at(row, x0 + (in ? xi + j : 0));
+                z[j] = in ? v : -INFINITY;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                r[u][k] = BF16 ? (__float_as_uint(z[2 * k]) >> 16) | (__float_as_uint(z[2 * k + 1]) & 0xFFFF0000u)
+                               : __float_as_uint(z[k]);
+        }
+    }
+}
+
+// Largest logit of the lane's share.
+template <bool BF16>
+__device__ __forceinline__ float lane_max(const u32x4 (&r)[kSliceVecs]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSliceVecs; ++u) {
+#pragma unroll
+        for (int h = 0; h < Vec16<BF16>::E / 4; ++h) {
+            float z[4];
+            quad_of<BF16>(r[u], h, z);
+            mx = max3f(mx, max3f(z[0], z[1], z[2]), z[3]);
+        }
+    }
+    return mx;
+}
+
+// Sum of 2^(z * c - m) over the lane's share: fp32 per vector, binary64
+// across vectors (each vector unpacked afresh: no unpacked copy kept live).
+template <bool BF16>
+__device__ __forceinline__ double lane_expsum(const u32x4 (&r)[kSliceVecs], float c, float m) {
+    constexpr int E = Vec16<BF16>::E;
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < kSliceVecs; ++u) {
+        u32x4 v = r[u];
+        asm volatile("" : "+v"(v));
+        float e[E];
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            float z[4];
+            quad_of<BF16>(v, h, z);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[4 * h + j] = ex2(fmaf(z[j], c, -m));
+        }
+        s += (double)tree_sum<E>(e);
+    }
+    return s;
+}
+
+// Wave-wide maximum (fixed butterfly; result uniform).
+__device__ __forceinline__ float wave_max_f(float x) {
+    x = max2f(x, dpp_f<kDppQuadXor1>(x));
+    x = max2f(x, dpp_f<kDppQuadXor2>(x));
+    x = max2f(x, dpp_f<kDppRowHalfMirror>(x));
+    x = max2f(x, dpp_f<kDppRowMirror>(x));
+    x = max2f(x, swz16_f(x));
+    return max2f(readlane_f(x, 0), readlane_f(x, 32));
+}
+
+// Statistics (m, s) of the slice held in rt (and rd when D), over the
+// workgroup: m is the ceiling of the slice's largest y = z * c (kNoRef if
+// none is finite), shared by every lane, so the lanes' sums of 2^(y - m) add
+// up without rescaling; the wave sums and the kSliceWaves wave partials are
+// added in a fixed order. t and d are uniform. Contains barriers.
+template <bool BF16, bool D>
+__device__ void slice_stats(const u32x4 (&rt)[kSliceVecs], const u32x4 (&rd)[kSliceVecs], float c, StatsLds* lds,
+                            Online& t, Online& d) {
+    static_assert(kSliceWaves == 4, "four wave partials are combined below");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float xt = wave_max_f(lane_max<BF16>(rt)), xd = -INFINITY;
+    if (D) xd = wave_max_f(lane_max<BF16>(rd));
+    __syncthreads();  // the LDS slots may still be read from the previous call
+    if (lane == 0) {
+        lds->m[0][wave] = xt;
+        if (D) lds->m[1][wave] = xd;
+    }
+    __syncthreads();
+    xt = max2f(max2f(lds->m[0][0], lds->m[0][1]), max2f(lds->m[0][2], lds->m[0][3]));
+    t.m = max2f(kNoRef, ceilf(xt * c));
+    const double st = wave_sum_d(lane_expsum<BF16>(rt, c, t.m));
+    double sd = 0.0;
+    if (D) {
+        xd = max2f(max2f(lds->m[1][0], lds->m[1][1]), max2f(lds->m[1][2], lds->m[1][3]));
+        d.m = max2f(kNoRef, ceilf(xd * c));
+        sd = wave_sum_d(lane_expsum<BF16>(rd, c, d.m));
+    }
+    if (lane == 0) {
+        lds->s[0][wave] = st;
+        if (D) lds->s[1][wave] = sd;
+    }
+    __syncthreads();
+    t.s = (lds->s[0][0] + lds->s[0][1]) + (lds->s[0][2] + lds->s[0][3]);
+    if (D) d.s = (lds->s[1][0] + lds->s[1][1]) + (lds->s[1][2] + lds->s[1][3]);
+}
 
 __device__ __forceinline__ unsigned long long pack_online(const Online& o) {
     return ((unsigned long long)__float_as_uint((float)o.s) << 32) | __float_as_uint(o.m);
 }
 
-__device__ __forceinline__ void merge_packed(Online& r, unsigned long long v) {
-    online_merge(r, __uint_as_float((unsigned)v), (double)__uint_as_float((unsigned)(v >> 32)));
+// Shared state of a workgroup's exchanges.
+struct SliceCtx {
+    unsigned long long* s_words;  // LDS [2 * kMaxSlices]
+    int* s_ready;
+    u32x4* s_draft;  // LDS [kSliceVecs][256]: this slice of the current draft row
+    int G, g, Ls, V, wait_limit;
+    __device__ int len(int k) const { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); }
+    __device__ u32x4 draft(int u) const { return s_draft[u * kSliceThreads + threadIdx.x]; }
+};
+
+// Slice statistics of rows tr (and dr when D), loaded here: a fallback path.
+template <bool BF16, bool VEC, bool D>
+__device__ void other_slice_stats(const SliceCtx& x, int k, const char* tr, const char* dr, float c, StatsLds* lds,
+                                  Online& t, Online& d) {
+    u32x4 vt[kSliceVecs], vd[kSliceVecs];
+    load_slice<BF16, VEC>(tr, (int64_t)k * x.Ls, x.len(k), vt);
+    if (D) load_slice<BF16, VEC>(dr, (int64_t)k * x.Ls, x.len(k), vd);
+    slice_stats<BF16, D>(vt, vd, c, lds, t, d);
 }
 
-// Row statistics of the examined rows (target, and draft when D) from the G
-// slices: publish this slice's partials into set[2g], set[2g + 1], gather all,
-// merge in slice order. Called by the whole workgroup.
+// Position `pos`: load this slice of target row tr into rt (and of draft row
+// dr into s_draft, when D), take the slice statistics, publish them into
+// set[2g], set[2g + 1], gather all G and merge them in slice order into st
+// (and sd). If the wait runs out every slice is loaded and computed here
+// alike. Called by the whole workgroup.
 template <bool BF16, bool VEC, bool D>
-__device__ void sliced_row_stats(unsigned long long* set, int G, int g, int Ls, int V, const void* zt, const void* zd,
-                                 float c, StatsLds* lds, int wait_limit, unsigned long long* s_words, int* s_ready,
-                                 RowStats& st, RowStats& sd) {
-    const int64_t x0 = (int64_t)g * Ls;
-    Online a, d;
-    span_stats<BF16, VEC, D, kSliceWaves, BF16 ? 2 : 1>(zt, zd, x0, (int)min((int64_t)Ls, (int64_t)V - x0), c, lds, a, d);
-    publish_word(set + 2 * g, pack_online(a));
-    publish_word(set + 2 * g + 1, D ? pack_online(d) : 0ull);  // both words: the gather waits for all 2G
-    if (!gather_words(set, 2 * G, wait_limit, s_words, s_ready)) {
-        // bounded wait ran out: every slice's partials, recomputed here alike
-        for (int k = 0; k < G; ++k) {
-            const int64_t xk = (int64_t)k * Ls;
-            Online ak, dk;
-            span_stats<BF16, VEC, D, kSliceWaves, BF16 ? 2 : 1>(zt, zd, xk, (int)min((int64_t)Ls, (int64_t)V - xk), c, lds, ak,
-                                                     dk);
+__device__ void position_stats(const SliceCtx& x, unsigned long long* set, const char* tr, const char* dr, float c,
+                               u32x4 (&rt)[kSliceVecs], StatsLds* lds, RowStats& st, RowStats& sd) {
+    const int64_t x0 = (int64_t)x.g * x.Ls;
+    Online a, d{kNoRef, 0.0};
+    u32x4 v[kSliceVecs];
+    if (D) load_slice<BF16, VEC>(dr, x0, x.len(x.g), v);
+    load_slice<BF16, VEC>(tr, x0, x.len(x.g), rt);
+    slice_stats<BF16, D>(rt, v, c, lds, a, d);
+    if (D) {
+#pragma unroll
+        for (int u = 0; u < kSliceVecs; ++u) x.s_draft[u * kSliceThreads + threadIdx.x] = v[u];  // own lanes only
+    }
+    publish_word(set + 2 * x.g, pack_online(a));
+    publish_word(set + 2 * x.g + 1, D ? pack_online(d) : 0ull);  // both words: the gather waits for all 2G
+    if (!gather_words(set, 2 * x.G, x.wait_limit, x.s_words, x.s_ready)) {
+        for (int k = 0; k < x.G; ++k) {
+            Online ak, dk{kNoRef, 0.0};
+            other_slice_stats<BF16, VEC, D>(x, k, tr, dr, c, lds, ak, dk);
             if (threadIdx.x == 0) {
-                s_words[2 * k] = pack_online(ak);
-                s_words[2 * k + 1] = D ? pack_online(dk) : 0ull;
+                x.s_words[2 * k] = pack_online(ak);
+                x.s_words[2 * k + 1] = D ? pack_online(dk) : 0ull;
             }
         }
+        load_slice<BF16, VEC>(tr, x0, x.len(x.g), rt);  // this slice again (its draft share is in LDS)
         __syncthreads();
     }
-    // merge the G <= 8 slices' partials in a fixed butterfly over lanes 0-7
-    // of every wavefront (lane k holds slice k), then take lane 0's result
+    // lane k holds slice k: the largest reference, then the slices' sums
+    // scaled to it (exact powers of two) added in the fixed butterfly order
     const int lane = threadIdx.x & (kWave - 1);
-    Online rt{kNoRef, 0.0}, rd{kNoRef, 0.0};
-    if (lane < G) {
-        merge_packed(rt, s_words[2 * lane]);
-        if (D) merge_packed(rd, s_words[2 * lane + 1]);
+    float mt = kNoRef, md = kNoRef;
+    double s_t = 0.0, s_d = 0.0;
+    if (lane < x.G) {
+        const unsigned long long w = x.s_words[2 * lane];
+        mt = __uint_as_float((unsigned)w);
+        s_t = (double)__uint_as_float((unsigned)(w >> 32));
+        if (D) {
+            const unsigned long long w2 = x.s_words[2 * lane + 1];
+            md = __uint_as_float((unsigned)w2);
+            s_d = (double)__uint_as_float((unsigned)(w2 >> 32));
+        }
     }
-    online_merge(rt, dpp_f<kDppQuadXor1>(rt.m), dpp_d<kDppQuadXor1>(rt.s));
-    online_merge(rt, dpp_f<kDppQuadXor2>(rt.m), dpp_d<kDppQuadXor2>(rt.s));
-    online_merge(rt, dpp_f<kDppRowHalfMirror>(rt.m), dpp_d<kDppRowHalfMirror>(rt.s));
-    st = RowStats{readlane_f(rt.m, 0), 1.0 / readlane_d(rt.s, 0)};
+    const float Mt = wave_max_f(mt);
+    st = RowStats{Mt, 1.0 / wave_sum_d(rescale(s_t, mt, Mt))};
     if (D) {
-        online_merge(rd, dpp_f<kDppQuadXor1>(rd.m), dpp_d<kDppQuadXor1>(rd.s));
-        online_merge(rd, dpp_f<kDppQuadXor2>(rd.m), dpp_d<kDppQuadXor2>(rd.s));
-        online_merge(rd, dpp_f<kDppRowHalfMirror>(rd.m), dpp_d<kDppRowHalfMirror>(rd.s));
-        sd = RowStats{readlane_f(rd.m, 0), 1.0 / readlane_d(rd.s, 0)};
+        const float Md = wave_max_f(md);
+        sd = RowStats{Md, 1.0 / wave_sum_d(rescale(s_d, md, Md))};
     }
     __syncthreads();  // s_words is reused by the next exchange
 }
 
-// Slice totals of the draw weights: this slice's table into seg (its total
-// published into set[g]); all G totals into s_tot, in slice order.
-template <class Src, class MakeSrc>
-__device__ void sliced_totals(unsigned long long* set, int G, int g, int m, int nseg_max, int Ls, int V, double* seg,
-                              int wait_limit, unsigned long long* s_words, int* s_ready, double* s_tot,
-                              MakeSrc make) {
-    const int64_t L = (int64_t)m * kSub;
-    auto nseg_of = [&](int k) {
-        const int64_t len = min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls);
-        return (int)((len + L - 1) / L);
-    };
-    const Src mine = make(g);
-    const double Sg = segment_totals<kSliceWaves>(mine, m, nseg_of(g), seg);
-    publish_word(set + g, (unsigned long long)__double_as_longlong(Sg));
-    if (gather_words(set, G, wait_limit, s_words, s_ready)) {
-        if (threadIdx.x < G) s_tot[threadIdx.x] = __longlong_as_double((long long)s_words[threadIdx.x]);
-    } else {
-        double* scratch = seg + nseg_max;  // keep this slice's table intact
-        for (int k = 0; k < G; ++k) {
-            const double Sk = segment_totals<kSliceWaves>(make(k), m, nseg_of(k), scratch);
-            if (threadIdx.x == 0) s_tot[k] = Sk;
-            __syncthreads();
+// Draw weights of elements 4h .. 4h + 3 of a vector pair: max(0, p - q) (D;
+// formed as in LogitSource) or max(0, p).
+template <bool BF16, bool D>
+__device__ __forceinline__ void quad_weights(const u32x4& vt, const u32x4& vd, int h, float c, const RowStats& st,
+                                             const Shift& k, double w[4]) {
+    float a[4], d[4];
+    quad_of<BF16>(vt, h, a);
+    if (D) quad_of<BF16>(vd, h, d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float e = ex2(fmaf(a[j], c, -st.m));
+        if (D) {
+            const float y = fmaf(d[j] - a[j], c, k.ki) + k.kf;
+            w[j] = y < 0.0f ? (double)(e * one_minus_exp2(y)) * st.inv : 0.0;
+        } else {
+            w[j] = fmax((double)e * st.inv, 0.0);  // a NaN gives 0
         }
     }
+}
+
+// Total draw weight of one vector pair, quad by quad in element order.
+template <bool BF16, bool D>
+__device__ __forceinline__ double vec_total(const u32x4& vt, const u32x4& vd, float c, const RowStats& st,
+                                            const Shift& k) {
+    double s = 0.0;
+#pragma unroll
+    for (int h = 0; h < Vec16<BF16>::E / 4; ++h) {
+        double w[4];
+        quad_weights<BF16, D>(vt, vd, h, c, st, k, w);
+        s += ((w[0] + w[1]) + w[2]) + w[3];
+    }
+    return s;
+}
+
+// The slice's draw weights summed per chunk (vector u of wavefront w's 64
+// lanes: 64 * E consecutive elements; chunk u * kSliceWaves + w, so chunks
+// run in element order) into chunk[]; returns the slice total, the chunks
+// summed in order (uniform). dvec(u) gives the draft vector u (D only).
+// Contains barriers.
+template <bool BF16, bool D, class DVec>
+__device__ double slice_total(const u32x4 (&rt)[kSliceVecs], DVec dvec, float c, const RowStats& st,
+                              const Shift& k, double* chunk) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    __syncthreads();  // chunk[] may still be read from the previous call
+#pragma unroll
+    for (int u = 0; u < kSliceVecs; ++u) {
+        const double tot = wave_sum_d(vec_total<BF16, D>(rt[u], D ? dvec(u) : rt[u], c, st, k));
+        if (lane == 0) chunk[u * kSliceWaves + wave] = tot;
+    }
     __syncthreads();
+    double S = 0.0;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) S += chunk[q];
+    return S;
+}
+
+// A total as a slot word: the sign bit flipped, so that no total is the empty
+// marker (weights are never negative; a NaN keeps a NaN pattern).
+__device__ __forceinline__ unsigned long long total_word(double S) {
+    return (unsigned long long)__double_as_longlong(S) ^ 0x8000000000000000ull;
+}
+__device__ __forceinline__ double word_total(unsigned long long w) {
+    return __longlong_as_double((long long)(w ^ 0x8000000000000000ull));
+}
+
+// Total draw weight of the row (pair) over the G slices: this slice's total
+// (its chunks left in chunk[]) is published into set[g], all G gathered into
+// s_tot and summed in slice order (uniform). If the wait runs out, every
+// slice is loaded and summed here alike; then this slice's chunks again.
+// Called by the whole workgroup.
+template <bool BF16, bool VEC, bool D>
+__device__ double exchange_totals(const SliceCtx& x, unsigned long long* set, const char* tr, const char* dr, float c,
+                                  const RowStats& st, const Shift& k, u32x4 (&rt)[kSliceVecs], double* chunk,
+                                  double* s_tot) {
+    auto own_draft = [&](int u) { return x.draft(u); };
+    const double Sg = slice_total<BF16, D>(rt, own_draft, c, st, k, chunk);
+    publish_word(set + x.g, total_word(Sg));
+    if (gather_words(set, x.G, x.wait_limit, x.s_words, x.s_ready)) {
+        if (threadIdx.x < x.G) s_tot[threadIdx.x] = word_total(x.s_words[threadIdx.x]);
+    } else {
+        for (int kk = 0; kk < x.G; ++kk) {
+            u32x4 vd[kSliceVecs];
+            load_slice<BF16, VEC>(tr, (int64_t)kk * x.Ls, x.len(kk), rt);
+            if (D) load_slice<BF16, VEC>(dr, (int64_t)kk * x.Ls, x.len(kk), vd);
+            auto other_draft = [&](int u) { return vd[u]; };
+            const double Sk = slice_total<BF16, D>(rt, other_draft, c, st, k, chunk);
+            if (threadIdx.x == 0) s_tot[kk] = Sk;
+        }
+        // this slice again (its draft share is in LDS), and its chunks
+        load_slice<BF16, VEC>(tr, (int64_t)x.g * x.Ls, x.len(x.g), rt);
+        slice_total<BF16, D>(rt, own_draft, c, st, k, chunk);
+    }
+    __syncthreads();
+    double S = 0.0;
+    for (int kk = 0; kk < x.G; ++kk) S += s_tot[kk];
+    return S;
+}
+
+// Element-level locate inside vector U of the calling wavefront's lanes:
+// the lanes' vector totals scanned in lane order, then each lane's elements
+// in order, quad by quad (weights formed again: no arrays kept). pre is the
+// cumulative weight before the chunk. Returns the offset in the slice of the
+// first positive-weight element whose cumulative weight exceeds thr, else
+// the chunk's last positive-weight element (-1 if none), in every lane.
+template <bool BF16, bool D, int U>
+__device__ int locate_in_chunk(const SliceCtx& x, const u32x4 (&rt)[kSliceVecs], float c, const RowStats& st,
+                               const Shift& k, double pre, double thr) {
+    constexpr int E = Vec16<BF16>::E;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const u32x4 vt = rt[U];
+    const u32x4 vd = D ? x.draft(U) : vt;
+    const double incl = wave_incl_scan_d(vec_total<BF16, D>(vt, vd, c, st, k), lane);
+    double excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.0;
+    double run = pre + excl;
+    const int first = (U * kSliceThreads + wave * kWave + lane) * E;
+    int cand = -1, lp = -1;
+#pragma unroll
+    for (int h = 0; h < E / 4; ++h) {
+        double w[4];
+        quad_weights<BF16, D>(vt, vd, h, c, st, k, w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            run += w[j];
+            if (cand < 0 && w[j] > 0.0 && run > thr) cand = first + 4 * h + j;
+            if (w[j] > 0.0) lp = first + 4 * h + j;
+        }
+    }
+    const uint64_t hit = __ballot(cand >= 0);
+    if (hit) return readlane_i(cand, __builtin_ctzll(hit));
+    const uint64_t pos = __ballot(lp >= 0);
+    return pos ? readlane_i(lp, 63 - __builtin_clzll(pos)) : -1;
+}
+
+// locate_in_chunk for vector u, with u turned into a constant (registers are
+// not indexable).
+template <bool BF16, bool D, int U>
+__device__ __forceinline__ int locate_dispatch(int u, const SliceCtx& x, const u32x4 (&rt)[kSliceVecs], float c,
+                                               const RowStats& st, const Shift& k, double pre, double thr) {
+    if constexpr (U + 1 == kSliceVecs) {
+        return locate_in_chunk<BF16, D, U>(x, rt, c, st, k, pre, thr);
+    } else {
+        return u == U ? locate_in_chunk<BF16, D, U>(x, rt, c, st, k, pre, thr)
+                      : locate_dispatch<BF16, D, U + 1>(u, x, rt, c, st, k, pre, thr);
+    }
+}
+
+// Offset in the slice of the drawn id: the first element with positive
+// weight whose cumulative weight (from the slice start) exceeds thr; if
+// rounding leaves none, the last positive-weight element of the chunk the
+// chunk totals point to (or of the slice, when thr is beyond them all).
+// Only the wavefront holding that chunk returns it (in every lane); the
+// others return -2.
+template <bool BF16, bool D>
+__device__ int locate_in_slice(const SliceCtx& x, const u32x4 (&rt)[kSliceVecs], float c, const RowStats& st,
+                               const Shift& k, const double* chunk, double thr) {
+    const int wave = threadIdx.x / kWave;
+    double cum = 0.0, pre = 0.0;
+    int qs = -1, qlast = -1;
+    for (int q = 0; q < kChunks; ++q) {
+        const double v = chunk[q];
+        if (v > 0.0) {
+            qlast = q;
+            if (qs < 0 && cum + v > thr) {
+                qs = q;
+                pre = cum;
+            }
+        }
+        cum += v;
+    }
+    if (qs < 0) {
+        if (qlast < 0) return wave == 0 ? -1 : -2;
+        qs = qlast;
+        thr = INFINITY;
+    }
+    if (wave != qs % kSliceWaves) return -2;
+    return locate_dispatch<BF16, D, 0>(qs / kSliceWaves, x, rt, c, st, k, pre, thr);
+}
+
+// Logit i of a row, the same for every lane, through the scalar unit: the
+// aligned 32-bit word holding it, then its half for bf16 (a bf16 row may
+// start at any even address, so the half follows from the address).
+template <bool BF16>
+__device__ __forceinline__ float uniform_logit(const char* row, int i) {
+    if (BF16) {
+        const uintptr_t a = (uintptr_t)row + (uintptr_t)i * 2;
+        const uint32_t w = __builtin_amdgcn_readfirstlane(*(const uint32_t*)(a & ~(uintptr_t)3));
+        return (a & 2) ? bf16_hi(w) : bf16_lo(w);
+    }
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(*(const uint32_t*)(row + (size_t)i * 4)));
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void accept_logits_sliced_kernel(
-    const void* __restrict__ zt, const void* __restrict__ zd, int K, int V, int G, int Ls, int m, int nseg_max, float c,
+__global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
+    const void* __restrict__ zt, const void* __restrict__ zd, int K, int V, int G, int Ls, float c,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens, const float* __restrict__ uniforms,
     int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token, unsigned long long* __restrict__ slots,
     int wait_limit) {
-    extern __shared__ double seg[];  // 2 * nseg_max: this slice's table, then a scratch table
     __shared__ StatsLds lds;
+    __shared__ u32x4 s_draft[kSliceVecs * kSliceThreads];
+    __shared__ double chunk[kChunks];
     __shared__ unsigned long long s_words[2 * kMaxSlices];
     __shared__ double s_tot[kMaxSlices];
     __shared__ int s_ready;
-    using L = Logit4<BF16>;
-    constexpr int kElem = BF16 ? 2 : 4;
     const int b = blockIdx.x / G, g = blockIdx.x - b * G;
     const int kb = clamp_len(lens, b, K);
-    const size_t row_bytes = (size_t)V * kElem;
+    const size_t row_bytes = (size_t)V * (BF16 ? 2 : 4);
     const char* tbase = (const char*)zt + (size_t)b * (size_t)(K + 1) * row_bytes;
     const char* dbase = (const char*)zd + (size_t)b * (size_t)K * row_bytes;
-    const int64_t x0 = (int64_t)g * Ls;
-    const int len = (int)min((int64_t)Ls, (int64_t)V - x0);
-    unsigned long long* my = slots + (size_t)b * (size_t)((K + 1) * 2 * G + 2 * G);
-    unsigned long long* draw_sets = my + (size_t)(K + 1) * 2 * G;
+    const SliceCtx x{s_words, &s_ready, s_draft, G, g, Ls, V, wait_limit};
+    // per sequence: 2G words of draw totals (the residual's or the bonus's,
+    // then the zero-residual fallback's), then 2G words per position
+    unsigned long long* my = slots + (size_t)b * (size_t)(2 * G) * (size_t)(K + 2);
+    unsigned long long* draw_sets = my;
+    unsigned long long* pos_sets = my + 2 * G;
 
     // 1. positions in order; stop at the first rejection
-    int n = kb;
-    bool have = false;
+    u32x4 rt[kSliceVecs];
     RowStats st{0.f, 0.0}, sd{0.f, 0.0};
-    for (int i = 0; i < kb; ++i) {
-        const int t = tokens[(int64_t)b * K + i];
-        if (t < 0 || t >= V) {  // out-of-range draft token: rejected, never dereferenced
-            n = i;
-            break;
-        }
-        const void* tr = tbase + (size_t)i * row_bytes;
-        const void* dr = dbase + (size_t)i * row_bytes;
-        sliced_row_stats<BF16, VEC, true>(my + (size_t)i * 2 * G, G, g, Ls, V, tr, dr, c, &lds, wait_limit, s_words,
-                                          &s_ready, st, sd);
-        if (!accepts(L::at(tr, t), L::at(dr, t), c, st, sd, uniforms[(int64_t)b * (K + 1) + i])) {
-            n = i;
-            have = true;
+    int n = 0;
+    bool residual = false;
+    for (; n < kb; ++n) {
+        const char* tr = tbase + (size_t)n * row_bytes;
+        const char* dr = dbase + (size_t)n * row_bytes;
+        const int t = tokens[(int64_t)b * K + n];
+        const bool valid = t >= 0 && t < V;  // an out-of-range draft token is rejected, never dereferenced
+        const float zt_t = uniform_logit<BF16>(tr, valid ? t : 0), zd_t = uniform_logit<BF16>(dr, valid ? t : 0);
+        position_stats<BF16, VEC, true>(x, pos_sets + (size_t)n * 2 * G, tr, dr, c, rt, &lds, st, sd);
+        if (!valid || !accepts(zt_t, zd_t, c, st, sd, uniforms[(int64_t)b * (K + 1) + n])) {
+            residual = true;
             break;
         }
     }
+    const char* trow = tbase + (size_t)n * row_bytes;  // n == kb: the bonus row
+    const char* drow = dbase + (size_t)n * row_bytes;  // read only for a residual
+    if (!residual)
+        position_stats<BF16, VEC, false>(x, pos_sets + (size_t)kb * 2 * G, trow, nullptr, c, rt, &lds, st, sd);
 
-    // 2-3. the draw, slice by slice
-    const bool residual = n < kb;
-    const int pos = residual ? n : kb;
-    const char* zt_row = tbase + (size_t)pos * row_bytes;
-    const char* zd_row = residual ? dbase + (size_t)n * row_bytes : nullptr;
-    if (!(residual && have)) {
-        if (residual)
-            sliced_row_stats<BF16, VEC, true>(my + (size_t)pos * 2 * G, G, g, Ls, V, zt_row, zd_row, c, &lds,
-                                              wait_limit, s_words, &s_ready, st, sd);
-        else
-            sliced_row_stats<BF16, VEC, false>(my + (size_t)pos * 2 * G, G, g, Ls, V, zt_row, nullptr, c, &lds,
-                                               wait_limit, s_words, &s_ready, st, sd);
-    }
-    using Res = LogitSource<BF16, VEC, true>;
-    using Bon = LogitSource<BF16, VEC, false>;
-    auto slice_len = [&](int k) { return (int)min((int64_t)Ls, (int64_t)V - (int64_t)k * Ls); };
+    // 2. total draw weight over the slices
     const Shift k0 = residual ? residual_shift(st, sd) : Shift{0.f, 0.f};
-    auto make_res = [&](int k) {
-        return Res{zt_row + (size_t)k * Ls * kElem, zd_row + (size_t)k * Ls * kElem, slice_len(k), c, st, sd, k0};
-    };
-    auto make_bon = [&](int k) {
-        return Bon{zt_row + (size_t)k * Ls * kElem, nullptr, slice_len(k), c, st, sd, Shift{0.f, 0.f}};
-    };
-    bool use_bon = !residual;
-    if (residual)
-        sliced_totals<Res>(draw_sets, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot, make_res);
-    else
-        sliced_totals<Bon>(draw_sets, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot, make_bon);
-    double S = 0.0;
-    for (int k = 0; k < G; ++k) S += s_tot[k];
+    bool bonus = !residual;
+    double S = residual ? exchange_totals<BF16, VEC, true>(x, draw_sets, trow, drow, c, st, k0, rt, chunk, s_tot)
+                        : exchange_totals<BF16, VEC, false>(x, draw_sets, trow, nullptr, c, st, k0, rt, chunk, s_tot);
     if (residual && !(S > 0.0)) {
         // p_n == q_n: no residual mass, draw from max(0, p_n)
-        use_bon = true;
-        sliced_totals<Bon>(draw_sets + G, G, g, m, nseg_max, Ls, V, seg, wait_limit, s_words, &s_ready, s_tot,
-                           make_bon);
-        S = 0.0;
-        for (int k = 0; k < G; ++k) S += s_tot[k];
+        bonus = true;
+        S = exchange_totals<BF16, VEC, false>(x, draw_sets + G, trow, nullptr, c, st, k0, rt, chunk, s_tot);
     }
     if (g == 0 && threadIdx.x == 0) {
         n_accepted[b] = n;
         if (!(S > 0.0)) next_token[b] = -1;
     }
     if (!(S > 0.0)) return;
-    // the slice holding u * S: the first with positive total whose running sum
-    // exceeds it; if rounding leaves none, the last with positive total
+
+    // 3. the slice holding u * S: the first with positive total whose running
+    // sum exceeds it; if rounding leaves none, the last with positive total.
+    // That slice locates the id in its copies.
     const double thr = (double)uniforms[(int64_t)b * (K + 1) + kb] * S;
     int ks = -1, klast = -1;
     double pre = 0.0, pre_ks = 0.0;
@@ -884,10 +1213,10 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
     }
     const double thr_local = ks < 0 ? INFINITY : thr - pre_ks;
     if (ks < 0) ks = klast;
-    if (g != ks || threadIdx.x >= kWave) return;
-    const int nseg = (len + (int)((int64_t)m * kSub) - 1) / (int)((int64_t)m * kSub);
-    const int x = use_bon ? locate(make_bon(g), m, nseg, seg, thr_local) : locate(make_res(g), m, nseg, seg, thr_local);
-    if (threadIdx.x == 0) next_token[b] = x < 0 ? -1 : (int)(x0 + x);
+    if (g != ks) return;
+    const int xi = bonus ? locate_in_slice<BF16, false>(x, rt, c, st, k0, chunk, thr_local)
+                         : locate_in_slice<BF16, true>(x, rt, c, st, k0, chunk, thr_local);
+    if (xi != -2 && (threadIdx.x & (kWave - 1)) == 0) next_token[b] = xi < 0 ? -1 : (int)((int64_t)g * Ls + xi);
 }
 
 __global__ void fill_empty(unsigned long long* __restrict__ p, int64_t n) {
@@ -921,35 +1250,34 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
     return hipGetLastError();
 }
 
-// Slices of the sliced verify kernels: at most 8, B * G <= 4096 workgroups of
-// 256 lanes (twice what the chip holds at once; the dispatch order keeps a
-// sequence's slices together), each slice at least 32768 elements (shorter
-// slices spend more on the exchanges than they save); Ls is a multiple of 1024
-// elements and every slice is non-empty. Measured on MI355X at B = 512,
-// K = 16, V = 256000 for the fused sampled verify: G = 8 about 8% faster than
-// G = 4 and 27% faster than G = 2.
-void coop_slice_shape(int B, int V, int& G, int& Ls) {
-    int g = 4096 / (B > 0 ? B : 1);
-    g = g < 1 ? 1 : (g > kMaxSlices ? kMaxSlices : g);
-    const int gv = (int)(((int64_t)V + 32767) / 32768);  // V may be INT32_MAX
-    g = g < gv ? g : (gv > 1 ? gv : 1);
-    int64_t ls = ((int64_t)V + g - 1) / g;
-    ls = (ls + 1023) / 1024 * 1024;
-    G = (int)(((int64_t)V + ls - 1) / ls);
-    Ls = (int)ls;
-}
-
 hipError_t launch_fill_empty(unsigned long long* slots, int64_t words, hipStream_t stream) {
     if (words <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_empty, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, slots, words);
     return hipGetLastError();
 }
 
+// Slices of the split fused verify: 256 lanes x kSliceVecs vectors x E
+// elements (12288 bf16 or 6144 fp32 logits) each, G = ceil(V / Ls) of them.
+// 0 when the rows are not split: rows of at most one slice, or of more than
+// kMaxSlices slices (one workgroup per sequence reads those).
+int fused_slices(int V, bool bf16, int& Ls) {
+    Ls = kSliceThreads * kSliceVecs * (bf16 ? 8 : 4);
+    const int64_t G = ((int64_t)V + Ls - 1) / Ls;
+    return (G >= 2 && G <= kMaxSlices) ? (int)G : 0;
+}
+
+// B sequences x (K + 2) x 2G exchange words: 2G per position, 2G for the draw.
+size_t fused_dtype_workspace_bytes(int B, int K, int V, bool bf16) {
+    int Ls;
+    const int G = fused_slices(V, bf16, Ls);
+    if (G == 0 || (int64_t)B * G > INT32_MAX) return 0;  // the grid is B * G workgroups
+    return (size_t)B * 2 * (size_t)G * (size_t)(K + 2) * sizeof(unsigned long long);
+}
+
+// The larger of the two dtypes' needs, so that one size serves either.
 size_t accept_logits_workspace_bytes(int B, int K, int V) {
-    int G, Ls;
-    coop_slice_shape(B, V, G, Ls);
-    if (G < 2) return 0;
-    return (size_t)B * ((size_t)(K + 1) * 2 * G + 2 * (size_t)G) * sizeof(unsigned long long);
+    const size_t a = fused_dtype_workspace_bytes(B, K, V, false), b = fused_dtype_workspace_bytes(B, K, V, true);
+    return a > b ? a : b;
 }
 
 hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
@@ -959,32 +1287,31 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
     const float c = 1.4426950408889634f / temperature;
     const uintptr_t al = bf16 ? 8 : 16;
     const bool vec = (V % 4 == 0) && ((uintptr_t)zt % al == 0) && ((uintptr_t)zd % al == 0);
-    const size_t need = accept_logits_workspace_bytes(B, K, V);
+    const size_t need = fused_dtype_workspace_bytes(B, K, V, bf16);
     if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
-        int G, Ls, m, nseg;
-        coop_slice_shape(B, V, G, Ls);
-        segment_shape(Ls, m, nseg);
+        int Ls;
+        const int G = fused_slices(V, bf16, Ls);
+        const bool vec16 = (V % (bf16 ? 8 : 4) == 0) && ((uintptr_t)zt % 16 == 0) && ((uintptr_t)zd % 16 == 0);
         const int64_t words = (int64_t)(need / sizeof(unsigned long long));
         unsigned long long* slots = (unsigned long long*)workspace;
         const hipError_t fe = launch_fill_empty(slots, words, stream);
         if (fe != hipSuccess) return fe;  // without the fill, stale slots would read as published
-        const size_t lds = 2 * (size_t)nseg * sizeof(double);
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
         const int wl = get_wait_limit();
         if (bf16) {
-            if (vec)
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, true>), grid, block, lds, stream, zt, zd, K, V, G,
-                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+            if (vec16)
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, true>), grid, block, 0, stream, zt, zd, K, V, G,
+                                   Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
             else
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, false>), grid, block, lds, stream, zt, zd, K, V, G,
-                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, false>), grid, block, 0, stream, zt, zd, K, V, G,
+                                   Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
         } else {
-            if (vec)
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, true>), grid, block, lds, stream, zt, zd, K, V, G,
-                                   Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+            if (vec16)
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, true>), grid, block, 0, stream, zt, zd, K, V,
+                                   G, Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
             else
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, false>), grid, block, lds, stream, zt, zd, K, V,
-                                   G, Ls, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, false>), grid, block, 0, stream, zt, zd, K, V,
+                                   G, Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
         }
         return hipGetLastError();
     }

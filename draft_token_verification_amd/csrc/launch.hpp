@@ -33,12 +33,6 @@ hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B
 // 0 when one workgroup per sequence is used regardless (short rows).
 size_t accept_logits_workspace_bytes(int B, int K, int V);
 
-// How the verify kernels split a sequence's rows over workgroups: G slices of
-// Ls elements (Ls a multiple of 1024, G <= kMaxCoopSlices, B * G <= 4096 where
-// possible).
-constexpr int kMaxCoopSlices = 8;
-void coop_slice_shape(int B, int V, int& G, int& Ls);
-
 // Fill `words` exchange slots with the empty marker, on `stream`.
 hipError_t launch_fill_empty(unsigned long long* slots, int64_t words, hipStream_t stream);
 

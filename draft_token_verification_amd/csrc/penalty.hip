@@ -21,7 +21,8 @@
 //     (id, count) pairs. The table is cleared by the same workgroup first,
 //     so the workspace needs no preparation.
 //  2. penalty_rows_kernel, one 1024-lane workgroup per live row: the row is
-//     streamed to fp32 (16-byte loads and stores), then only the history's
+//     streamed to fp32 (16-byte loads and stores, four loads in flight per
+//     lane), then only the history's
 //     ids are patched: each listed id with its count plus its occurrences in
 //     the row's draft prefix, and each prefix id absent from the committed
 //     history (once, at its first occurrence in the prefix). A row reads and
@@ -34,6 +35,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kMaxPrefix = kWave;  // draft prefixes are at most SV_MAX_K = 64 tokens
+constexpr int kCopyUnroll = 4;     // loads in flight per lane in the row copy
 
 // Table slot of an id: a multiplicative hash, then linear probing.
 __device__ __forceinline__ uint32_t slot_of(int32_t id, uint32_t mask) {
@@ -134,13 +136,12 @@ __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
         return BF16 ? bf16_at((const uint16_t*)zrow, x) : ((const float*)zrow)[x];
     };
 
-    // 1. the row in fp32
+    // 1. the row in fp32, kCopyUnroll 16-byte loads in flight per lane
     if (VEC) {
         constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte load
         const u32x4* vin = (const u32x4*)zrow;
         const int nv = V / E;
-        for (int j = tid; j < nv; j += kThreads) {
-            const u32x4 w = vin[j];
+        auto put = [&](int j, const u32x4& w) {
             f32x4* o = (f32x4*)(orow + (size_t)j * E);
             if (BF16) {
                 store_nt(o, f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])});
@@ -149,7 +150,16 @@ __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
                 store_nt(o, f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
                                   __uint_as_float(w[3])});
             }
+        };
+        int j = tid;
+        for (; j + (kCopyUnroll - 1) * kThreads < nv; j += kCopyUnroll * kThreads) {
+            u32x4 w[kCopyUnroll];
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) w[u] = vin[j + u * kThreads];
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) put(j + u * kThreads, w[u]);
         }
+        for (; j < nv; j += kThreads) put(j, vin[j]);
     } else {
         for (int x = tid; x < V; x += kThreads) orow[x] = at(x);
     }

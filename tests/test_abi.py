@@ -236,13 +236,18 @@ def test_commit_rejects_bad_arguments(sv, args, fragment):
 
 
 def test_accept_logits_workspace_size(sv):
-    # B * ((K + 1) * 2 * G + 2 * G) 8-byte slots; G = 8 slices for B = 512 at V = 256000
-    assert sv.sv_accept_logits_workspace_bytes(512, 16, 256000) == 512 * (17 * 2 * 8 + 2 * 8) * 8
-    assert sv.sv_accept_logits_workspace_bytes(1, 4, 256000) == 1 * (5 * 2 * 8 + 2 * 8) * 8
-    assert sv.sv_accept_logits_workspace_bytes(64, 4, 70000) == 64 * (5 * 2 * 3 + 2 * 3) * 8
-    assert sv.sv_accept_logits_workspace_bytes(1024, 7, 152064) == 1024 * (8 * 2 * 4 + 2 * 4) * 8
-    assert sv.sv_accept_logits_workspace_bytes(64, 4, 32768) == 0     # short rows: one workgroup per sequence
-    assert sv.sv_accept_logits_workspace_bytes(4096, 4, 256000) == 0  # more sequences than slices fit
+    # B * (K + 2) * 2G 8-byte slots: 2G words per position and 2G for the draw, with G = ceil(V / Ls)
+    # slices of Ls = 6144 fp32 or 12288 bf16 logits (the larger need of the two dtypes), 2 <= G <= 64
+    w = lambda B, K, G: B * (K + 2) * 2 * G * 8
+    assert sv.sv_accept_logits_workspace_bytes(512, 16, 256000) == w(512, 16, 42)
+    assert sv.sv_accept_logits_workspace_bytes(1, 4, 256000) == w(1, 4, 42)
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 70000) == w(64, 4, 12)
+    assert sv.sv_accept_logits_workspace_bytes(1024, 7, 152064) == w(1024, 7, 25)
+    assert sv.sv_accept_logits_workspace_bytes(4096, 4, 256000) == w(4096, 4, 42)
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 8192) == w(64, 4, 2)
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 600000) == w(64, 4, 49)  # fp32 rows unsplit, bf16 in 49
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 6144) == 0     # one slice: one workgroup per sequence
+    assert sv.sv_accept_logits_workspace_bytes(64, 4, 64 * 12288 + 1) == 0  # more than 64 slices of either dtype
     assert sv.sv_accept_logits_workspace_bytes(0, 4, 256000) == 0
 
 

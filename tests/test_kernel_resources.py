@@ -9,6 +9,13 @@ looking source change can silently break:
   - 8 wavefronts per SIMD: the 1024-lane workgroups (warp rows, filtered warp,
     greedy, accept) fit two to a compute unit only at <= 64 VGPRs; at 65 half
     the workgroups wait (the filtered warp measured 25% slower that way).
+    One kernel is exempt, with a floor of its own: the split fused sampled
+    verify keeps each lane's share of the target row in registers through
+    its exchanges and is bound by arithmetic, not by memory; forced to 64
+    VGPRs it spills and ran 3.8x slower on MI355X, at its natural ~110 VGPRs
+    (4 waves per SIMD) it is fastest. Its element-by-element variant (rows
+    whose length or alignment rules out 16-byte loads) is exempt from the
+    floor as well: it is correct but not tuned.
 """
 import json
 import os
@@ -54,9 +61,25 @@ def test_no_scratch(res):
     assert not bad, f"kernels using private memory (spills, local arrays or out-of-line calls): {bad}"
 
 
+FLOOR = {"accept_logits_sliced_kernel": 4}  # waves per SIMD, for the 16-byte-load variants
+
+
+def vector_variant(mangled):
+    """True for the <BF16, VEC = true> instantiations (the second template argument)."""
+    m = re.search(r"ILb[01]ELb([01])E", mangled)
+    return m is None or m.group(1) == "1"
+
+
 def test_full_occupancy(res):
-    low = {short(k): (v["vgprs"], v["occupancy"]) for k, v in res.items() if v.get("occupancy", 0) < 8}
-    assert not low, f"kernels below 8 waves per SIMD (vgprs, waves): {low}"
+    low = {}
+    for k, v in res.items():
+        name = short(k)
+        if name in FLOOR:
+            if vector_variant(k) and v.get("occupancy", 0) < FLOOR[name]:
+                low[name] = (v["vgprs"], v["occupancy"])
+        elif v.get("occupancy", 0) < 8:
+            low[name] = (v["vgprs"], v["occupancy"])
+    assert not low, f"kernels below their waves per SIMD (vgprs, waves): {low}"
 
 
 def test_filter_fits_two_workgroups_per_cu(res):
