@@ -20,13 +20,21 @@
 //     history buffer, so probing ends), then compacted into a list of
 //     (id, count) pairs. The table is cleared by the same workgroup first,
 //     so the workspace needs no preparation.
-//  2. penalty_rows_kernel, one 1024-lane workgroup per live row: the row is
-//     streamed to fp32 (16-byte loads and stores, four loads in flight per
-//     lane), then only the history's
-//     ids are patched: each listed id with its count plus its occurrences in
-//     the row's draft prefix, and each prefix id absent from the committed
-//     history (once, at its first occurrence in the prefix). A row reads and
-//     writes V elements plus O(history) scattered ones.
+//  2. penalty_rows_kernel: each live row in slices of 32768 ids, one 1024-lane
+//     workgroup per slice (as the warp's split path). A workgroup issues all
+//     of its loads at once (32 ids per lane, 4 per load, so each lane's output
+//     is one 16-byte store and a wave's stores are contiguous), marks in an LDS bitmap
+//     the ids of the row's history (the committed list and the row's draft
+//     prefix) that fall in its slice while they are in flight, with each
+//     committed id's count in LDS (a byte; 255 and above are looked up in
+//     the table), then writes each vector in fp32, patching in registers
+//     those that hold marked ids (count = committed count + prefix
+//     occurrences). A row is read once and written once. Rows whose length
+//     (V not a multiple of 4) or alignment rules out vector access are copied
+//     element by element by one workgroup and patched afterwards with
+//     scattered stores.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,7 +43,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kMaxPrefix = kWave;  // draft prefixes are at most SV_MAX_K = 64 tokens
-constexpr int kCopyUnroll = 4;     // loads in flight per lane in the row copy
+constexpr int kSlice = kThreads * 32;  // ids per workgroup in the 16-byte path: 32 per lane, loaded at once
 
 // Table slot of an id: a multiplicative hash, then linear probing.
 __device__ __forceinline__ uint32_t slot_of(int32_t id, uint32_t mask) {
@@ -120,11 +128,15 @@ __device__ __forceinline__ int table_count(const TableView& t, int32_t id, uint3
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
-    const void* __restrict__ logits, int R, int V, const int32_t* __restrict__ lens, int extra_rows, bool have_hist,
-    int P, const void* __restrict__ ws, const int32_t* __restrict__ tokens, int K, const float* __restrict__ theta,
-    const float* __restrict__ presence, const float* __restrict__ frequency, float* __restrict__ out) {
+    const void* __restrict__ logits, int R, int V, int G, const int32_t* __restrict__ lens, int extra_rows,
+    bool have_hist, int P, const void* __restrict__ ws, const int32_t* __restrict__ tokens, int K,
+    const float* __restrict__ theta, const float* __restrict__ presence, const float* __restrict__ frequency,
+    float* __restrict__ out) {
     __shared__ int32_t s_pre[kMaxPrefix];
-    const int row = blockIdx.x;
+    __shared__ uint32_t s_mark[kSlice / 32];   // VEC: committed ids of the slice, one bit each
+    __shared__ uint32_t s_pmark[kSlice / 32];  // VEC: draft-prefix ids of the slice
+    __shared__ uint8_t s_cnt[kSlice];          // VEC: committed count of each marked id (255: look it up)
+    const int row = blockIdx.x / G, g = blockIdx.x - row * G;
     const int b = row / R, r = row - b * R;
     const int live = clamp_len(lens, b, R - extra_rows) + extra_rows;
     if (r >= live) return;
@@ -135,39 +147,9 @@ __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
     auto at = [&](int64_t x) {
         return BF16 ? bf16_at((const uint16_t*)zrow, x) : ((const float*)zrow)[x];
     };
-
-    // 1. the row in fp32, kCopyUnroll 16-byte loads in flight per lane
-    if (VEC) {
-        constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte load
-        const u32x4* vin = (const u32x4*)zrow;
-        const int nv = V / E;
-        auto put = [&](int j, const u32x4& w) {
-            f32x4* o = (f32x4*)(orow + (size_t)j * E);
-            if (BF16) {
-                store_nt(o, f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])});
-                store_nt(o + 1, f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])});
-            } else {
-                store_nt(o, f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
-                                  __uint_as_float(w[3])});
-            }
-        };
-        int j = tid;
-        for (; j + (kCopyUnroll - 1) * kThreads < nv; j += kCopyUnroll * kThreads) {
-            u32x4 w[kCopyUnroll];
-#pragma unroll
-            for (int u = 0; u < kCopyUnroll; ++u) w[u] = vin[j + u * kThreads];
-#pragma unroll
-            for (int u = 0; u < kCopyUnroll; ++u) put(j + u * kThreads, w[u]);
-        }
-        for (; j < nv; j += kThreads) put(j, vin[j]);
-    } else {
-        for (int x = tid; x < V; x += kThreads) orow[x] = at(x);
-    }
     // the draft prefix of this row: tokens[b, 0 .. r-1]
     const int np = tokens ? r : 0;
     if (tid < np) s_pre[tid] = tokens[(size_t)b * K + tid];
-    __syncthreads();  // the copy's stores are complete before any patch overwrites one
-
     const float th = theta ? theta[b] : 1.0f;
     const float pr = presence ? presence[b] : 0.0f;
     const float fr = frequency ? frequency[b] : 0.0f;
@@ -177,9 +159,81 @@ __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
         return c;
     };
     const uint32_t mask = (uint32_t)P - 1u;
-    // 2. ids of the committed history, with their prefix occurrences added
+    const TableView t = table_of(const_cast<void*>(ws), b, P);
+
+    if (VEC) {
+        // slice g of the row: kSlice ids, 4 per load (8 bytes of bf16 or 16 of
+        // fp32) so that each lane's output is one 16-byte store and a wave's
+        // stores are contiguous; all loads issued first, the marking below
+        // runs while they are in flight
+        constexpr int E = 4;
+        constexpr int kVecs = kSlice / kThreads / E;
+        const int x0 = g * kSlice;
+        const int nv = (min(kSlice, V - x0)) / E;  // vectors in the slice
+        using Raw = typename std::conditional<BF16, u32x2, u32x4>::type;
+        const Raw* vin = (const Raw*)(zrow + (size_t)x0 * es);
+        Raw w[kVecs];
+#pragma unroll
+        for (int u = 0; u < kVecs; ++u) w[u] = __builtin_nontemporal_load(vin + min(u * kThreads + tid, nv - 1));
+        // 1. mark the history ids that fall in the slice: the committed ones
+        // with their counts (each id is listed once), then the prefix's
+        s_mark[tid] = 0u;
+        s_pmark[tid] = 0u;
+        __syncthreads();
+        if (have_hist) {
+            const int n = *t.n;
+            for (int k = tid; k < n; k += kThreads) {
+                const int o = t.list[2 * k] - x0;
+                if (o >= 0 && o < kSlice) {
+                    atomicOr(&s_mark[o >> 5], 1u << (o & 31));
+                    s_cnt[o] = (uint8_t)min(t.list[2 * k + 1], 255);
+                }
+            }
+        }
+        if (tid < np) {
+            const int o = s_pre[tid] - x0;
+            if (o >= 0 && o < kSlice && s_pre[tid] < V) atomicOr(&s_pmark[o >> 5], 1u << (o & 31));
+        }
+        __syncthreads();
+        // 2. each vector in fp32, patched in registers where it holds marked ids
+#pragma unroll
+        for (int u = 0; u < kVecs; ++u) {
+            const int j = u * kThreads + tid;
+            if (j >= nv) continue;
+            float z[4];
+            if constexpr (BF16) {
+                z[0] = bf16_lo(w[u][0]);
+                z[1] = bf16_hi(w[u][0]);
+                z[2] = bf16_lo(w[u][1]);
+                z[3] = bf16_hi(w[u][1]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) z[k] = __uint_as_float(w[u][k]);
+            }
+            const int o = j * E;
+            const uint32_t cb = (s_mark[o >> 5] >> (o & 31)) & 0xFu, pb = (s_pmark[o >> 5] >> (o & 31)) & 0xFu;
+            if (cb | pb) {  // rare: ids of the history
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    int c = 0;
+                    if (cb & (1u << e)) {
+                        c = s_cnt[o + e];
+                        if (c == 255) c = table_count(t, x0 + o + e, mask);
+                    }
+                    if (pb & (1u << e)) c += prefix_count(x0 + o + e, np);
+                    if (c > 0) z[e] = penalised(z[e], c, th, pr, fr);
+                }
+            }
+            store_nt((f32x4*)(orow + (size_t)(x0 + o)), f32x4{z[0], z[1], z[2], z[3]});
+        }
+        return;
+    }
+
+    // element by element: the row in fp32, then the history's ids patched
+    for (int x = tid; x < V; x += kThreads) orow[x] = at(x);
+    __syncthreads();  // the prefix is in LDS and the copy's stores are complete before any patch overwrites one
+    // ids of the committed history, with their prefix occurrences added
     if (have_hist) {
-        const TableView t = table_of(const_cast<void*>(ws), b, P);
         const int n = *t.n;
         for (int k = tid; k < n; k += kThreads) {
             const int32_t id = t.list[2 * k];
@@ -187,11 +241,11 @@ __global__ __launch_bounds__(kThreads) void penalty_rows_kernel(
             orow[id] = penalised(at(id), c, th, pr, fr);
         }
     }
-    // 3. ids that only the prefix holds, patched once (at their first occurrence)
+    // ids that only the prefix holds, patched once (at their first occurrence)
     if (tid < np) {
         const int32_t id = s_pre[tid];
         if (id >= 0 && id < V && prefix_count(id, tid) == 0) {
-            const bool committed = have_hist && table_count(table_of(const_cast<void*>(ws), b, P), id, mask) > 0;
+            const bool committed = have_hist && table_count(t, id, mask) > 0;
             if (!committed) orow[id] = penalised(at(id), prefix_count(id, np), th, pr, fr);
         }
     }
@@ -225,21 +279,25 @@ hipError_t launch_penalties(const void* logits, bool bf16, int B, int R, int V, 
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const bool vec = (V % (bf16 ? 8 : 4) == 0) && ((uintptr_t)logits % 16 == 0) && ((uintptr_t)out % 16 == 0);
-    const dim3 grid((unsigned)((int64_t)B * R));
+    const int64_t rows = (int64_t)B * R;
+    const int64_t G = ((int64_t)V + kSlice - 1) / kSlice;
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % (bf16 ? 8 : 16) == 0) && ((uintptr_t)out % 16 == 0) &&
+                     rows * G <= INT32_MAX;
+    const int g = vec ? (int)G : 1;
+    const dim3 grid((unsigned)(rows * g));
     if (bf16) {
         if (vec)
-            hipLaunchKernelGGL((penalty_rows_kernel<true, true>), grid, dim3(kThreads), 0, stream, logits, R, V, lens,
-                               extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
-        else
-            hipLaunchKernelGGL((penalty_rows_kernel<true, false>), grid, dim3(kThreads), 0, stream, logits, R, V, lens,
-                               extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((penalty_rows_kernel<false, true>), grid, dim3(kThreads), 0, stream, logits, R, V,
+            hipLaunchKernelGGL((penalty_rows_kernel<true, true>), grid, dim3(kThreads), 0, stream, logits, R, V, g,
                                lens, extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
         else
-            hipLaunchKernelGGL((penalty_rows_kernel<false, false>), grid, dim3(kThreads), 0, stream, logits, R, V,
+            hipLaunchKernelGGL((penalty_rows_kernel<true, false>), grid, dim3(kThreads), 0, stream, logits, R, V, g,
+                               lens, extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((penalty_rows_kernel<false, true>), grid, dim3(kThreads), 0, stream, logits, R, V, g,
+                               lens, extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
+        else
+            hipLaunchKernelGGL((penalty_rows_kernel<false, false>), grid, dim3(kThreads), 0, stream, logits, R, V, g,
                                lens, extra_rows, have_hist, P, workspace, tokens, K, theta, presence, frequency, out);
     }
     return hipGetLastError();

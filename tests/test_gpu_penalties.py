@@ -181,3 +181,21 @@ def test_penalised_verify_round(sv, name):
         zt_h[sl], zd_h[sl], tok_h[sl], u_h[sl], None if lens_h is None else lens_h[sl], T, rel_window=w), B),
         f"{name}: penalties -> warp -> accept")
     print(f"[{name}] penalised greedy mean n {n_o.mean():.2f}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_penalties_counts_beyond_a_byte(sv, dtype):
+    """Committed counts of 255 and more (the streaming path keeps counts below
+    255 in LDS and looks larger ones up in the history table): a history made
+    of three ids repeated, plus a draft prefix repeating one of them."""
+    rng = np.random.default_rng(31)
+    B, K, V, cap = 3, 4, 40000, 1200
+    z = (3 * torch.randn(B, K + 1, V, generator=torch.Generator().manual_seed(8))).to(dtype).cuda()
+    ids = np.array([5, 33333, 20000], np.int32)
+    seq = ids[rng.integers(0, 3, (B, cap))].astype(np.int32)
+    seq[1, :] = 33333                                   # one id 1200 times
+    seq_len = np.array([cap, 700, 256], np.int32)       # counts about 400, 700 and 85
+    toks = np.tile(np.array([33333, 5, 7, 33333], np.int32), (B, 1))
+    theta, pres, freq = params(B, rng)
+    theta[0], pres[0], freq[0] = 1.1, 0.2, 0.001       # sequence 0 penalised too
+    check(sv, z, None, 1, seq, seq_len, toks, theta, pres, freq, f"counts-{dtype}")
