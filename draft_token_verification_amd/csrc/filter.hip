@@ -564,6 +564,64 @@ __device__ __forceinline__ void mark_kept_quads(const uint32_t* key, const bool*
     __syncthreads();
 }
 
+// The k-th largest of the candidate keys held in registers (1 <= k <= their
+// count): the largest t with at least k keys >= t, found digit by digit (8
+// bits, from the top) with block-wide LDS histograms of the keys that match
+// the digits chosen so far. Three histograms rotate: pass p fills number
+// p % 3 and clears the next one, which pass p - 2 used and every lane had
+// read before the barrier of pass p - 1; so a pass needs a single barrier.
+// Every lane gets the result. Contains barriers.
+template <int kPer, int kBits>
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t* key, const bool* valid, int k, FilterLds* L) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    uint32_t* hist[3] = {L->tcnt, (uint32_t*)L->tmass, (uint32_t*)L->tmass + kBins};
+    if (tid < kBins) hist[0][tid] = 0u;
+    __syncthreads();
+    uint32_t prefix = 0u;
+    int above = 0;  // keys whose digits so far exceed the chosen ones
+    int p = 0;
+#pragma unroll
+    for (int shift = kBits - 8; shift >= 0; shift -= 8, ++p) {
+        uint32_t* h = hist[p % 3];
+        // the next pass's histogram: last read two passes ago, by every lane
+        // before it reached the previous pass's barrier
+        if (tid < kBins) hist[(p + 1) % 3][tid] = 0u;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (valid[j] && (shift + 8 >= kBits || (key[j] >> (shift + 8)) == (prefix >> (shift + 8))))
+                atomicAdd(&h[(key[j] >> shift) & (kBins - 1)], 1u);
+        __syncthreads();
+        // lane l holds bins 255 - 4l .. 252 - 4l: the first bin, from the top,
+        // at which the count of keys at or above reaches k
+        uint32_t v[4], run = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = h[kBins - 1 - 4 * lane - i];
+            run += v[i];
+        }
+        uint32_t incl = run;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, d, kWave);
+            if (lane >= d) incl += y;
+        }
+        int c = above + (int)(incl - run), found = -1, cf = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (found < 0 && c + (int)v[i] >= k) {
+                found = i;
+                cf = c;
+            }
+            c += (int)v[i];
+        }
+        const uint64_t ball = __ballot(found >= 0);
+        const int l = __builtin_ctzll(ball);  // never empty: at least k keys match the prefix
+        above = readlane_i(cf, l);
+        prefix |= (uint32_t)(kBins - 1 - 4 * l - readlane_i(found, l)) << shift;
+    }
+    return prefix;
+}
+
 // Thresholds from the nc candidates in cand[] (every key above the gather's
 // cut): tau (smallest kept key) and s_kept (fixed-point mass of the kept
 // ids). Each thread holds up to 4 candidates in registers.
@@ -630,12 +688,7 @@ __device__ __forceinline__ bool select_thresholds(int nc, int V, float c, float 
         return tot;
     };
     uint32_t kth = 0u;
-    if (kon) {
-        for (int bit = kBits - 1; bit >= 0; --bit) {
-            const uint32_t t = kth | (1u << bit);
-            if (count_ge(t) >= k) kth = t;
-        }
-    }
+    if (kon) kth = radix_kth<kPer, kBits>(key, valid, k, L);
     uint32_t* kmap = (uint32_t*)&L->mass[0][0];
     if (!pon) {
         tau = kth;
