@@ -200,7 +200,8 @@ def _f32(x):
 def apply_penalties(logits, lens=None, extra_rows: int = 0, seq=None, seq_len=None, tokens=None, theta=None,
                     presence=None, frequency=None, lib=None):
     """Penalties of the live rows of logits [B, R, V]: row r of sequence b takes the history
-    seq[b, :seq_len[b]] + tokens[b, :r]. Per-sequence theta / presence / frequency [B] (None: off).
+    seq[b, :seq_len[b]] + tokens[b, :r]. Per-sequence theta / presence / frequency: None (off), a
+    number for every sequence, or [B].
     Returns fp32 [B, R, V] with NaN in rows that are not live."""
     a, dt = _array(logits)
     B, R, V = a.shape
@@ -211,9 +212,19 @@ def apply_penalties(logits, lens=None, extra_rows: int = 0, seq=None, seq_len=No
     tk = _i32(tokens)
     cap = 0 if sq is None else sq.shape[1]
     K = 0 if tk is None else tk.shape[1]
+
+    def per_sequence(x, name):  # None, a number for every sequence, or [B]
+        if x is None:
+            return None
+        if np.ndim(x.detach().cpu().numpy() if hasattr(x, "detach") else x) == 0:
+            return np.full(B, float(x), dtype=np.float32)
+        x = _f32(x)
+        if x.shape != (B,):
+            raise ValueError(f"{name} must be a number or [B] = {(B,)}")
+        return x
+    th, pr, fr = (per_sequence(x, n) for x, n in ((theta, "theta"), (presence, "presence"), (frequency, "frequency")))
     (lib or _lib()).or_apply_penalties(_ptr(a), dt, B, R, V, _ptr(ln), int(extra_rows), _ptr(sq), _ptr(sl), cap,
-                                       _ptr(tk), K, _ptr(_f32(theta)), _ptr(_f32(presence)), _ptr(_f32(frequency)),
-                                       _ptr(out))
+                                       _ptr(tk), K, _ptr(th), _ptr(pr), _ptr(fr), _ptr(out))
     return out
 
 

@@ -86,6 +86,7 @@ CASES = [
     ("bf16-aligned", torch.bfloat16, 6, 5, 4096, 40),
     ("fp32-aligned", torch.float32, 6, 5, 4096, 40),
     ("bf16-unaligned", torch.bfloat16, 5, 4, 4099, 17),
+    ("fp32-unaligned", torch.float32, 4, 3, 20011, 30),
     ("fp32-long-history", torch.float32, 3, 3, 50000, 5000),
     ("bf16-k64", torch.bfloat16, 2, 64, 1000, 300),
 ]

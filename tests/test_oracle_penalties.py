@@ -132,3 +132,17 @@ def test_penalised_pipeline_is_the_filtered_warp_of_penalised_rows():
         assert p[hit] < base[hit]
     untouched = [x for x in range(V) if x not in set(hist.tolist())]
     assert (p[untouched] >= base[untouched]).all()
+
+
+def test_apply_penalties_parameters_broadcast():
+    """A number stands for every sequence; an array must be [B]."""
+    rng = np.random.default_rng(9)
+    B, R, V = 3, 2, 40
+    z = rng.standard_normal((B, R, V)).astype(np.float32)
+    seq = rng.integers(0, V, (B, 10)).astype(np.int32)
+    seq_len = np.array([10, 4, 0], np.int32)
+    a = oracle.apply_penalties(z, None, 1, seq, seq_len, None, 1.3, 0.2, 0.1)
+    b = oracle.apply_penalties(z, None, 1, seq, seq_len, None, np.full(B, 1.3), np.full(B, 0.2), np.full(B, 0.1))
+    np.testing.assert_array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle.apply_penalties(z, None, 1, seq, seq_len, None, np.ones(B + 1))
