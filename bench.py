@@ -17,7 +17,9 @@ hbm rounds/s. ``modes`` gives rounds/s per mode (greedy round, sampled round
 through the warps, sampled round fused from logits, the filtered warps and the
 penalty stage), each with its bytes needed (what the method must move) and,
 when rocprofv3 counters of these sources are on file, its bytes read, both as
-GB/s and as fractions of MI355X's 8 TB/s. ``roofline`` is the dominant
+GB/s and as fractions of MI355X's 8 TB/s; the greedy round is also timed at
+look-ahead depths L = 1, 2 and K + 1 (rows read ahead of the decision), with
+the bytes those depths load. ``roofline`` is the dominant
 kernel (the warp) on algorithmic bytes. ``cpu_baseline`` times the fp64 CPU
 oracle on a bounded sample of the same workload with every host thread and
 with one (medians over repeats).
@@ -241,6 +243,18 @@ def main():
     modes_out["greedy"] = mode_record("greedy", *ms["greedy"], needed=greedy_bytes,
                                       read=read_bytes("greedy_sliced_kernel") or read_bytes("greedy_kernel"),
                                       mean_n=round(float(n_g.mean()), 4))
+    if sv.sv_verify_greedy_workspace_bytes(B, K, V) > 0:
+        # the split walk's look-ahead depth L (rows read ahead of the decision): the same results, more
+        # bytes loaded -- (min(K_b, n + L) + 1) rows of each sequence -- and the time they take
+        la = {}
+        try:
+            for depth in (1, 2, K + 1):
+                sv.sv_set_greedy_lookahead(depth)
+                loaded = int(((np.minimum(kb, n_g + depth) + 1) * V * elem).sum()) + 4 * B * K + 8 * B
+                la[str(depth)] = mode_record("greedy", *measure(greedy), needed=greedy_bytes, read=loaded)
+        finally:
+            sv.sv_set_greedy_lookahead()
+        modes_out["greedy"]["lookahead"] = la
     sw_needed = accept_bytes + (warp_bytes_t + warp_bytes_d if logits else 0)
     rd_acc = read_bytes("accept_kernel")
     rd_warp = read_bytes("warp_coop_kernel", 2) if logits else 0

@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime first, so the library binds to the same one
 
 __all__ = ["sv_softmax_warp", "sv_softmax_warp_workspace_bytes", "sv_softmax_warp_noalloc",
-           "SV_NOALLOC_SCRATCH_BYTES", "sv_set_wait_limit", "sv_verify_greedy",
+           "SV_NOALLOC_SCRATCH_BYTES", "sv_set_wait_limit", "sv_set_greedy_lookahead", "SV_GREEDY_LOOKAHEAD",
+           "sv_verify_greedy",
            "sv_verify_greedy_workspace_bytes", "sv_accept",
            "sv_accept_logits", "sv_accept_logits_workspace_bytes", "sv_softmax_warp_filtered", "sv_verify_greedy_margin", "sv_gate_update",
            "sv_gate_choose", "GATE_DEFAULTS", "sv_commit", "SpeculativeDecoder", "sv_apply_penalties",
@@ -93,6 +94,8 @@ def _load():
     lib.sv_softmax_warp_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_set_wait_limit.argtypes = [i32]
     lib.sv_set_wait_limit.restype = c_int
+    lib.sv_set_greedy_lookahead.argtypes = [i32]
+    lib.sv_set_greedy_lookahead.restype = c_int
     lib.sv_softmax_warp.restype = c_int
     lib.sv_verify_greedy.argtypes = [vp, c_int, i32, i32, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sv_verify_greedy_workspace_bytes.argtypes = [i32, i32, i64]
@@ -226,6 +229,15 @@ def sv_set_wait_limit(polls: int, device=None) -> None:
     """Diagnostic: polls before a warp workgroup computes its row's statistics alone (0 forces it)."""
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
         _check("sv_set_wait_limit", _lib.sv_set_wait_limit(int(polls)))
+
+
+SV_GREEDY_LOOKAHEAD = 0
+
+
+def sv_set_greedy_lookahead(rows: int = SV_GREEDY_LOOKAHEAD) -> None:
+    """Rows the split greedy walk reads ahead of its decision, process-wide (0, the default, is the
+    exact walk; K + 1 or more reads every live row). Results never change, only bytes read and time."""
+    _check("sv_set_greedy_lookahead", _lib.sv_set_greedy_lookahead(int(rows)))
 
 
 def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: Optional[torch.Tensor] = None,

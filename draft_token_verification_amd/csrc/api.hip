@@ -133,6 +133,13 @@ sv_status sv_set_wait_limit(int32_t polls) {
     return ok();
 }
 
+sv_status sv_set_greedy_lookahead(int32_t rows) {
+    if (rows < 0 || rows > SV_MAX_K + 1)
+        return fail(SV_ERR_INVALID_ARG, "sv_set_greedy_lookahead: rows = %d outside [0, %d]", rows, SV_MAX_K + 1);
+    sv::set_greedy_lookahead(rows);
+    return ok();
+}
+
 sv_status sv_softmax_warp(const void* logits, int dtype, int32_t B, int32_t R, int64_t V, const int32_t* draft_lens,
                           int32_t extra_rows, float temperature, float* probs, void* workspace, size_t workspace_bytes,
                           void* stream) {

@@ -20,8 +20,11 @@
 //   - wave64 merge with DPP quad permutes and row mirrors, a ds_swizzle and
 //     two scalar lane reads; the 16 wave results meet in LDS and every
 //     wavefront merges them again, so the row's argmax is uniform in all lanes.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
+#include "specverify.h"
 
 namespace sv {
 namespace {
@@ -264,6 +267,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 // instead of one. Every wait is bounded: a workgroup that gives up computes
 // the missing slices itself, so the result is the same either way.
 //
+// Look-ahead (the depth L of the walk): a workgroup may read and scan its
+// slices of rows i+1 .. i+L before it waits for the other slices of row i,
+// so that the wait overlaps the next rows' loads. The scanned results wait
+// in LDS; row r is published only once row r-1 has matched, so a workgroup
+// never publishes a row it does not go on to gather. L = 0 is the exact
+// walk; rows read ahead of a miss are read for nothing, which costs time
+// whenever HBM is saturated. Results are the same for every L: a row is
+// still decided only from all G slices of that row.
+//
 // The workspace needs no fill before a launch: an empty slot is a zero word
 // (a published word never is: it carries index + 1, or a set low bit), and
 // every launch leaves the workspace all zero again. When a workgroup is done
@@ -302,11 +314,12 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
     const void* __restrict__ target, int K, int V, int G, int Ls, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ lens, int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token,
     float* __restrict__ top2_margin, unsigned long long* __restrict__ departed, unsigned long long* __restrict__ slots,
-    int wait_limit) {
+    int wait_limit, int lookahead) {
     __shared__ float lds_v[2][kSliceWaves];
     __shared__ int lds_i[2][kSliceWaves];
     __shared__ float lds_s[M ? 2 : 1][kSliceWaves];
     __shared__ unsigned long long s_words[2 * kMaxGreedySlices];
+    __shared__ unsigned long long s_ahead[SV_MAX_K + 1][M ? 2 : 1];  // this slice's scanned rows, not yet published
     __shared__ int s_ready;
     constexpr int W = M ? 2 : 1;  // words per slice and position
     const int b = blockIdx.x / G, g = blockIdx.x - b * G;
@@ -321,20 +334,34 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
         return ((unsigned long long)__float_as_uint(v) << 32) | (unsigned long long)((uint32_t)i + 1u);
     };
     auto pack2 = [](float s) { return ((unsigned long long)__float_as_uint(s) << 32) | 1ull; };
+    auto slot_set = [&](int r) { return slots + ((size_t)b * (K + 1) + r) * (size_t)(G * W); };
+    // this slice of row r, scanned into s_ahead[r] (thread 0 writes and later reads it)
     int parity = 0;
+    auto scan_row = [&](int r) {
+        float vr, sr = -INFINITY;
+        const int ar = span_argmax<BF16, M, kSliceWaves, M ? kMarginUnroll : kSliceUnroll>(
+            base + (size_t)r * row_bytes, g * Ls, slice_len(g), lds_v, lds_i, lds_s, parity, vr, sr);
+        parity ^= 1;
+        if (threadIdx.x == 0) {
+            s_ahead[r][0] = pack(vr, ar);
+            if (M) s_ahead[r][W - 1] = pack2(sr);
+        }
+    };
     int i = 0;
+    int scanned = 0;  // rows 0 .. scanned-1 of this slice are scanned
     float v, s = -INFINITY;
     int am;
     bool waited_out = false;
     for (;; ++i) {
         const char* row = base + (size_t)i * row_bytes;
-        unsigned long long* set = slots + ((size_t)b * (K + 1) + i) * (size_t)(G * W);
-        s = -INFINITY;
-        am = span_argmax<BF16, M, kSliceWaves, M ? kMarginUnroll : kSliceUnroll>(row, g * Ls, slice_len(g), lds_v, lds_i,
-                                                                                 lds_s, parity, v, s);
-        parity ^= 1;
-        publish_word(set + g * W, pack(v, am));
-        if (M) publish_word(set + g * W + 1, pack2(s));
+        unsigned long long* set = slot_set(i);
+        if (scanned == i) scan_row(scanned++);
+        if (threadIdx.x == 0) {
+            publish_word(set + g * W, s_ahead[i][0]);
+            if (M) publish_word(set + g * W + 1, s_ahead[i][W - 1]);
+        }
+        // rows up to i + L (at most K_b) read while the other slices of row i arrive
+        for (const int last = min(kb, i + lookahead); scanned <= last;) scan_row(scanned++);
         if (!gather_words(set, G * W, wait_limit, s_words, &s_ready, 0ull)) {
             // bounded wait ran out: every slice's result, computed here alike
             // (two vectors per lane in flight: a rare path, kept small)
@@ -377,7 +404,7 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
         next_token[b] = am;
         if (M) top2_margin[b] = v - s;
     }
-    depart(departed + b, slots + (size_t)b * (K + 1) * (size_t)(G * W), (i + 1) * G * W, G, waited_out);
+    depart(departed + b, slot_set(0), (i + 1) * G * W, G, waited_out);
 }
 
 }  // namespace
@@ -412,6 +439,12 @@ size_t greedy_dtype_workspace_bytes(int B, int K, int V, bool bf16) {
     return ((size_t)B + (size_t)B * (size_t)(K + 1) * 2 * (size_t)G) * sizeof(unsigned long long);
 }
 
+namespace {
+std::atomic<int> g_lookahead{SV_GREEDY_LOOKAHEAD};  // rows the split walk reads ahead of its decision
+}  // namespace
+
+void set_greedy_lookahead(int rows) { g_lookahead.store(rows); }
+
 // The larger of the two dtypes' needs (fp32 rows are split into more slices),
 // so that one size serves either.
 size_t greedy_workspace_bytes(int B, int K, int V) { return greedy_dtype_workspace_bytes(B, K, V, false); }
@@ -426,21 +459,21 @@ hipError_t launch_greedy(const void* target, bool bf16, int B, int K, int V, con
         unsigned long long* departed = (unsigned long long*)workspace;  // zero between launches
         unsigned long long* slots = departed + B;
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
-        const int wl = get_wait_limit();
+        const int wl = get_wait_limit(), la = g_lookahead.load();
         if (top2_margin) {
             if (bf16)
                 hipLaunchKernelGGL((greedy_sliced_kernel<true, true>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl, la);
             else
                 hipLaunchKernelGGL((greedy_sliced_kernel<false, true>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl, la);
         } else {
             if (bf16)
                 hipLaunchKernelGGL((greedy_sliced_kernel<true, false>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl, la);
             else
                 hipLaunchKernelGGL((greedy_sliced_kernel<false, false>), grid, block, 0, stream, target, K, V, G, Ls,
-                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl);
+                                   tokens, lens, n_accepted, next_token, top2_margin, departed, slots, wl, la);
         }
         return hipGetLastError();
     }

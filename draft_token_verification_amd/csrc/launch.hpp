@@ -83,4 +83,8 @@ hipError_t static_scratch(void** ptr);
 void set_wait_limit(int tries);
 int get_wait_limit();
 
+// Rows the split greedy verify reads ahead of its decision (applies to
+// launches made after the call, on every device).
+void set_greedy_lookahead(int rows);
+
 }  // namespace sv

@@ -148,6 +148,22 @@ sv_status sv_softmax_warp_noalloc(const void* logits, int dtype, int32_t B, int3
  * SV_ERR_INVALID_ARG for a negative value. */
 sv_status sv_set_wait_limit(int32_t polls);
 
+/* Tuning control, process-wide: the look-ahead depth L of the split greedy
+ * walk (sv_verify_greedy and sv_verify_greedy_margin with a workspace), for
+ * calls made after this one. At position i each workgroup reads its slices
+ * of target rows up to min(K_b, i + L) before it waits for the rest of row
+ * i, so that the wait overlaps the next rows' loads. L = 0 (the default,
+ * SV_GREEDY_LOOKAHEAD) is the walk the method describes: row i+1 is read
+ * only after row i matched (spec-verify card, "Method"; llmstudio blog
+ * "Как работает speculative decoding и MTP при инференсе LLM", section 13).
+ * Rows read ahead of a sequence's first miss are read but not needed;
+ * L >= K + 1 reads every live row. Every L gives the same results; only the
+ * bytes read and the time change. Without a workspace, or for rows of at
+ * most 128 KB (one workgroup per sequence, no exchange), L is not used.
+ * Returns SV_ERR_INVALID_ARG for rows outside [0, SV_MAX_K + 1]. */
+#define SV_GREEDY_LOOKAHEAD 0
+sv_status sv_set_greedy_lookahead(int32_t rows);
+
 /*
  * sv_softmax_warp_filtered -- the sampler pipeline temperature -> top-k ->
  * top-p -> renormalise (llmstudio blog "Как работает speculative decoding и
@@ -266,7 +282,8 @@ size_t sv_apply_penalties_workspace_bytes(int32_t B, int32_t cap);
  *              sequence's rows are split over workgroups (one 32 KB slice of
  *              each row per workgroup, up to 64) that exchange partial
  *              argmaxes, so a long chain of matches is read by many compute
- *              units; NULL or 0 bytes selects one workgroup per sequence
+ *              units (see sv_set_greedy_lookahead for how far ahead of its
+ *              decision each reads); NULL or 0 bytes selects one workgroup per sequence
  *              (fewer bytes than the query returns is SV_ERR_WORKSPACE). The
  *              results are identical either way.
  * Result: n_accepted[b] in [0, K_b], next_token[b] in [0, V); bit-exact.

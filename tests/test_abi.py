@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                                     "sv_apply_penalties", "sv_apply_penalties_workspace_bytes",
                                     "sv_commit", "sv_gate_choose",
                                     "sv_gate_update",
-                                    "sv_last_error", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
+                                    "sv_last_error", "sv_set_greedy_lookahead", "sv_set_wait_limit", "sv_softmax_warp", "sv_softmax_warp_filtered",
                                     "sv_softmax_warp_noalloc", "sv_softmax_warp_workspace_bytes", "sv_status_string",
                                     "sv_verify_greedy",
                                     "sv_verify_greedy_margin", "sv_verify_greedy_workspace_bytes"]
@@ -142,6 +142,19 @@ def test_warp_workspace_size(sv):
 
 def test_wait_limit_rejects_negative(sv):
     assert sv._lib.sv_set_wait_limit(-1) == 1
+
+
+def test_greedy_lookahead_checks_its_arguments(sv):
+    lib = sv._lib
+    for rows in [-1, 66, 1 << 30]:
+        assert lib.sv_set_greedy_lookahead(rows) == 1, rows
+        assert b"sv_set_greedy_lookahead" in lib.sv_last_error()
+    try:
+        for rows in [0, 1, 65]:
+            assert lib.sv_set_greedy_lookahead(rows) == 0, rows
+    finally:
+        sv.sv_set_greedy_lookahead()
+    assert int(re.search(r"#define SV_GREEDY_LOOKAHEAD (\d+)", open(HEADER).read()).group(1)) == sv.SV_GREEDY_LOOKAHEAD
 
 
 @pytest.mark.parametrize("args,fragment", [

@@ -5,8 +5,9 @@ exchange (value, index) and runner-up partials; without one, one workgroup
 walks the sequence. Both must give the oracle's n_accepted / next_token
 bit-exactly (spec-verify card, "Method"), and the margin variant the same
 top1 - top2 margin. The split path is also run with a zero poll limit, so that
-every workgroup computes the other slices itself instead of waiting: the
-results must not change. Cases put equal maxima in different slices, the
+every workgroup computes the other slices itself instead of waiting, and under
+several look-ahead depths (rows read ahead of the decision: one, two, all):
+the results must not change. Cases put equal maxima in different slices, the
 maximum in the last element of a ragged last slice, -0.0 against +0.0 across
 slices, all -inf rows, rows off the 16-byte grid, out-of-range tokens and
 ragged draft lengths.
@@ -35,13 +36,22 @@ def host(t):
     return None if t is None else t.detach().cpu()
 
 
+# look-ahead depths of the split walk: one and two rows ahead of the decision, and every live row
+LOOKAHEADS = {"ahead1": 1, "ahead2": 2, "full": 65}
+
+
 def paths(sv, target, tokens, lens, margin):
-    """{path: (n, next, margin or None)} for the single, split and split-without-waiting paths."""
+    """{path: (n, next, margin or None)} for the single, split and split-without-waiting paths, and
+    the split path under each look-ahead setting."""
     empty = torch.empty(0, dtype=torch.uint8, device=target.device)
     out = {}
-    for name, ws, polls in (("single", empty, DEFAULT_POLLS), ("split", None, DEFAULT_POLLS),
-                            ("split-nowait", None, 0)):
+    runs = [("single", empty, DEFAULT_POLLS, None), ("split", None, DEFAULT_POLLS, None),
+            ("split-nowait", None, 0, None)]
+    runs += [("split-" + k, None, DEFAULT_POLLS, la) for k, la in LOOKAHEADS.items()]
+    for name, ws, polls, la in runs:
         sv.sv_set_wait_limit(polls)
+        if la is not None:
+            sv.sv_set_greedy_lookahead(la)
         try:
             if margin:
                 n, nx, mg = sv.sv_verify_greedy_margin(target, tokens, lens, workspace=ws)
@@ -50,6 +60,7 @@ def paths(sv, target, tokens, lens, margin):
             torch.cuda.synchronize()
         finally:
             sv.sv_set_wait_limit(DEFAULT_POLLS)
+            sv.sv_set_greedy_lookahead()
         out[name] = (host(n).numpy(), host(nx).numpy(), None if mg is None else host(mg).numpy())
     return out
 
@@ -133,14 +144,16 @@ def test_paths_full_size(sv):
     check(sv, b.target, toks.contiguous(), b.lens, name + "/full")
 
 
-@pytest.mark.parametrize("polls", [DEFAULT_POLLS, 0])
-def test_workspace_is_left_zero(sv, polls):
+@pytest.mark.parametrize("polls,la", [(DEFAULT_POLLS, None), (0, None), (DEFAULT_POLLS, LOOKAHEADS["ahead1"]),
+                                      (DEFAULT_POLLS, LOOKAHEADS["ahead2"]), (0, LOOKAHEADS["full"])],
+                         ids=["default", "nowait", "ahead1", "ahead2", "nowait-full"])
+def test_workspace_is_left_zero(sv, polls, la):
     """The split path needs no reset before a launch: a workspace that holds
     zeros is all zero again after every call (the last workgroup of each
-    sequence clears the words the sequence used), also when every workgroup
-    gives up waiting and computes the other slices itself. Several calls in a
-    row on one workspace, with and without the margin, stay equal to the
-    oracle."""
+    sequence clears the words the sequence used; rows read ahead are never
+    published before their turn), also when every workgroup gives up waiting
+    and computes the other slices itself. Several calls in a row on one workspace, with and without the
+    margin, stay equal to the oracle."""
     name = "logits-bf16-b512-k16-v256000-zipf"
     b = synth.generate(name, "cuda", B=24)
     chain = b.target.argmax(-1).to(torch.int32)[:, :b.K]
@@ -150,6 +163,8 @@ def test_workspace_is_left_zero(sv, polls):
     n_o, nx_o = oracle.verify_greedy(host(b.target), host(toks), None)
     ws = torch.zeros(sv.sv_verify_greedy_workspace_bytes(b.B, b.K, b.V), dtype=torch.uint8, device="cuda")
     sv.sv_set_wait_limit(polls)
+    if la is not None:
+        sv.sv_set_greedy_lookahead(la)
     try:
         for rep in range(3):
             for margin in (False, True):
@@ -163,4 +178,5 @@ def test_workspace_is_left_zero(sv, polls):
                 assert int(ws.count_nonzero()) == 0, f"rep {rep} margin {margin}: workspace not left zero"
     finally:
         sv.sv_set_wait_limit(DEFAULT_POLLS)
-    print(f"[workspace left zero] polls={polls}: 6 calls, mean n {n_o.mean():.2f}", flush=True)
+        sv.sv_set_greedy_lookahead()
+    print(f"[workspace left zero] polls={polls} look-ahead {la}: 6 calls, mean n {n_o.mean():.2f}", flush=True)
