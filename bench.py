@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="logits-bf16-b512-k16-v256000-zipf")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lookahead-sweep", action="store_true",
+                    help="skip the greedy look-ahead depths (profiler runs: one launch shape, one depth)")
     ap.add_argument("--top-k", type=int, default=50, help="top-k of the filtered-warp leg")
     ap.add_argument("--top-p", type=float, default=0.9, help="top-p of the filtered-warp leg")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -243,7 +245,7 @@ def main():
     modes_out["greedy"] = mode_record("greedy", *ms["greedy"], needed=greedy_bytes,
                                       read=read_bytes("greedy_sliced_kernel") or read_bytes("greedy_kernel"),
                                       mean_n=round(float(n_g.mean()), 4))
-    if sv.sv_verify_greedy_workspace_bytes(B, K, V) > 0:
+    if sv.sv_verify_greedy_workspace_bytes(B, K, V) > 0 and not args.no_lookahead_sweep:
         # the split walk's look-ahead depth L (rows read ahead of the decision): the same results, more
         # bytes loaded -- (min(K_b, n + L) + 1) rows of each sequence -- and the time they take
         la = {}
