@@ -1,0 +1,41 @@
+"""The C ABI from a C++ caller with no Python in between (tests/c_abi/round_trip.cpp,
+built by __graft_entry__.build()): the greedy verify bit-exact and the sampled
+round (both warps, then sv_accept) equal to the fp64 oracle except where the
+oracle flags a boundary within 1e-7, then both rounds timed back to back from
+C. The printed latencies are what a native caller sees: kernel time plus the
+HIP launch, without the binding's argument marshalling."""
+import json
+import os
+import subprocess
+
+import pytest
+import torch
+
+BINARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "round_trip")
+CASES = [(1, 4, 32000, 1), (64, 4, 32000, 2), (8, 7, 70001, 3), (16, 16, 256000, 4)]
+
+
+@pytest.fixture(scope="module")
+def binary():
+    if not os.path.exists(BINARY):
+        pytest.skip("tests/c_abi/round_trip is not built (__graft_entry__.build() builds it)")
+    return BINARY
+
+
+def test_program_links_and_checks_its_arguments(binary):
+    """No GPU needed: the program starts (both libraries resolve) and rejects a bad call."""
+    r = subprocess.run([binary], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,K,V,seed", CASES)
+def test_round_trip(binary, B, K, V, seed):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    r = subprocess.run([binary, str(B), str(K), str(V), str(seed), "50"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, f"rc {r.returncode}: {r.stdout} {r.stderr}"
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    print(f"[c-abi] {line}", flush=True)
+    assert line["greedy_mismatches"] == 0 and line["sampled_mismatches"] == 0
