@@ -825,6 +825,24 @@ __device__ __forceinline__ float wave_max_f(float x) {
     return max2f(readlane_f(x, 0), readlane_f(x, 32));
 }
 
+// The N wave partials a[0 .. N) combined in a fixed pairwise order.
+template <int N>
+__device__ __forceinline__ float lds_max(const float* a) {
+    if constexpr (N == 1) {
+        return a[0];
+    } else {
+        return max2f(lds_max<N / 2>(a), lds_max<N - N / 2>(a + N / 2));
+    }
+}
+template <int N>
+__device__ __forceinline__ double lds_sum(const double* a) {
+    if constexpr (N == 1) {
+        return a[0];
+    } else {
+        return lds_sum<N / 2>(a) + lds_sum<N - N / 2>(a + N / 2);
+    }
+}
+
 // Statistics (m, s) of the slice held in rt (and rd when D), over the
 // workgroup: m is the ceiling of the slice's largest y = z * c (kNoRef if
 // none is finite), shared by every lane, so the lanes' sums of 2^(y - m) add
@@ -833,7 +851,7 @@ __device__ __forceinline__ float wave_max_f(float x) {
 template <bool BF16, bool D>
 __device__ void slice_stats(const u32x4 (&rt)[kSliceVecs], const u32x4 (&rd)[kSliceVecs], float c, StatsLds* lds,
                             Online& t, Online& d) {
-    static_assert(kSliceWaves == 4, "four wave partials are combined below");
+    static_assert(kSliceWaves <= kWaves, "the wave partials live in StatsLds");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     float xt = wave_max_f(lane_max<BF16>(rt)), xd = -INFINITY;
     if (D) xd = wave_max_f(lane_max<BF16>(rd));
@@ -843,13 +861,11 @@ __device__ void slice_stats(const u32x4 (&rt)[kSliceVecs], const u32x4 (&rd)[kSl
         if (D) lds->m[1][wave] = xd;
     }
     __syncthreads();
-    xt = max2f(max2f(lds->m[0][0], lds->m[0][1]), max2f(lds->m[0][2], lds->m[0][3]));
-    t.m = max2f(kNoRef, ceilf(xt * c));
+    t.m = max2f(kNoRef, ceilf(lds_max<kSliceWaves>(lds->m[0]) * c));
     const double st = wave_sum_d(lane_expsum<BF16>(rt, c, t.m));
     double sd = 0.0;
     if (D) {
-        xd = max2f(max2f(lds->m[1][0], lds->m[1][1]), max2f(lds->m[1][2], lds->m[1][3]));
-        d.m = max2f(kNoRef, ceilf(xd * c));
+        d.m = max2f(kNoRef, ceilf(lds_max<kSliceWaves>(lds->m[1]) * c));
         sd = wave_sum_d(lane_expsum<BF16>(rd, c, d.m));
     }
     if (lane == 0) {
@@ -857,8 +873,8 @@ __device__ void slice_stats(const u32x4 (&rt)[kSliceVecs], const u32x4 (&rd)[kSl
         if (D) lds->s[1][wave] = sd;
     }
     __syncthreads();
-    t.s = (lds->s[0][0] + lds->s[0][1]) + (lds->s[0][2] + lds->s[0][3]);
-    if (D) d.s = (lds->s[1][0] + lds->s[1][1]) + (lds->s[1][2] + lds->s[1][3]);
+    t.s = lds_sum<kSliceWaves>(lds->s[0]);
+    if (D) d.s = lds_sum<kSliceWaves>(lds->s[1]);
 }
 
 __device__ __forceinline__ unsigned long long pack_online(const Online& o) {
