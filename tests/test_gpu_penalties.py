@@ -10,7 +10,9 @@ of the whole sampler pipeline built on it.
     oracle's composition;
   - penalties -> warp -> sampled verify and penalties -> greedy verify on a
     verify round, every sequence against the oracle (greedy bit-exact, sampled
-    under the parity bar of tests/sampled_check.py).
+    under the parity bar of tests/sampled_check.py);
+  - the stage at the largest workload's full size: sampled sequences bit for
+    bit, and on every row the set of changed ids.
 """
 import zlib
 
@@ -200,3 +202,49 @@ def test_penalties_counts_beyond_a_byte(sv, dtype):
     theta, pres, freq = params(B, rng)
     theta[0], pres[0], freq[0] = 1.1, 0.2, 0.001       # sequence 0 penalised too
     check(sv, z, None, 1, seq, seq_len, toks, theta, pres, freq, f"counts-{dtype}")
+
+
+def test_penalties_largest_workload(sv):
+    """The penalty stage at the size and launch configuration the benchmark
+    times: the 512 x 17 target rows of 256000 bf16 logits, a committed history
+    of up to 2048 tokens per sequence (the two-kernel path: history tables,
+    then 8 row slices of 32768 ids per workgroup), each row's draft prefix and
+    the benchmark's parameters (theta 1.2, presence 0.3, frequency 0.1).
+      - every live row of 32 sampled sequences bit for bit against the oracle;
+      - every row of the batch: an element changes exactly where its id is in
+        the row's history (committed ids or the row's draft prefix). Every such
+        id changes, because presence + frequency * c >= 0.4 is subtracted."""
+    name = "logits-bf16-b512-k16-v256000-zipf"
+    b = synth.generate(name, "cuda")
+    B, K, V = b.B, b.K, b.V
+    cap = 2048
+    rng = np.random.default_rng(11)
+    seq = rng.integers(0, V, (B, cap)).astype(np.int32)
+    seq_len = rng.integers(cap // 2, cap + 1, B).astype(np.int32)
+    d = lambda x: torch.as_tensor(x).cuda()
+    ws = torch.empty(sv.sv_apply_penalties_workspace_bytes(B, cap), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, K + 1, V), SENTINEL, device="cuda")
+    print(f"[{name}] penalties on {B * (K + 1)} rows, history cap {cap}", flush=True)
+    sv.sv_apply_penalties(b.target, b.lens, 1, d(seq), d(seq_len), b.tokens, 1.2, 0.3, 0.1, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    toks = host(b.tokens).numpy()
+
+    picks = np.sort(rng.choice(B, 32, replace=False))
+    ref = oracle.apply_penalties(host(b.target[picks]), None, 1, seq[picks], seq_len[picks], toks[picks], 1.2, 0.3,
+                                 0.1)
+    got = host(out[picks]).numpy()
+    np.testing.assert_array_equal(got.view(np.int32), ref.view(np.int32), err_msg=f"{name}: sampled sequences")
+
+    # every row: the changed ids are exactly the row's history ids
+    for b0 in range(0, B, 64):
+        sl = slice(b0, min(B, b0 + 64))
+        z = b.target[sl].float()
+        diff = (out[sl] != z)
+        for bb in range(sl.start, sl.stop):
+            hist = set(seq[bb, : seq_len[bb]].tolist())
+            for r in range(K + 1):
+                ids = np.array(sorted(hist | set(toks[bb, :r].tolist())), dtype=np.int64)
+                expect = torch.zeros(V, dtype=torch.bool, device="cuda")
+                expect[torch.as_tensor(ids, device="cuda")] = True
+                assert torch.equal(diff[bb - b0, r], expect), f"{name}: changed ids of row ({bb}, {r})"
+    print(f"[{name}] 32 sequences bit-exact; changed ids match the histories on all {B * (K + 1)} rows", flush=True)
