@@ -60,6 +60,8 @@ def load_library(path: str):
     lib.or_accept.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, ctypes.c_int, f64, vp, vp, vp]
     lib.or_accept_logits.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, ctypes.c_int, f64, vp, vp,
                                      vp]
+    lib.or_accept_logits_lse.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, f64, vp, vp, vp, vp, ctypes.c_int, f64,
+                                         vp, vp, vp]
     f32 = ctypes.c_float
     lib.or_penalize_row.argtypes = [vp, ctypes.c_int, i64, vp, i64, f32, f32, f32, vp]
     lib.or_apply_penalties.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, i64, vp, i64, vp, vp, vp, vp]
@@ -311,11 +313,15 @@ def accept(p, q, tokens, uniforms, lens=None, rel_window: float = 1e-5, lib=None
     return n, nx, fl
 
 
-def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_window: float = 1e-5, lib=None):
+def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_window: float = 1e-5, lib=None,
+                  draft_lse=None):
     """Sampled verify from logits: or_accept on softmax(z / T) of the examined rows, in fp64.
 
     zt [B, K+1, V], zd [B, K, V] logits (same dtype). Returns (n_accepted, next_token, flags),
     flagged with the same relative ratio and CDF windows as ``accept``.
+
+    draft_lse [B, K] (fp32): each draft row's distribution given by its
+    log-normaliser, q_i(x) = exp(zd_i(x) / T - draft_lse[b, i]) (or_accept_logits_lse).
     """
     ta, dt = _array(zt)
     B, K1, V = ta.shape
@@ -335,8 +341,15 @@ def accept_logits(zt, zd, tokens, uniforms, lens=None, T: float = 1.0, rel_windo
     n = np.empty(B, dtype=np.int32)
     nx = np.empty(B, dtype=np.int32)
     fl = np.empty(B, dtype=np.int32)
-    (lib or _lib()).or_accept_logits(_ptr(ta), _ptr(da), dt, B, K, V, float(T), _ptr(t), _ptr(ln), _ptr(ua), du,
-                                     float(rel_window), _ptr(n), _ptr(nx), _ptr(fl))
+    if draft_lse is None:
+        (lib or _lib()).or_accept_logits(_ptr(ta), _ptr(da), dt, B, K, V, float(T), _ptr(t), _ptr(ln), _ptr(ua), du,
+                                         float(rel_window), _ptr(n), _ptr(nx), _ptr(fl))
+    else:
+        ls = _f32(draft_lse)
+        if ls.size != B * K:
+            raise ValueError(f"draft_lse must hold B*K = {B * K} values, got {ls.size}")
+        (lib or _lib()).or_accept_logits_lse(_ptr(ta), _ptr(da), dt, B, K, V, float(T), _ptr(ls), _ptr(t), _ptr(ln),
+                                             _ptr(ua), du, float(rel_window), _ptr(n), _ptr(nx), _ptr(fl))
     return n, nx, fl
 
 

@@ -39,6 +39,9 @@
  *  R8  Greedy reads its rows as given (logits or probabilities, no warp).
  *  R9  The bonus and fallback draws weigh ids by max(0, p) (identical to p
  *      for valid probability rows).
+ *  R29 A draft distribution given by its log-normaliser (draft_lse) is taken
+ *      as given: q_i(x) = exp(z_draft,i(x) / T - lse_i), not renormalised, so
+ *      a wrong lse scales q_i (and with it the accept ratio and the residual).
  */
 #include <math.h>
 #include <stdint.h>
@@ -254,10 +257,24 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
  * or_warp_row; only the rows the procedure examines are warped. Flags use
  * the same relative windows as or_accept: a tested u within rel_window * rho
  * of its ratio, a draw threshold within rel_window * C of a cumulative
- * weight C. */
-void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
-                      const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
-                      double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags) {
+ * weight C.
+ *
+ * With draft_lse (or_accept_logits_lse) the draft distribution of position i
+ * is given by its log-normaliser instead of being normalised here:
+ * q_i(x) = exp(z_draft,i(x) / T - draft_lse[b, i]) (R29). The draft model
+ * computes this normaliser when it samples t_i from q_i; with the row's true
+ * log-sum-exp the procedure is or_accept_logits exactly, up to the rounding
+ * of the value passed in. */
+
+/* q(x) = exp(z(x) / T - lse) over one row (R29). */
+static void draft_row_given_lse(const void* z, int dtype, int64_t V, double T, double lse, double* q) {
+    for (int64_t x = 0; x < V; ++x) q[x] = exp(elem(z, dtype, x) / T - lse);
+}
+
+static void accept_logits_impl(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                               const float* draft_lse, const int32_t* tokens, const int32_t* lens,
+                               const void* uniforms, int u_dtype, double rel_window, int32_t* n_accepted,
+                               int32_t* next_token, int32_t* flags) {
 #pragma omp parallel
     {
         double* p = (double*)malloc((size_t)V * sizeof(double));
@@ -275,7 +292,10 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
                     break;
                 }
                 or_warp_row(row_ptr(zt, dtype, b * (K + 1) + i, V), dtype, V, T, p);
-                or_warp_row(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, q);
+                if (draft_lse)
+                    draft_row_given_lse(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, (double)draft_lse[b * K + i], q);
+                else
+                    or_warp_row(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, q);
                 double rho = q[t] > 0.0 ? p[t] / q[t] : (p[t] > 0.0 ? INFINITY : 0.0);
                 if (isfinite(rho) && fabs(ui - rho) <= rel_window * rho) flag |= OR_FLAG_RATIO;
                 if (!(ui < rho)) {
@@ -289,7 +309,10 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
             if (n < kb) {
                 /* p, q hold row n unless the loop stopped on an out-of-range token */
                 or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);
-                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);
+                if (draft_lse)
+                    draft_row_given_lse(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, (double)draft_lse[b * K + n], q);
+                else
+                    or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);
                 if (or_mass(p, q, OR_F64, 0, V) > 0.0) {
                     next = or_icdf(p, q, OR_F64, 0, V, u_final, rel_window, &f2);
                 } else {
@@ -307,6 +330,20 @@ void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int6
         free(p);
         free(q);
     }
+}
+
+void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                      const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
+                      double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags) {
+    accept_logits_impl(zt, zd, dtype, B, K, V, T, NULL, tokens, lens, uniforms, u_dtype, rel_window, n_accepted,
+                       next_token, flags);
+}
+
+void or_accept_logits_lse(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                          const float* draft_lse, const int32_t* tokens, const int32_t* lens, const void* uniforms,
+                          int u_dtype, double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags) {
+    accept_logits_impl(zt, zd, dtype, B, K, V, T, draft_lse, tokens, lens, uniforms, u_dtype, rel_window, n_accepted,
+                       next_token, flags);
 }
 
 /* ---- sampler penalties: the pipeline's first stage [BLOG s.38, s.39] ----

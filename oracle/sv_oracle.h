@@ -53,6 +53,10 @@ void or_accept(const void* p, const void* q, int dtype, int64_t B, int64_t K, in
 void or_accept_logits(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
                       const int32_t* tokens, const int32_t* lens, const void* uniforms, int u_dtype,
                       double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags);
+/* or_accept_logits with q_i(x) = exp(z_draft,i(x) / T - draft_lse[b*K + i]) (R29). */
+void or_accept_logits_lse(const void* zt, const void* zd, int dtype, int64_t B, int64_t K, int64_t V, double T,
+                          const float* draft_lse, const int32_t* tokens, const int32_t* lens, const void* uniforms,
+                          int u_dtype, double rel_window, int32_t* n_accepted, int32_t* next_token, int32_t* flags);
 
 void or_penalize_row(const void* z, int dtype, int64_t V, const int32_t* hist, int64_t nh, float theta,
                      float presence, float frequency, float* out);

@@ -157,6 +157,12 @@ static void verifies(void) {
             or_accept(p, q, OR_F32, B, K, V, tok, ln, uf, OR_F32, 1e-5, n, nx, fl);
             or_accept_logits(zt, zd, OR_F32, B, K, V, 0.9, tok, ln, u, OR_F64, 1e-5, n, nx, fl);
             for (int64_t b = 0; b < B; ++b) CHECK(n[b] >= 0 && n[b] <= K && nx[b] >= -1 && nx[b] < V);
+            /* given draft normalisers: exact-size [B, K] array (one element when K = 0) */
+            float* lse = exact((size_t)(B * (K > 0 ? K : 1)) * 4);
+            for (int64_t i = 0; i < B * (K > 0 ? K : 1); ++i) lse[i] = (float)(3.0 * uniform01());
+            or_accept_logits_lse(zt, zd, OR_F32, B, K, V, 0.9, lse, tok, ln, u, OR_F64, 1e-5, n, nx, fl);
+            for (int64_t b = 0; b < B; ++b) CHECK(n[b] >= 0 && n[b] <= K && nx[b] >= -1 && nx[b] < V);
+            free(lse);
         }
         for (int kind = 0; kind <= 1; ++kind) {
             int32_t f = 0;

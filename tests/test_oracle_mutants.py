@@ -137,6 +137,45 @@ def check_logits(lib):
     assert (n1 == n2).all() and (x1 == x2).all()
 
 
+def check_logits_lse(lib):
+    # a draft normaliser larger by log(1.25) scales q by 0.8: exact law against
+    # the closed forms, on rows where q < c * p at some ids and not at others (so
+    # that acceptance and residual both depend on every row's scale)
+    from tests.test_oracle_logits import exact_lse
+    rng = np.random.default_rng(7)
+    K, V, T, c = 2, 4, 0.6, 1.25
+    zt = 1.5 * rng.standard_normal((K + 1, V)) + 2.0
+    zd = zt[:K] + rng.standard_normal((K, V)) + 3.0  # softmax is unchanged; the normaliser is far from 0
+    sm = lambda y: np.exp(y - y.max(-1, keepdims=True)) / np.exp(y - y.max(-1, keepdims=True)).sum(-1, keepdims=True)
+    p, q = sm(zt / T), sm(zd / T)
+    lse = (exact_lse(zd, T) + np.log(c)).astype(np.float32)
+    qs = np.exp(zd / T - lse.astype(np.float64)[:, None])
+
+    def run(P, Q, Tk, U):
+        Bn = P.shape[0]
+        n, nx, _ = oracle.accept_logits(np.broadcast_to(zt, (Bn, K + 1, V)).copy(),
+                                        np.broadcast_to(zd, (Bn, K, V)).copy(), Tk, U, None, T, lib=lib,
+                                        draft_lse=np.broadcast_to(lse, (Bn, K)).copy())
+        return n, nx
+
+    below = q < c * p[:K]
+    assert below.any(-1).all() and (~below).any(-1).all()
+    law, bad = enumerate_law(p, qs, run)
+    scale = np.prod(qs.sum(-1))
+    a = np.minimum(q, c * p[:K]).sum(-1)
+    for i in range(K + 1):
+        assert prob_n_at_least(law, i) / scale == pytest.approx(np.prod(a[:i]), abs=1e-6)
+    for i in range(K):
+        r = np.maximum(0.0, p[i] - q[i] / c)
+        r = r / r.sum() if r.sum() > 0 else p[i]
+        want = np.prod(a[:i]) * (np.minimum(q[i], c * p[i]) + (1.0 - a[i]) * r)
+        np.testing.assert_allclose(emitted_marginal(law, i, V) / scale, want, atol=1e-6)
+    assert bad == 0
+    # the accept and draw boundaries themselves (closed forms), where a scale slip shows
+    from tests.test_oracle_logits import given_lse_boundaries
+    given_lse_boundaries(zt, zd, T, c, lib=lib)
+
+
 def check_filtered(lib):
     # tie groups at the top-k boundary and in the nucleus (closed forms)
     z = np.array([5.0, 4.0, 3.0, 4.0, 4.0, 1.0], dtype=np.float32)
@@ -212,7 +251,7 @@ def check_penalties(lib):
 
 
 ALL_CHECKS = [check_argmax, check_greedy, check_sampled_law, check_ragged, check_warp, check_icdf, check_logits,
-              check_filtered, check_gate, check_penalties]
+              check_logits_lse, check_filtered, check_gate, check_penalties]
 
 # (what goes wrong, exact source text, planted replacement)
 MUTANTS = [
@@ -244,8 +283,17 @@ MUTANTS = [
      "or_warp_row(row_ptr(zd, dtype, b * K + i, V), dtype, V, T, q);",
      "or_warp_row(row_ptr(zd, dtype, b * (K + 1) + i, V), dtype, V, T, q);"),
     ("logits verify draws the correction from the wrong row",
-     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);",
-     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);\n                or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);"),
+     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + n, V), dtype, V, T, p);",
+     "or_warp_row(row_ptr(zt, dtype, b * (K + 1) + kb, V), dtype, V, T, p);"),
+    ("given draft normaliser added instead of subtracted", "exp(elem(z, dtype, x) / T - lse)",
+     "exp(elem(z, dtype, x) / T + lse)"),
+    ("given draft normaliser without the temperature", "exp(elem(z, dtype, x) / T - lse)",
+     "exp(elem(z, dtype, x) - lse)"),
+    ("given draft normaliser of position 0 used at every position", "(double)draft_lse[b * K + i], q);",
+     "(double)draft_lse[b * K], q);"),
+    ("correction renormalises a given draft row",
+     "draft_row_given_lse(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, (double)draft_lse[b * K + n], q);",
+     "or_warp_row(row_ptr(zd, dtype, b * K + n, V), dtype, V, T, q);"),
     ("top-k drops the ties of the k-th value", "while (n < V && s[n].y >= kth) ++n;", "while (n < V && s[n].y > kth) ++n;"),
     ("top-k keeps one value too many", "double kth = s[top_k - 1].y;", "double kth = s[top_k < V - 1 ? top_k : top_k - 1].y;"),
     ("top-p measured against the unfiltered mass", "for (int64_t i = 0; i < n; ++i) S += exp(s[i].y - m);",
