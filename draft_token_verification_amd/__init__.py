@@ -108,7 +108,10 @@ def _load():
     lib.sv_accept_logits_workspace_bytes.argtypes = [i32, i32, i64]
     lib.sv_accept_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.sv_accept_logits.restype = c_int
-    if lib.sv_abi_version() != 3:
+    lib.sv_accept_logits_lse.argtypes = [vp, vp, c_int, i32, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
+    lib.sv_accept_logits_lse.restype = c_int
+    if lib.sv_abi_version() != 4:
         raise ImportError("libspecverify ABI version mismatch")
     return lib
 
@@ -584,7 +587,8 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
                      draft_tokens: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: float = 1.0,
                      draft_lens: Optional[torch.Tensor] = None,
                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     workspace: Optional[torch.Tensor] = None,
+                     draft_lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Speculative-sampling verify from logits (fp32 or bf16) -> (n_accepted[B], next_token[B]).
 
     ``workspace`` (uint8 device tensor) defaults to one kept per device and stream, sized by
@@ -592,6 +596,10 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
 
     target_logits [B, K+1, V], draft_logits [B, K, V] (same dtype), draft_tokens [B, K],
     uniforms [B, K+1] fp32; the rows are warped with temperature T on the fly.
+
+    ``draft_lse`` (fp32 [B, K], optional) gives each draft row's normaliser
+    log sum_x exp(draft_logits / T) (sv_accept_logits_lse): the draft rows are then read
+    only at the rejected position.
     """
     _dev(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -614,6 +622,10 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
     lens = _int32(draft_lens, "draft_lens", dev)
     if lens is not None and tuple(lens.shape) != (B,):
         raise ValueError("draft_lens must be [B]")
+    if draft_lse is not None:
+        _dev(draft_lse, "draft_lse")
+        if draft_lse.dtype != torch.float32 or tuple(draft_lse.shape) != (B, K) or draft_lse.device != dev:
+            raise ValueError(f"draft_lse must be fp32 {(B, K)} on {dev}")
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
     with torch.cuda.device(dev):
@@ -624,10 +636,19 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the logits' device")
         ws_bytes = 0 if workspace is None else workspace.numel()
-        st = _lib.sv_accept_logits(_ptr(target_logits), _ptr(draft_logits if K > 0 else None), code, B, K, V,
-                                   float(temperature), _ptr(toks), _ptr(lens), _ptr(uniforms), _ptr(n), _ptr(nx),
-                                   _ptr(workspace), ws_bytes, stream)
-    _check("sv_accept_logits", st)
+        if draft_lse is None:
+            fn = "sv_accept_logits"
+            st = _lib.sv_accept_logits(_ptr(target_logits), _ptr(draft_logits if K > 0 else None), code, B, K, V,
+                                       float(temperature), _ptr(toks), _ptr(lens), _ptr(uniforms), _ptr(n), _ptr(nx),
+                                       _ptr(workspace), ws_bytes, stream)
+        else:
+            fn = "sv_accept_logits_lse"
+            lse = draft_lse.contiguous()
+            st = _lib.sv_accept_logits_lse(_ptr(target_logits), _ptr(draft_logits if K > 0 else None), code, B, K,
+                                           V, float(temperature), _ptr(lse if K > 0 else None), _ptr(toks),
+                                           _ptr(lens), _ptr(uniforms), _ptr(n), _ptr(nx), _ptr(workspace), ws_bytes,
+                                           stream)
+    _check(fn, st)
     return n, nx
 
 

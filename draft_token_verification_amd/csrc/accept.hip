@@ -164,6 +164,26 @@ __device__ __forceinline__ bool accepts(float zt, float zd, float c, const RowSt
     return (double)u < two_e * (st.inv / sd.inv);
 }
 
+// Statistics of a draft row given by its natural-log normaliser lse at
+// temperature T (the draft model computes it when it samples from the row):
+// in the kernels' log2 domain (y = z * c, c = log2(e) / T) the row's mass is
+// 2^L with L = lse * log2(e), so m = ceil(L) and 1/inv = 2^(L - m). Finite
+// lse only.
+__device__ __forceinline__ RowStats given_stats(float lse) {
+    const double L = (double)lse * 1.4426950408889634;
+    const float m = (float)ceil(L);
+    return RowStats{m, exp2((double)m - L)};
+}
+
+// The accept test with a given draft normaliser lse. Not finite: +inf makes
+// q = 0 and NaN makes q NaN, neither positive, so the ratio is +inf (accept
+// unless p(t) = 0); -inf makes q = +inf, so the ratio is 0 (reject).
+__device__ __forceinline__ bool accepts_given(float zt, float zd, float c, const RowStats& st, float lse, float u) {
+    if (lse == INFINITY || lse != lse) return zt != -INFINITY;
+    if (lse == -INFINITY) return false;
+    return accepts(zt, zd, c, st, given_stats(lse), u);
+}
+
 // 1 - 2^y for y < 0, with a relative error of a few 1e-7 everywhere: a
 // series in t = y ln 2 near 0 (|t| <= 0.18, truncated after t^6 / 6!, whose
 // remainder is below 1e-8 relative) and 1 - exp2(y) below, where the result
@@ -622,10 +642,13 @@ __device__ void row_stats_pass(const void* zt, const void* zd, int V, float c, S
     if (D) sd = RowStats{rd.m, 1.0 / rd.s};
 }
 
-template <bool BF16, bool VEC>
+// LSE: the draft rows' normalisers are given (draft_lse [B, K]); a draft row
+// is then read only at the rejected position, for the residual.
+template <bool BF16, bool VEC, bool LSE>
 __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __restrict__ zt,
                                                                  const void* __restrict__ zd, int K, int V, int m,
-                                                                 int nseg, float c, const int32_t* __restrict__ tokens,
+                                                                 int nseg, float c, const float* __restrict__ draft_lse,
+                                                                 const int32_t* __restrict__ tokens,
                                                                  const int32_t* __restrict__ lens,
                                                                  const float* __restrict__ uniforms,
                                                                  int32_t* __restrict__ n_accepted,
@@ -651,24 +674,31 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
         }
         const void* tr = tbase + (size_t)i * row_bytes;
         const void* dr = dbase + (size_t)i * row_bytes;
-        row_stats_pass<BF16, VEC, true>(tr, dr, V, c, &lds, st, sd);
-        if (!accepts(L::at(tr, t), L::at(dr, t), c, st, sd, uniforms[(int64_t)b * (K + 1) + i])) {
+        const float u = uniforms[(int64_t)b * (K + 1) + i];
+        row_stats_pass<BF16, VEC, !LSE>(tr, dr, V, c, &lds, st, sd);
+        const bool ok = LSE ? accepts_given(L::at(tr, t), L::at(dr, t), c, st, draft_lse[(int64_t)b * K + i], u)
+                            : accepts(L::at(tr, t), L::at(dr, t), c, st, sd, u);
+        if (!ok) {
             n = i;
             have = true;
             break;
         }
     }
 
-    // 2-3. the draw
-    const bool residual = n < kb;
-    const void* zt_row = tbase + (size_t)(residual ? n : kb) * row_bytes;
+    // 2-3. the draw (LSE: a rejection whose normaliser is not finite has q = 0
+    // or a residual of no mass, and draws from max(0, p_n))
+    bool residual = n < kb;
+    const float lse_n = LSE && residual ? draft_lse[(int64_t)b * K + n] : 0.0f;
+    if (LSE && residual && !(lse_n > -INFINITY && lse_n < INFINITY)) residual = false;
+    const void* zt_row = tbase + (size_t)(n < kb ? n : kb) * row_bytes;
     const void* zd_row = residual ? (const void*)(dbase + (size_t)n * row_bytes) : nullptr;
-    if (!(residual && have)) {
-        if (residual)
+    if (!(n < kb && have)) {
+        if (residual && !LSE)
             row_stats_pass<BF16, VEC, true>(zt_row, zd_row, V, c, &lds, st, sd);
         else
             row_stats_pass<BF16, VEC, false>(zt_row, nullptr, V, c, &lds, st, sd);
     }
+    if (LSE && residual) sd = given_stats(lse_n);
     const LogitSource<BF16, VEC, true> res{zt_row, zd_row, V, c, st, sd,
                                            residual ? residual_shift(st, sd) : Shift{0.f, 0.f}};
     const LogitSource<BF16, VEC, false> bon{zt_row, nullptr, V, c, st, sd, Shift{0.f, 0.f}};
@@ -1149,12 +1179,15 @@ __device__ __forceinline__ float uniform_logit(const char* row, int i) {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(*(const uint32_t*)(row + (size_t)i * 4)));
 }
 
-template <bool BF16, bool VEC>
+// LSE: the draft rows' normalisers are given (draft_lse [B, K]); only the
+// target rows' statistics are exchanged, and a draft row is read only at the
+// rejected position, for the residual.
+template <bool BF16, bool VEC, bool LSE>
 __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
     const void* __restrict__ zt, const void* __restrict__ zd, int K, int V, int G, int Ls, float c,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens, const float* __restrict__ uniforms,
-    int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token, unsigned long long* __restrict__ slots,
-    int wait_limit) {
+    const float* __restrict__ draft_lse, const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens,
+    const float* __restrict__ uniforms, int32_t* __restrict__ n_accepted, int32_t* __restrict__ next_token,
+    unsigned long long* __restrict__ slots, int wait_limit) {
     __shared__ StatsLds lds;
     __shared__ u32x4 s_draft[kSliceVecs * kSliceThreads];
     __shared__ double chunk[kChunks];
@@ -1184,8 +1217,11 @@ __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
         const int t = tokens[(int64_t)b * K + n];
         const bool valid = t >= 0 && t < V;  // an out-of-range draft token is rejected, never dereferenced
         const float zt_t = uniform_logit<BF16>(tr, valid ? t : 0), zd_t = uniform_logit<BF16>(dr, valid ? t : 0);
-        position_stats<BF16, VEC, true>(x, pos_sets + (size_t)n * 2 * G, tr, dr, c, rt, &lds, st, sd);
-        if (!valid || !accepts(zt_t, zd_t, c, st, sd, uniforms[(int64_t)b * (K + 1) + n])) {
+        const float u = uniforms[(int64_t)b * (K + 1) + n];
+        position_stats<BF16, VEC, !LSE>(x, pos_sets + (size_t)n * 2 * G, tr, dr, c, rt, &lds, st, sd);
+        const bool ok = LSE ? accepts_given(zt_t, zd_t, c, st, draft_lse[(int64_t)b * K + n], u)
+                            : accepts(zt_t, zd_t, c, st, sd, u);
+        if (!valid || !ok) {
             residual = true;
             break;
         }
@@ -1194,6 +1230,21 @@ __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
     const char* drow = dbase + (size_t)n * row_bytes;  // read only for a residual
     if (!residual)
         position_stats<BF16, VEC, false>(x, pos_sets + (size_t)kb * 2 * G, trow, nullptr, c, rt, &lds, st, sd);
+    if (LSE && residual) {
+        // the given normaliser of row n: not finite means q = 0 or a residual of
+        // no mass, so the draw takes max(0, p_n); otherwise this slice of draft
+        // row n goes to LDS for the residual
+        const float l = draft_lse[(int64_t)b * K + n];
+        if (l > -INFINITY && l < INFINITY) {
+            sd = given_stats(l);
+            u32x4 v[kSliceVecs];
+            load_slice<BF16, VEC>(drow, (int64_t)g * Ls, x.len(g), v);
+#pragma unroll
+            for (int u = 0; u < kSliceVecs; ++u) s_draft[u * kSliceThreads + threadIdx.x] = v[u];  // own lanes only
+        } else {
+            residual = false;
+        }
+    }
 
     // 2. total draw weight over the slices
     const Shift k0 = residual ? residual_shift(st, sd) : Shift{0.f, 0.f};
@@ -1296,60 +1347,64 @@ size_t accept_logits_workspace_bytes(int B, int K, int V) {
     return a > b ? a : b;
 }
 
-hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
-                                const int32_t* tokens, const int32_t* lens, const float* uniforms,
-                                int32_t* n_accepted, int32_t* next_token, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
-    const float c = 1.4426950408889634f / temperature;
-    const uintptr_t al = bf16 ? 8 : 16;
+namespace {
+
+// The launches of one dtype and one kind of draft input (LSE: normalisers given).
+template <bool BF16, bool LSE>
+hipError_t launch_accept_logits_t(const void* zt, const void* zd, int B, int K, int V, float c, const float* draft_lse,
+                                  const int32_t* tokens, const int32_t* lens, const float* uniforms,
+                                  int32_t* n_accepted, int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    const uintptr_t al = BF16 ? 8 : 16;
     const bool vec = (V % 4 == 0) && ((uintptr_t)zt % al == 0) && ((uintptr_t)zd % al == 0);
-    const size_t need = fused_dtype_workspace_bytes(B, K, V, bf16);
+    const size_t need = fused_dtype_workspace_bytes(B, K, V, BF16);
     if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % 8 == 0) {
         int Ls;
-        const int G = fused_slices(V, bf16, Ls);
-        const bool vec16 = (V % (bf16 ? 8 : 4) == 0) && ((uintptr_t)zt % 16 == 0) && ((uintptr_t)zd % 16 == 0);
+        const int G = fused_slices(V, BF16, Ls);
+        const bool vec16 = (V % (BF16 ? 8 : 4) == 0) && ((uintptr_t)zt % 16 == 0) && ((uintptr_t)zd % 16 == 0);
         const int64_t words = (int64_t)(need / sizeof(unsigned long long));
         unsigned long long* slots = (unsigned long long*)workspace;
         const hipError_t fe = launch_fill_empty(slots, words, stream);
         if (fe != hipSuccess) return fe;  // without the fill, stale slots would read as published
         const dim3 grid((unsigned)B * (unsigned)G), block(kSliceThreads);
         const int wl = get_wait_limit();
-        if (bf16) {
-            if (vec16)
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, true>), grid, block, 0, stream, zt, zd, K, V, G,
-                                   Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
-            else
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<true, false>), grid, block, 0, stream, zt, zd, K, V, G,
-                                   Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
-        } else {
-            if (vec16)
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, true>), grid, block, 0, stream, zt, zd, K, V,
-                                   G, Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
-            else
-                hipLaunchKernelGGL((accept_logits_sliced_kernel<false, false>), grid, block, 0, stream, zt, zd, K, V,
-                                   G, Ls, c, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
-        }
+        if (vec16)
+            hipLaunchKernelGGL((accept_logits_sliced_kernel<BF16, true, LSE>), grid, block, 0, stream, zt, zd, K, V, G,
+                               Ls, c, draft_lse, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
+        else
+            hipLaunchKernelGGL((accept_logits_sliced_kernel<BF16, false, LSE>), grid, block, 0, stream, zt, zd, K, V,
+                               G, Ls, c, draft_lse, tokens, lens, uniforms, n_accepted, next_token, slots, wl);
         return hipGetLastError();
     }
     int m, nseg;
     segment_shape(V, m, nseg);
     const size_t lds = (size_t)nseg * sizeof(double);
-    if (bf16) {
-        if (vec)
-            hipLaunchKernelGGL((accept_logits_kernel<true, true>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K, V,
-                               m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
-        else
-            hipLaunchKernelGGL((accept_logits_kernel<true, false>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
-                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((accept_logits_kernel<false, true>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
-                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
-        else
-            hipLaunchKernelGGL((accept_logits_kernel<false, false>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
-                               V, m, nseg, c, tokens, lens, uniforms, n_accepted, next_token);
-    }
+    if (vec)
+        hipLaunchKernelGGL((accept_logits_kernel<BF16, true, LSE>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K, V,
+                           m, nseg, c, draft_lse, tokens, lens, uniforms, n_accepted, next_token);
+    else
+        hipLaunchKernelGGL((accept_logits_kernel<BF16, false, LSE>), dim3(B), dim3(kThreads), lds, stream, zt, zd, K,
+                           V, m, nseg, c, draft_lse, tokens, lens, uniforms, n_accepted, next_token);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
+                                const float* draft_lse, const int32_t* tokens, const int32_t* lens,
+                                const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    const float c = 1.4426950408889634f / temperature;
+    if (bf16)
+        return draft_lse ? launch_accept_logits_t<true, true>(zt, zd, B, K, V, c, draft_lse, tokens, lens, uniforms,
+                                                              n_accepted, next_token, workspace, workspace_bytes, stream)
+                         : launch_accept_logits_t<true, false>(zt, zd, B, K, V, c, nullptr, tokens, lens, uniforms,
+                                                               n_accepted, next_token, workspace, workspace_bytes,
+                                                               stream);
+    return draft_lse ? launch_accept_logits_t<false, true>(zt, zd, B, K, V, c, draft_lse, tokens, lens, uniforms,
+                                                           n_accepted, next_token, workspace, workspace_bytes, stream)
+                     : launch_accept_logits_t<false, false>(zt, zd, B, K, V, c, nullptr, tokens, lens, uniforms,
+                                                            n_accepted, next_token, workspace, workspace_bytes, stream);
 }
 
 }  // namespace sv

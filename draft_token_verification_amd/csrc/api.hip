@@ -377,31 +377,52 @@ size_t sv_accept_logits_workspace_bytes(int32_t B, int32_t K, int64_t V) {
     return sv::accept_logits_workspace_bytes(B, K, (int)V);
 }
 
-sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
-                           int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
-                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-    const char* fn = "sv_accept_logits";
+// The checks and launch shared by the two verify-from-logits entry points.
+static sv_status accept_logits_common(const char* fn, const void* target_logits, const void* draft_logits, int dtype,
+                               int32_t B, int32_t K, int64_t V, float temperature, const float* draft_lse,
+                               bool lse_required, const int32_t* draft_tokens, const int32_t* draft_lens,
+                               const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     sv_status st;
     if ((st = check_dtype(dtype)) != SV_OK) return st;
     if ((st = check_sizes(fn, B, K, V)) != SV_OK) return st;
     if (!(temperature > 0.0f) || !std::isfinite(temperature))
         return fail(SV_ERR_INVALID_ARG, "%s: temperature %g must be finite and > 0", fn, (double)temperature);
     if (B == 0) return ok();
-    if (!target_logits || !uniforms || !n_accepted || !next_token || (K > 0 && (!draft_logits || !draft_tokens)))
+    if (!target_logits || !uniforms || !n_accepted || !next_token ||
+        (K > 0 && (!draft_logits || !draft_tokens || (lse_required && !draft_lse))))
         return fail(SV_ERR_INVALID_ARG, "%s: null required pointer", fn);
     const size_t es = dtype_bytes(dtype);
     if (!aligned(target_logits, es) || (draft_logits && !aligned(draft_logits, es)) || !aligned(uniforms, 4) ||
         !aligned(n_accepted, 4) || !aligned(next_token, 4) || (draft_tokens && !aligned(draft_tokens, 4)) ||
-        (draft_lens && !aligned(draft_lens, 4)))
+        (draft_lens && !aligned(draft_lens, 4)) || (draft_lse && !aligned(draft_lse, 4)))
         return fail(SV_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     if ((st = check_workspace(fn, workspace, workspace_bytes, sv::accept_logits_workspace_bytes(B, K, (int)V))) !=
         SV_OK)
         return st;
     if ((st = check_device()) != SV_OK) return st;
     return launched(fn, sv::launch_accept_logits(target_logits, draft_logits, dtype == SV_BF16, B, K, (int)V,
-                                                 temperature, draft_tokens, draft_lens, uniforms, n_accepted,
-                                                 next_token, workspace, workspace_bytes, (hipStream_t)stream));
+                                                 temperature, K > 0 ? draft_lse : nullptr, draft_tokens, draft_lens,
+                                                 uniforms, n_accepted, next_token, workspace, workspace_bytes,
+                                                 (hipStream_t)stream));
+}
+
+sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
+                           int64_t V, float temperature, const int32_t* draft_tokens, const int32_t* draft_lens,
+                           const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return accept_logits_common("sv_accept_logits", target_logits, draft_logits, dtype, B, K, V, temperature, nullptr,
+                                false, draft_tokens, draft_lens, uniforms, n_accepted, next_token, workspace,
+                                workspace_bytes, stream);
+}
+
+sv_status sv_accept_logits_lse(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
+                               int64_t V, float temperature, const float* draft_lse, const int32_t* draft_tokens,
+                               const int32_t* draft_lens, const float* uniforms, int32_t* n_accepted,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream) {
+    return accept_logits_common("sv_accept_logits_lse", target_logits, draft_logits, dtype, B, K, V, temperature,
+                                draft_lse, true, draft_tokens, draft_lens, uniforms, n_accepted, next_token,
+                                workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -25,10 +25,12 @@ hipError_t launch_accept(const float* p, const float* q, int B, int K, int V, co
 // With a workspace of at least accept_logits_workspace_bytes(B, K, V) bytes
 // (8-byte aligned), each sequence is split over several workgroups; otherwise
 // one workgroup per sequence.
+// draft_lse (may be null): the draft rows' log-normalisers at the temperature,
+// [B, K]; given, the draft rows are read only at the rejected position.
 hipError_t launch_accept_logits(const void* zt, const void* zd, bool bf16, int B, int K, int V, float temperature,
-                                const int32_t* tokens, const int32_t* lens, const float* uniforms,
-                                int32_t* n_accepted, int32_t* next_token, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const float* draft_lse, const int32_t* tokens, const int32_t* lens,
+                                const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 // 0 when one workgroup per sequence is used regardless (short rows).
 size_t accept_logits_workspace_bytes(int B, int K, int V);

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 3
+#define SV_ABI_VERSION 4
 #define SV_MAX_K 64 /* draft lengths up to 64, one wavefront lane per position */
 
 typedef enum {
@@ -447,10 +447,47 @@ sv_status sv_accept_logits(const void* target_logits, const void* draft_logits, 
                            const float* uniforms, int32_t* n_accepted, int32_t* next_token, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sv_accept_logits uses for these sizes (0 when it uses one
- * workgroup per sequence regardless: rows of at most 32768 elements, or
- * more than 2048 sequences). */
+/* Workspace bytes sv_accept_logits and sv_accept_logits_lse use for these
+ * sizes, the larger need of the two dtypes (0 when they use one workgroup per
+ * sequence regardless: rows that fit one slice of 6144 fp32 or 12288 bf16
+ * logits in either dtype, or need more than 64 slices in both). */
 size_t sv_accept_logits_workspace_bytes(int32_t B, int32_t K, int64_t V);
+
+/*
+ * sv_accept_logits_lse -- sv_accept_logits with each draft row's distribution
+ * given by its normaliser, for callers whose draft model has it already (it
+ * computes the normaliser when it samples t_i from the row).
+ *
+ * The pages define q_i as the draft model's distribution at position i, the
+ * one t_i was sampled from (spec-verify card, "Method"; llmstudio blog,
+ * sections 15-17 and 21-22). Here it is
+ *   q_i(x) = exp(draft_logits[b, i, x] / T - draft_lse[b, i]),
+ * taken as given, in the accept ratio and in the residual alike. With the
+ * row's true log-sum-exp, log sum_x exp(draft_logits[b, i, x] / T), the result
+ * is sv_accept_logits' up to the rounding of the value passed in (relative
+ * |lse| * 6e-8 on q); a different value scales q_i, and the verify follows
+ * that scaled q_i. Only the target rows' statistics are computed: a draft row
+ * is read at the accept test's one logit z_d,i(t_i) per examined position,
+ * and whole only at the rejected position (for the residual), so a round
+ * reads about (n_b + 1) target rows and one draft row per sequence.
+ *
+ * draft_lse    device fp32 [B, K], row-major (position i of sequence b at
+ *              b * K + i), borrowed: the natural-log normaliser of draft row
+ *              (b, i) at `temperature`. Entries past K_b are not read. Not
+ *              finite: +inf (q_i = 0) and NaN (q_i NaN, not positive) accept
+ *              t_i unless p_i(t_i) = 0; -inf (q_i = +inf) rejects it. A
+ *              rejection at a position whose entry is not finite draws from
+ *              max(0, p_n) (no residual mass).
+ *              May be null only when B == 0 or K == 0. 4-byte aligned.
+ * Every other argument, the workspace and the accuracy are as for
+ * sv_accept_logits.
+ * Errors: as sv_accept_logits, plus SV_ERR_INVALID_ARG for a null draft_lse
+ * when K > 0.
+ */
+sv_status sv_accept_logits_lse(const void* target_logits, const void* draft_logits, int dtype, int32_t B, int32_t K,
+                               int64_t V, float temperature, const float* draft_lse, const int32_t* draft_tokens,
+                               const int32_t* draft_lens, const float* uniforms, int32_t* n_accepted,
+                               int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sv_commit -- append one verify round to each sequence's token buffer on the

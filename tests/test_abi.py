@@ -30,7 +30,8 @@ def sv():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_accept_logits_workspace_bytes",
+    assert declared_functions() == ["sv_abi_version", "sv_accept", "sv_accept_logits", "sv_accept_logits_lse",
+                                    "sv_accept_logits_workspace_bytes",
                                     "sv_apply_penalties", "sv_apply_penalties_workspace_bytes",
                                     "sv_commit", "sv_gate_choose",
                                     "sv_gate_update",
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_symbol(sv):
 
 def test_constants_match_header(sv):
     text = open(HEADER).read()
-    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 3
+    assert int(re.search(r"#define SV_ABI_VERSION (\d+)", text).group(1)) == sv.abi_version() == 4
     assert int(re.search(r"#define SV_MAX_K (\d+)", text).group(1)) == sv.SV_MAX_K
     assert re.search(r"SV_F32 = 0", text) and re.search(r"SV_BF16 = 1", text)
     for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARG"), (2, "SV_ERR_UNSUPPORTED"), (3, "SV_ERR_HIP"),
@@ -168,6 +169,28 @@ def test_greedy_lookahead_checks_its_arguments(sv):
 def test_accept_logits_rejects_bad_arguments(sv, args, fragment):
     assert sv._lib.sv_accept_logits(*args) == 1
     assert fragment in sv._lib.sv_last_error().decode()
+    # the same checks with given draft normalisers (draft_lse after the temperature)
+    with_lse = args[:7] + (FAKE,) + args[7:]
+    assert sv._lib.sv_accept_logits_lse(*with_lse) == 1
+    assert fragment in sv._lib.sv_last_error().decode()
+
+
+def test_accept_logits_lse_checks_its_normalisers(sv):
+    """draft_lse is required when K > 0 (not for K = 0 or an empty batch), must be
+    4-byte aligned, and an undersized workspace is SV_ERR_WORKSPACE as for
+    sv_accept_logits; all before any device is looked for."""
+    lib = sv._lib
+    assert lib.sv_accept_logits_lse(FAKE, FAKE, 1, 2, 4, 100, 1.0, None, FAKE, None, FAKE, FAKE, FAKE, None, 0,
+                                    None) == 1
+    assert "null" in lib.sv_last_error().decode()
+    assert lib.sv_accept_logits_lse(FAKE, FAKE, 1, 2, 4, 100, 1.0, ODD, FAKE, None, FAKE, FAKE, FAKE, None, 0,
+                                    None) == 1
+    assert "misaligned" in lib.sv_last_error().decode()
+    assert lib.sv_accept_logits_lse(None, None, 1, 0, 4, 100, 1.0, None, None, None, None, None, None, None, 0,
+                                    None) == 0
+    need = sv.sv_accept_logits_workspace_bytes(64, 4, 256000)
+    assert lib.sv_accept_logits_lse(FAKE, FAKE, 1, 64, 4, 256000, 1.0, FAKE, FAKE, None, FAKE, FAKE, FAKE, ALIGNED,
+                                    need // 2, None) == 4
 
 
 @pytest.mark.parametrize("args,fragment", [

@@ -12,7 +12,8 @@ bf16 and fp32, and several temperatures. Every case goes through:
     "Method"; the margin as the oracle's top1 - top2 in fp32);
   - sv_softmax_warp: within 1e-5 absolute on live rows, dead rows untouched;
   - sv_accept on the oracle's probabilities and sv_accept_logits on the
-    logits: the sampled parity bar of tests/sampled_check.py;
+    logits, also with the draft rows' normalisers given: the sampled parity
+    bar of tests/sampled_check.py;
   - sv_softmax_warp_filtered with random top-k / top-p: the filtered-warp
     check of tests/test_gpu_filtered.py;
   - sv_apply_penalties with a random committed history: bit-exact.
@@ -123,6 +124,16 @@ def test_random_shapes(sv, seed):
     compare_sampled(host(n).numpy(), host(nx).numpy(),
                     lambda w: oracle.accept_logits(zt_h, zd_h, tokens, uniforms, lens, T, rel_window=w),
                     label + " accept_logits")
+
+    # the same with the draft rows' normalisers given (fp64 log-sum-exp on the CPU, rounded to fp32)
+    if K > 0:
+        lse = torch.logsumexp(zd_h.double() / T, -1).float()
+        n, nx = sv.sv_accept_logits(zt_d, zd_d, tok_d, u_d, T, lens_d, draft_lse=lse.cuda())
+        torch.cuda.synchronize()
+        compare_sampled(host(n).numpy(), host(nx).numpy(),
+                        lambda w: oracle.accept_logits(zt_h, zd_h, tokens, uniforms, lens, T, rel_window=w,
+                                                       draft_lse=lse),
+                        label + " accept_logits_lse")
 
     # the filtered warp, top-k / top-p drawn per sequence (0 and 1.0: off)
     tk = torch.from_numpy(rng.choice([0, 1, 2, 5, 50, V, V + 1], B).astype(np.int32))
