@@ -14,8 +14,9 @@ Every mode is timed twice with HIP events on the stream the kernels run on:
 together, so that no call finds its inputs in the L2 caches or the MALL; and
 "resident", calling on one copy over and over. ``value`` is the whole step's
 hbm rounds/s. ``modes`` gives rounds/s per mode (greedy round, sampled round
-through the warps, sampled round fused from logits, the filtered warps and the
-penalty stage), each with its bytes needed (what the method must move) and,
+through the warps, sampled round fused from logits -- also with the draft
+rows' normalisers given -- the filtered warps and the penalty stage), each
+with its bytes needed (what the method must move) and,
 when rocprofv3 counters of these sources are on file, its bytes read, both as
 GB/s and as fractions of MI355X's 8 TB/s; the greedy round is also timed at
 look-ahead depths L = 1, 2 and K + 1 (rows read ahead of the decision), with
@@ -131,7 +132,14 @@ def main():
     p = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev) if logits else None
     q = torch.empty((B, K, V), dtype=torch.float32, device=dev) if logits else None
     o = {m: (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
-         for m in ("greedy", "sampled", "fused")}
+         for m in ("greedy", "sampled", "fused", "fused_lse")}
+    # each draft row's normaliser log sum_x exp(z_d / T): an input the draft model has when it
+    # samples (the same for every copy of the inputs); fp64 in torch, rounded to fp32
+    lse = None
+    if logits and K > 0:
+        lse = torch.empty((B, K), dtype=torch.float32, device=dev)
+        for b0 in range(0, B, 32):
+            lse[b0:b0 + 32] = torch.logsumexp(batch.draft[b0:b0 + 32].double() / T, -1).float()
 
     # the modes, each a function of the input copy it reads
     def greedy(c):
@@ -157,6 +165,10 @@ def main():
         sv.sv_accept_logits(rot.target[c], rot.draft[c], rot.tokens[c], rot.uniforms[c], T, rot.lens[c],
                             out=o["fused"])
 
+    def fused_lse(c):
+        sv.sv_accept_logits(rot.target[c], rot.draft[c], rot.tokens[c], rot.uniforms[c], T, rot.lens[c],
+                            out=o["fused_lse"], draft_lse=lse)
+
     def step(c):  # one pass of the whole hot path: both warps, the sampled verify, the greedy verify
         sampled_warps(c)
         greedy(c)
@@ -177,6 +189,8 @@ def main():
     modes = {"step": step, "greedy": greedy, "sampled_warps": sampled_warps}
     if logits:
         modes["sampled_fused"] = fused
+    if lse is not None:
+        modes["sampled_fused_lse"] = fused_lse
     ms = {m: measure(fn) for m, fn in modes.items()}
 
     # the step's kernels one by one (HBM copies): events between the launches
@@ -271,6 +285,17 @@ def main():
             "sampled_fused", *ms["sampled_fused"], needed=fused_bytes,
             read=read_bytes("accept_logits_sliced_kernel") or read_bytes("accept_logits_kernel"),
             mean_n=round(float(n_f.mean()), 4))
+    if lse is not None:
+        n_l = o["fused_lse"][0].cpu().numpy().astype(np.int64)
+        # target rows 0..n, the draft row n at a rejection, one draft logit per examined position,
+        # the normalisers of the examined positions
+        examined = np.minimum(n_l + 1, kb)
+        lse_bytes = int(((n_l + 1 + (n_l < kb)) * V * elem + examined * (elem + 4)).sum()) + 4 * B * (2 * K + 1) \
+            + 8 * B
+        modes_out["sampled_fused_lse"] = mode_record(
+            "sampled_fused_lse", *ms["sampled_fused_lse"], needed=lse_bytes,
+            read=read_bytes("accept_logits_sliced_kernel_lse") or read_bytes("accept_logits_kernel_lse"),
+            mean_n=round(float(n_l.mean()), 4), same_as_fused=bool((n_l == n_f).all()))
     step_hbm, step_res = ms["step"]
     modes_out["step"] = mode_record("step", step_hbm, step_res, needed=sw_needed + greedy_bytes)
 
@@ -413,6 +438,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
     kernel_re = re.compile(r"\b(warp_coop_kernel|warp_rows_kernel|warp_filter_kernel|accept_kernel|"
                            r"accept_logits_kernel|accept_logits_sliced_kernel|greedy_kernel|greedy_sliced_kernel|"
                            r"penalty_table_kernel|penalty_rows_kernel|fill_slots|fill_empty)\b")
+    lse_re = re.compile(r"accept_logits(?:_sliced)?_kernel(?:<\w+, \w+, true>|ILb[01]ELb[01]ELb1E)")
 
     def load(path, counter):
         per, copy = {}, []
@@ -422,7 +448,10 @@ def traffic_from_counters(fetch_csv, write_csv, workload, out_path):
             v = float(r["Counter_Value"]) * 1024.0
             m = kernel_re.search(r["Kernel_Name"])
             if m:
-                per.setdefault((m.group(1), int(r["Grid_Size"])), []).append(v)
+                k = m.group(1)
+                if k.startswith("accept_logits") and lse_re.search(r["Kernel_Name"]):
+                    k += "_lse"  # the instantiation with given draft normalisers
+                per.setdefault((k, int(r["Grid_Size"])), []).append(v)
             elif "copyBuffer" in r["Kernel_Name"]:  # the runtime's device-to-device copy
                 copy.append(v)
         big = [v for v in copy if v > 0.25 * COPY_BYTES]  # the calibration copies, not small transfers
