@@ -1,8 +1,11 @@
 // round_trip.cpp -- a caller of libspecverify through its C ABI alone, with no
-// Python in between: a seeded batch of fp32 logits, the greedy verify, and the
+// Python in between: a seeded batch of fp32 logits, the greedy verify, the
 // sampled round (sv_softmax_warp on the target and the draft rows, then
-// sv_accept), each checked against the fp64 oracle (oracle/sv_oracle.h, linked
-// here as test infrastructure), then timed back to back with HIP events.
+// sv_accept), the same round fused (sv_accept_logits) and fused with the draft
+// rows' normalisers given (sv_accept_logits_lse, the normalisers computed here
+// as the draft model's sampler would), each checked against the fp64 oracle
+// (oracle/sv_oracle.h, linked here as test infrastructure), then timed back to
+// back with HIP events.
 //
 // usage: round_trip B K V seed reps
 // Prints one JSON line; exits 1 on a mismatch, 2 on a library or HIP error.
@@ -108,8 +111,18 @@ int main(int argc, char** argv) {
         }
     }
     for (auto& x : u) x = (float)rng.uniform();
+    // each draft row's normaliser log sum_x exp(z / T), in binary64 (what the draft
+    // model's sampler computes when it draws from the row)
+    std::vector<float> lse((size_t)B * K);
+    for (size_t r = 0; r < lse.size(); ++r) {
+        const float* row = &zd[r * V];
+        double m = -INFINITY, s = 0.0;
+        for (int64_t x = 0; x < V; ++x) m = std::fmax(m, (double)row[x] / T);
+        for (int64_t x = 0; x < V; ++x) s += std::exp((double)row[x] / T - m);
+        lse[r] = (float)(m + std::log(s));
+    }
 
-    float *d_zt = to_device(zt), *d_zd = to_device(zd), *d_u = to_device(u);
+    float *d_zt = to_device(zt), *d_zd = to_device(zd), *d_u = to_device(u), *d_lse = to_device(lse);
     int32_t *d_tok = to_device(tok), *d_lens = to_device(lens);
     int32_t *d_n = nullptr, *d_nx = nullptr;
     HIP_OK(hipMalloc(&d_n, B * sizeof(int32_t)));
@@ -119,12 +132,14 @@ int main(int argc, char** argv) {
     HIP_OK(hipMalloc(&d_q, zd.size() * sizeof(float)));
     const size_t ws_g = sv_verify_greedy_workspace_bytes(B, K, V);
     const size_t ws_w = sv_softmax_warp_workspace_bytes(B, K + 1, V);
-    void *d_wg = nullptr, *d_ww = nullptr;
+    const size_t ws_f = sv_accept_logits_workspace_bytes(B, K, V);
+    void *d_wg = nullptr, *d_ww = nullptr, *d_wf = nullptr;
     if (ws_g) {
         HIP_OK(hipMalloc(&d_wg, ws_g));
         HIP_OK(hipMemset(d_wg, 0, ws_g));  // the greedy workspace holds zeros before its first use
     }
     if (ws_w) HIP_OK(hipMalloc(&d_ww, ws_w));
+    if (ws_f) HIP_OK(hipMalloc(&d_wf, ws_f));  // contents irrelevant: the call initialises its slots
     hipStream_t st;
     HIP_OK(hipStreamCreate(&st));
 
@@ -135,6 +150,27 @@ int main(int argc, char** argv) {
         SV_OK(sv_softmax_warp(d_zt, SV_F32, B, K + 1, V, d_lens, 1, T, d_p, d_ww, ws_w, st));
         SV_OK(sv_softmax_warp(d_zd, SV_F32, B, K, V, d_lens, 0, T, d_q, d_ww, ws_w, st));
         SV_OK(sv_accept(d_p, d_q, B, K, V, d_tok, d_lens, d_u, d_n, d_nx, st));
+    };
+    auto fused = [&]() {
+        SV_OK(sv_accept_logits(d_zt, d_zd, SV_F32, B, K, V, T, d_tok, d_lens, d_u, d_n, d_nx, d_wf, ws_f, st));
+    };
+    auto fused_lse = [&]() {
+        SV_OK(sv_accept_logits_lse(d_zt, d_zd, SV_F32, B, K, V, T, d_lse, d_tok, d_lens, d_u, d_n, d_nx, d_wf, ws_f,
+                                   st));
+    };
+    // sampled results against the oracle's (1e-7 flags): a ratio flag exempts the
+    // whole sequence, a CDF flag its drawn id
+    auto sampled_diff = [&](const std::vector<int32_t>& n, const std::vector<int32_t>& nx,
+                            const std::vector<int32_t>& n_o, const std::vector<int32_t>& nx_o,
+                            const std::vector<int32_t>& fl, int& flagged) {
+        int diff = 0;
+        flagged = 0;
+        for (int b = 0; b < B; ++b) {
+            const bool ratio = fl[b] & OR_FLAG_RATIO, cdf = fl[b] & OR_FLAG_CDF;
+            flagged += ratio || cdf;
+            if (!ratio && (n[b] != n_o[b] || (!cdf && nx[b] != nx_o[b]))) ++diff;
+        }
+        return diff;
     };
 
     // parity
@@ -151,12 +187,17 @@ int main(int argc, char** argv) {
     nx = to_host(d_nx, B);
     or_accept_logits(zt.data(), zd.data(), OR_F32, B, K, V, T, tok.data(), lens.data(), u.data(), OR_F32, 1e-7,
                      n_o.data(), nx_o.data(), fl.data());
-    int sampled_diff = 0, flagged = 0;
-    for (int b = 0; b < B; ++b) {
-        const bool ratio = fl[b] & OR_FLAG_RATIO, cdf = fl[b] & OR_FLAG_CDF;
-        flagged += ratio || cdf;
-        if (!ratio && (n[b] != n_o[b] || (!cdf && nx[b] != nx_o[b]))) ++sampled_diff;
-    }
+    int flagged = 0, flagged_lse = 0, unused = 0;
+    const int sampled_d = sampled_diff(n, nx, n_o, nx_o, fl, flagged);
+    fused();
+    HIP_OK(hipStreamSynchronize(st));
+    const int fused_d = sampled_diff(to_host(d_n, B), to_host(d_nx, B), n_o, nx_o, fl, unused);
+    fused_lse();
+    HIP_OK(hipStreamSynchronize(st));
+    std::vector<int32_t> n_l(B), nx_l(B), fl_l(B);
+    or_accept_logits_lse(zt.data(), zd.data(), OR_F32, B, K, V, T, lse.data(), tok.data(), lens.data(), u.data(),
+                         OR_F32, 1e-7, n_l.data(), nx_l.data(), fl_l.data());
+    const int fused_lse_d = sampled_diff(to_host(d_n, B), to_host(d_nx, B), n_l, nx_l, fl_l, flagged_lse);
 
     // latency: rounds issued back to back from C
     hipEvent_t e0, e1;
@@ -172,9 +213,12 @@ int main(int argc, char** argv) {
         HIP_OK(hipEventElapsedTime(&ms, e0, e1));
         return 1000.0 * ms / reps;
     };
-    const double g_us = time_us(greedy), s_us = time_us(sampled);
+    const double g_us = time_us(greedy), s_us = time_us(sampled), f_us = time_us(fused), l_us = time_us(fused_lse);
     std::printf("{\"B\": %d, \"K\": %d, \"V\": %lld, \"greedy_round_us\": %.2f, \"sampled_round_us\": %.2f, "
-                "\"greedy_mismatches\": %d, \"sampled_mismatches\": %d, \"sampled_flagged\": %d}\n",
-                B, K, (long long)V, g_us, s_us, greedy_diff, sampled_diff, flagged);
-    return greedy_diff || sampled_diff ? 1 : 0;
+                "\"fused_round_us\": %.2f, \"fused_lse_round_us\": %.2f, \"greedy_mismatches\": %d, "
+                "\"sampled_mismatches\": %d, \"fused_mismatches\": %d, \"fused_lse_mismatches\": %d, "
+                "\"sampled_flagged\": %d, \"fused_lse_flagged\": %d}\n",
+                B, K, (long long)V, g_us, s_us, f_us, l_us, greedy_diff, sampled_d, fused_d, fused_lse_d, flagged,
+                flagged_lse);
+    return greedy_diff || sampled_d || fused_d || fused_lse_d ? 1 : 0;
 }

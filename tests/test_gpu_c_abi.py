@@ -1,7 +1,8 @@
 """The C ABI from a C++ caller with no Python in between (tests/c_abi/round_trip.cpp,
-built by __graft_entry__.build()): the greedy verify bit-exact and the sampled
-round (both warps, then sv_accept) equal to the fp64 oracle except where the
-oracle flags a boundary within 1e-7, then both rounds timed back to back from
+built by __graft_entry__.build()): the greedy verify bit-exact, and the sampled
+round three ways (both warps then sv_accept; sv_accept_logits; sv_accept_logits_lse
+with normalisers the program computes) equal to the fp64 oracle except where the
+oracle flags a boundary within 1e-7, then every round timed back to back from
 C. The printed latencies are what a native caller sees: kernel time plus the
 HIP launch, without the binding's argument marshalling."""
 import json
@@ -39,3 +40,5 @@ def test_round_trip(binary, B, K, V, seed):
     line = json.loads(r.stdout.strip().splitlines()[-1])
     print(f"[c-abi] {line}", flush=True)
     assert line["greedy_mismatches"] == 0 and line["sampled_mismatches"] == 0
+    assert line["fused_mismatches"] == 0 and line["fused_lse_mismatches"] == 0
+    assert line["sampled_flagged"] <= max(1, B // 100) and line["fused_lse_flagged"] <= max(1, B // 100)
