@@ -29,7 +29,7 @@ from tests.test_gpu_filtered import check as check_filtered
 pytestmark = pytest.mark.gpu
 
 VOCABS = [1, 2, 3, 5, 8, 31, 64, 100, 1000, 4097, 6145, 12289, 32768, 32771, 40000, 65537, 70001]
-CASES = 96
+CASES = 256
 
 
 @pytest.fixture(scope="module")
