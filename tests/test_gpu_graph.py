@@ -25,23 +25,25 @@ def sv():
     return sv
 
 
-def round_calls(sv, b, toks, u, outs, T):
+def round_calls(sv, b, toks, u, outs, T, lse):
     """The calls of one verify round on logits, writing into `outs`."""
     lens = b.lens
-    p, q, ng, xg, mg, na, xa, nf, xf, pf = outs
+    p, q, ng, xg, mg, na, xa, nf, xf, pf, nl, xl = outs
     sv.sv_verify_greedy_margin(b.target, toks, lens, out=(ng, xg, mg))
     sv.sv_softmax_warp(b.target, T, lens, 1, out=p)
     sv.sv_softmax_warp(b.draft, T, lens, 0, out=q)
     sv.sv_accept(p, q, toks, u, lens, out=(na, xa))
     sv.sv_accept_logits(b.target, b.draft, toks, u, T, lens, out=(nf, xf))
     sv.sv_softmax_warp_filtered(b.target, T, lens, 1, 50, 0.9, out=pf)
+    sv.sv_accept_logits(b.target, b.draft, toks, u, T, lens, out=(nl, xl), draft_lse=lse)
 
 
 def new_outputs(b, dev):
     B, K, V = b.B, b.K, b.V
     i32 = lambda: torch.full((B,), -7, dtype=torch.int32, device=dev)
     return (torch.zeros((B, K + 1, V), device=dev), torch.zeros((B, K, V), device=dev), i32(), i32(),
-            torch.zeros(B, device=dev), i32(), i32(), i32(), i32(), torch.zeros((B, K + 1, V), device=dev))
+            torch.zeros(B, device=dev), i32(), i32(), i32(), i32(), torch.zeros((B, K + 1, V), device=dev), i32(),
+            i32())
 
 
 @pytest.mark.parametrize("case", [
@@ -55,17 +57,18 @@ def test_captured_round_replays_like_eager(sv, case):
     T = b.temperature
     toks = b.tokens.clone()
     u = b.uniforms.clone()
+    lse = torch.logsumexp(b.draft.double() / T, -1).float()  # the draft rows' normalisers (inputs)
     cap_out = new_outputs(b, dev)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for _ in range(2):  # warm up on the capture stream (workspaces, lazy set-up)
-            round_calls(sv, b, toks, u, cap_out, T)
+            round_calls(sv, b, toks, u, cap_out, T, lse)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        round_calls(sv, b, toks, u, cap_out, T)
+        round_calls(sv, b, toks, u, cap_out, T, lse)
     torch.cuda.synchronize()
     for rep in range(3):
         # new inputs in the captured buffers: draft tokens that follow the target's argmax for a few
@@ -77,12 +80,12 @@ def test_captured_round_replays_like_eager(sv, case):
         toks.copy_(t_new)
         u.copy_(r.uniforms)
         eager_out = new_outputs(b, dev)
-        round_calls(sv, b, toks, u, eager_out, T)   # eager, on the default stream
+        round_calls(sv, b, toks, u, eager_out, T, lse)   # eager, on the default stream
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         names = ["p", "q", "greedy n", "greedy next", "margin", "accept n", "accept next", "fused n", "fused next",
-                 "filtered p"]
+                 "filtered p", "fused (given normalisers) n", "fused (given normalisers) next"]
         for nm, a, e in zip(names, cap_out, eager_out):
             assert torch.equal(a, e), f"{name}: replay {rep}: {nm} differs from the eager call"
         print(f"[{name}] replay {rep}: all outputs equal the eager round "
@@ -100,23 +103,25 @@ def test_replay_after_the_stream_needs_a_larger_workspace(sv):
     small = synth.generate(name, dev, B=8)
     big = synth.generate(name, dev, B=64, seed=77)
     T = small.temperature
+    lse_s = torch.logsumexp(small.draft.double() / T, -1).float()
+    lse_b = torch.logsumexp(big.draft.double() / T, -1).float()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     outs = new_outputs(small, dev)
     with torch.cuda.stream(s):
-        round_calls(sv, small, small.tokens, small.uniforms, outs, T)
+        round_calls(sv, small, small.tokens, small.uniforms, outs, T, lse_s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        round_calls(sv, small, small.tokens, small.uniforms, outs, T)
+        round_calls(sv, small, small.tokens, small.uniforms, outs, T, lse_s)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):  # needs larger workspaces on the same stream
         big_outs = new_outputs(big, dev)
-        round_calls(sv, big, big.tokens, big.uniforms, big_outs, T)
+        round_calls(sv, big, big.tokens, big.uniforms, big_outs, T, lse_b)
         filler = [torch.full((1 << 20,), 3.0, device=dev) for _ in range(8)]  # memory the allocator hands out now
     torch.cuda.synchronize()
     eager = new_outputs(small, dev)
-    round_calls(sv, small, small.tokens, small.uniforms, eager, T)
+    round_calls(sv, small, small.tokens, small.uniforms, eager, T, lse_s)
     for rep in range(2):
         g.replay()
         torch.cuda.synchronize()
