@@ -6,7 +6,9 @@ and ragged or out-of-range per-sequence lengths, vocabularies from 1 id to past
 the thresholds where each kernel switches mapping (the split greedy walk above
 128 KB rows, the split fused verify above one 12288- or 6144-logit slice, the
 cooperative warp for V a multiple of 4), rows starting off the 16-byte grid,
-bf16 and fp32, and several temperatures. Every case goes through:
+bf16 and fp32, and several temperatures. A second sweep takes vocabularies of
+128256 to 2^20 ids with small batches, where the split kernels use many
+slices. Every case goes through:
   - sv_verify_greedy and sv_verify_greedy_margin, with and without a
     workspace, at a random look-ahead depth: bit-exact (spec-verify card,
     "Method"; the margin as the oracle's top1 - top2 in fp32);
@@ -65,9 +67,41 @@ def on_device(a, dtype, offset):
     return buf[offset:].view(t.shape)
 
 
+LARGE_VOCABS = [128256, 152064, 256000, 262147, 524288, 786431, 1048576]
+LARGE_CASES = 28
+
+
+def draw_large_case(seed):
+    """Vocabularies of real models and past them (up to the filtered warp's kept-quad map limit of 2^20),
+    where the split kernels use many slices (greedy and the fused verify up to 64), small batches.
+
+    Logit scales of 3 and 8 only: over 2^20 ids a row of scale 0.5 is nearly flat, every id carries
+    about 1e-6 of the mass, and the 1e-7 audit window around the cumulative weights near the end of
+    the row covers a large share of the uniforms, so most draws are flagged (a property of the input,
+    not of the kernels) and such rows check little."""
+    rng = np.random.default_rng(50_000 + seed)
+    B = int(rng.integers(1, 5))
+    K = int(rng.integers(0, 9))
+    V = int(LARGE_VOCABS[seed % len(LARGE_VOCABS)])
+    dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    offset = int(rng.integers(0, 2))
+    lens = None if rng.random() < 0.3 else rng.integers(-1, K + 2, B).astype(np.int32)
+    T = float(rng.choice([0.7, 1.0, 1.6]))
+    sigma = float(rng.choice([3.0, 8.0]))
+    return rng, B, K, V, dtype, offset, lens, T, sigma
+
+
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_shapes(sv, seed):
-    rng, B, K, V, dtype, offset, lens, T, sigma = draw_case(seed)
+    check_case(sv, seed, *draw_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(LARGE_CASES))
+def test_random_large_vocab(sv, seed):
+    check_case(sv, f"large {seed}", *draw_large_case(seed))
+
+
+def check_case(sv, seed, rng, B, K, V, dtype, offset, lens, T, sigma):
     label = f"seed {seed}: B={B} K={K} V={V} {str(dtype)[6:]} offset={offset} lens={lens} T={T} sigma={sigma}"
     print(f"[random] {label}", flush=True)
     zt = (sigma * rng.standard_normal((B, K + 1, V))).astype(np.float32)
