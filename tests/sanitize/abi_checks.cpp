@@ -161,6 +161,17 @@ int main() {
         const size_t need = sv_accept_logits_workspace_bytes(64, 8, 152064);
         EXPECT(sv_accept_logits(a, a, SV_F32, 64, 8, 152064, 1.0f, i32, nullptr, f, i32, i32, a, need - 8, nullptr),
                WS);
+        // the form with given draft normalisers: the same checks, plus its own argument
+        EXPECT(sv_accept_logits_lse(a, a, SV_F32, 1, 4, 8, 0.0f, f, i32, nullptr, f, i32, i32, nullptr, 0, nullptr),
+               INV);
+        EXPECT(sv_accept_logits_lse(a, a, SV_F32, 1, 4, 8, 1.0f, nullptr, i32, nullptr, f, i32, i32, nullptr, 0,
+                                    nullptr), INV);
+        EXPECT(sv_accept_logits_lse(a, a, SV_F32, 1, 4, 8, 1.0f, (const float*)mis2, i32, nullptr, f, i32, i32,
+                                    nullptr, 0, nullptr), INV);
+        EXPECT(sv_accept_logits_lse(a, a, SV_F32, 64, 8, 152064, 1.0f, f, i32, nullptr, f, i32, i32, a, need - 8,
+                                    nullptr), WS);
+        EXPECT(sv_accept_logits_lse(nullptr, nullptr, SV_F32, 0, 4, 8, 1.0f, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, 0, nullptr), SV_OK);
     }
 
     // ---- draft-length gate ----
