@@ -71,7 +71,7 @@ def b_live_rows(b):
 
 def test_cooperative_kernels_under_contention(sv):
     """Throughput of the kernels whose workgroups exchange partial results (warp,
-    split greedy, split fused verify) while another stream keeps the compute
+    split greedy, split fused verify, also with given draft normalisers) while another stream keeps the compute
     units and HBM busy with a large elementwise kernel for the whole timed
     region. Each waits, bounded, for the other workgroups of its row or
     sequence and recomputes their share if they do not come; that recompute
@@ -84,10 +84,13 @@ def test_cooperative_kernels_under_contention(sv):
     dev = torch.device("cuda", 0)
     b = synth.generate(name, dev, B=128)
     T = b.temperature
+    lse = torch.logsumexp(b.draft.double() / T, -1).float()
     calls = {
         "warp": lambda: sv.sv_softmax_warp(b.target, T, b.lens, 1),
         "greedy": lambda: sv.sv_verify_greedy(b.target, b.tokens, b.lens),
         "fused": lambda: sv.sv_accept_logits(b.target, b.draft, b.tokens, b.uniforms, T, b.lens),
+        "fused, draft normalisers given": lambda: sv.sv_accept_logits(b.target, b.draft, b.tokens, b.uniforms, T,
+                                                                      b.lens, draft_lse=lse),
     }
     ref = {}
     for k, f in calls.items():
