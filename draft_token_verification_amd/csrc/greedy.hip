@@ -262,10 +262,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 // sequence b and reads it in one batch of loads (a 32 KB slice: one memory
 // round trip per position). At each position every slice publishes its
 // (value, index) -- and, with M, its runner-up value -- into slots of the
-// caller's workspace, and every workgroup merges all G, so all take the same
-// decision. A long chain of matches thus reads each row with G compute units
-// instead of one. Every wait is bounded: a workgroup that gives up computes
-// the missing slices itself, so the result is the same either way.
+// caller's workspace, and every workgroup decides the row from the slices'
+// words alike. A row matches only when all G words are in and none beats the
+// draft token; a miss is certain as soon as one word beats it, so at the
+// miss (the last row of most sequences) a workgroup need not wait for the
+// slowest slice. The row's argmax, the output, is then taken from all G
+// words by the last of the sequence's workgroups to finish. A long chain of
+// matches thus reads each row with G compute units instead of one. Every wait
+// is bounded: a workgroup that gives up computes the missing slices itself,
+// so the result is the same either way.
 //
 // Look-ahead (the depth L of the walk): a workgroup may read and scan its
 // slices of rows i+1 .. i+L before it waits for the other slices of row i,
@@ -274,37 +279,118 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 // never publishes a row it does not go on to gather. L = 0 is the exact
 // walk; rows read ahead of a miss are read for nothing, which costs time
 // whenever HBM is saturated. Results are the same for every L: a row is
-// still decided only from all G slices of that row.
+// still decided only from the G slices of that row.
 //
 // The workspace needs no fill before a launch: an empty slot is a zero word
 // (a published word never is: it carries index + 1, or a set low bit), and
 // every launch leaves the workspace all zero again. When a workgroup is done
 // with its sequence (every slot access finished) it counts itself out on the
-// sequence's departure counter; the last of the G clears every slot word the
-// sequence used and the counter. So a workspace must hold zeros before its
-// first use, and the next launch finds it so.
+// sequence's departure counter; the last of the G gathers the last row's
+// words, writes the outputs, and clears every slot word the sequence used
+// and the counter. So a workspace must hold zeros before its first use, and
+// the next launch finds it so.
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
 constexpr int kSliceUnroll = 8;  // 128 bytes per lane in flight: a 32 KB slice in one batch
 constexpr int kMarginUnroll = 6;  // with the runner-up values (8 would spill): the slice in two batches
 constexpr int kMaxGreedySlices = kWave;  // slice results are merged across one wavefront
 
+// Outcomes of the decision on one row.
+constexpr int kWaitedOut = 0, kRowMatch = 1, kRowMiss = 2;
+
+// Wavefront 0 polls the value words set[k * W] of the G slices of a row
+// (bounded) until the row is decided against draft token tok, whose slice is
+// gt (-1 when tok is outside [0, V): a miss). A row matches iff no element
+// beats tok in the argmax order, i.e. iff no slice's best does. So the row is
+// a miss as soon as one published word beats tok: the word of tok's own
+// slice when its best is not tok, or another slice's when its value is above
+// tok's logit (the best of tok's slice) or equal to it at a lower index. It
+// matches once all G words are published and none beats tok. The decision
+// also waits for this workgroup's own words (slice g), so that its publishes
+// are visible before it can count itself out. Returns the outcome, uniform
+// over the workgroup (kWaitedOut if the wait ran out first). Contains a
+// barrier.
+template <int W>
+__device__ int decide_row(const unsigned long long* set, int G, int g, int tok, int gt, int wait_limit, int* s_flag) {
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const unsigned long long all = G == kWave ? ~0ull : (1ull << G) - 1ull;
+        int res = kWaitedOut;
+        for (int tries = 0; tries <= wait_limit; ++tries) {
+            unsigned long long w = 0ull;
+            if (lane < G) w = __hip_atomic_load(set + lane * W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool own = true;  // the runner-up word too, when there is one
+            if (W > 1) own = __hip_atomic_load(set + g * W + W - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0ull;
+            const unsigned long long pres = __ballot(w != 0ull);
+            if (own && ((pres >> g) & 1ull)) {
+                if (gt < 0) {
+                    res = kRowMiss;
+                    break;
+                }
+                if ((pres >> gt) & 1ull) {
+                    const float v = __uint_as_float((uint32_t)(w >> 32));
+                    const int idx = (int)((uint32_t)w - 1u);
+                    if (readlane_i(idx, gt) != tok) {
+                        res = kRowMiss;
+                        break;
+                    }
+                    const float z = readlane_f(v, gt);
+                    if (__ballot((w != 0ull) & ((v > z) | ((v == z) & (idx < tok)))) != 0ull) {
+                        res = kRowMiss;
+                        break;
+                    }
+                    if (pres == all) {
+                        res = kRowMatch;
+                        break;
+                    }
+                }
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) *s_flag = res;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_flag);
+}
+
 // Wavefront 0 counts the workgroup out of its sequence once it has made its
-// last slot access; the last of the sequence's G workgroups clears the
-// sequence's `nwords` slot words and the counter, returning them to zero.
-// The count needs no fence in the common case: every gather polls the
-// workgroup's own word too, through the same device-coherent loads as the
-// others, so a workgroup's published words are visible before it counts
-// itself out, and its loads have all returned. Only a workgroup that gave up
-// waiting (`waited_out`) may still have a word in flight: it releases first.
-__device__ __forceinline__ void depart(unsigned long long* counter, unsigned long long* words, int nwords, int G,
-                                       bool waited_out) {
+// last slot access; returns (uniform) whether it was the last of the G. The
+// count needs no fence in the common case: the workgroup has seen its own
+// published words through the same device-coherent loads as the others use
+// (`own_seen`), so they are visible before it counts itself out. Otherwise
+// it polls them first (bounded), and one whose words it could not see, or
+// that gave up waiting earlier (`waited_out`), releases first.
+template <int W>
+__device__ bool count_out(unsigned long long* counter, const unsigned long long* own, int G, bool own_seen,
+                          bool waited_out, int wait_limit, int* s_flag) {
+    if (threadIdx.x < kWave) {
+        if (!own_seen && !waited_out) {
+            bool seen = false;
+            for (int tries = 0; tries <= wait_limit && !seen; ++tries) {
+                unsigned long long w = 1ull;
+                if (threadIdx.x < W) w = __hip_atomic_load(own + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                seen = __ballot(w == 0ull) == 0ull;
+                if (!seen) __builtin_amdgcn_s_sleep(2);
+            }
+            waited_out = !seen;
+        }
+        if (waited_out) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        unsigned long long prev = 0;
+        if (threadIdx.x == 0) prev = __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) *s_flag = prev == (unsigned long long)(G - 1);
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+}
+
+// The last workgroup out returns the sequence's `nwords` slot words and its
+// counter to zero (wavefront 0; every other workgroup has counted out, so no
+// slot of the sequence is accessed again in this launch).
+__device__ __forceinline__ void clear_sequence(unsigned long long* counter, unsigned long long* words, int nwords) {
     if (threadIdx.x >= kWave) return;
-    if (waited_out) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    unsigned long long prev = 0;
-    if (threadIdx.x == 0) prev = __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__shfl(prev, 0, kWave) != (unsigned long long)(G - 1)) return;
-    for (int k = threadIdx.x; k < nwords; k += kWave)
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));  // formed here: a copy kept from the kernel's start would be spilled
+    for (int k = tid; k < nwords; k += kWave)
         __hip_atomic_store(words + k, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -321,6 +407,8 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
     __shared__ unsigned long long s_words[2 * kMaxGreedySlices];
     __shared__ unsigned long long s_ahead[SV_MAX_K + 1][M ? 2 : 1];  // this slice's scanned rows, not yet published
     __shared__ int s_ready;
+    __shared__ int s_decided[2];  // alternate by position: a wavefront may still read the previous one
+    __shared__ int s_last;
     constexpr int W = M ? 2 : 1;  // words per slice and position
     const int b = blockIdx.x / G, g = blockIdx.x - b * G;
     const int lane = threadIdx.x & (kWave - 1);
@@ -347,13 +435,49 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
             if (M) s_ahead[r][W - 1] = pack2(sr);
         }
     };
-    int i = 0;
-    int scanned = 0;  // rows 0 .. scanned-1 of this slice are scanned
+    // every slice's words of row `row`, computed here alike into s_words when
+    // a bounded wait ran out (two vectors per lane in flight: a rare path,
+    // kept small)
+    auto compute_all = [&](const char* row) {
+        for (int k = 0; k < G; ++k) {
+            float vk, sk = -INFINITY;
+            const int ik =
+                span_argmax<BF16, M, kSliceWaves, 2>(row, k * Ls, slice_len(k), lds_v, lds_i, lds_s, parity, vk, sk);
+            parity ^= 1;
+            if (threadIdx.x == 0) {
+                s_words[k * W] = pack(vk, ik);
+                if (M) s_words[k * W + 1] = pack2(sk);
+            }
+        }
+        __syncthreads();
+    };
+    // merge of the G <= 64 slices' words in s_words: lane k holds slice k, the
+    // wave-wide merge (the (value, index) order is total and the runner-up is a
+    // plain maximum, so every merge order gives the same result)
     float v, s = -INFINITY;
     int am;
-    bool waited_out = false;
+    auto merge_words = [&]() {
+        v = -INFINITY;
+        am = INT32_MAX;
+        s = -INFINITY;
+        // the lane index formed here, on this rare path: a copy kept from the
+        // kernel's start would be spilled
+        int k = (int)threadIdx.x & (kWave - 1);
+        asm volatile("" : "+v"(k));
+        if (k < G) {
+            v = __uint_as_float((uint32_t)(s_words[k * W] >> 32));
+            am = (int)((uint32_t)s_words[k * W] - 1u);
+            if (M) s = __uint_as_float((uint32_t)(s_words[k * W + 1] >> 32));
+        }
+        if (M)
+            wave_top2(v, am, s);
+        else
+            wave_argmax(v, am);
+    };
+    int i = 0;
+    int scanned = 0;  // rows 0 .. scanned-1 of this slice are scanned
+    bool waited_out = false, own_seen = false;
     for (;; ++i) {
-        const char* row = base + (size_t)i * row_bytes;
         unsigned long long* set = slot_set(i);
         if (scanned == i) scan_row(scanned++);
         if (threadIdx.x == 0) {
@@ -362,49 +486,36 @@ __global__ __launch_bounds__(kSliceThreads) __attribute__((amdgpu_waves_per_eu(8
         }
         // rows up to i + L (at most K_b) read while the other slices of row i arrive
         for (const int last = min(kb, i + lookahead); scanned <= last;) scan_row(scanned++);
-        if (!gather_words(set, G * W, wait_limit, s_words, &s_ready, 0ull)) {
-            // bounded wait ran out: every slice's result, computed here alike
-            // (two vectors per lane in flight: a rare path, kept small)
-            waited_out = true;
-            for (int k = 0; k < G; ++k) {
-                float vk, sk = -INFINITY;
-                const int ik = span_argmax<BF16, M, kSliceWaves, 2>(row, k * Ls, slice_len(k), lds_v, lds_i, lds_s,
-                                                                    parity, vk, sk);
-                parity ^= 1;
-                if (threadIdx.x == 0) {
-                    s_words[k * W] = pack(vk, ik);
-                    if (M) s_words[k * W + 1] = pack2(sk);
-                }
-            }
-            __syncthreads();
+        // the last row has no draft token to test: its argmax is taken by the
+        // last workgroup out
+        if (i == kb) break;
+        const int tok = readlane_i(my_tok, i);
+        const int gt = (tok >= 0 && tok < V) ? tok / Ls : -1;  // outside [0, V): a miss
+        const int r = decide_row<W>(set, G, g, tok, gt, wait_limit, &s_decided[i & 1]);
+        if (r == kRowMatch) continue;
+        if (r == kRowMiss) {
+            own_seen = true;
+            break;
         }
-        // merge the G <= 64 slices: lane k holds slice k, the wave-wide merge
-        // (the (value, index) order is total and the runner-up is a plain
-        // maximum, so every merge order gives the same result)
-        {
-            v = -INFINITY;
-            am = INT32_MAX;
-            s = -INFINITY;
-            if (lane < G) {
-                v = __uint_as_float((uint32_t)(s_words[lane * W] >> 32));
-                am = (int)((uint32_t)s_words[lane * W] - 1u);
-                if (M) s = __uint_as_float((uint32_t)(s_words[lane * W + 1] >> 32));
-            }
-            if (M)
-                wave_top2(v, am, s);
-            else
-                wave_argmax(v, am);
-        }
-        __syncthreads();  // s_words is rewritten by the next position's gather
-        // a token outside [0, V) never equals an argmax: it is a miss
-        if (i == kb || readlane_i(my_tok, i) != am) break;
+        waited_out = true;
+        compute_all(base + (size_t)i * row_bytes);
+        merge_words();
+        __syncthreads();  // s_words is rewritten by the next position
+        if (tok != am) break;
     }
-    if (g == 0 && threadIdx.x == 0) {
+    // row i is the sequence's last: the workgroups count out, and the last one
+    // takes the row's argmax from all G slices, writes the outputs and clears
+    // the sequence's slots
+    unsigned long long* set = slot_set(i);
+    if (!count_out<W>(departed + b, set + g * W, G, own_seen, waited_out, wait_limit, &s_last)) return;
+    if (!gather_words(set, G * W, wait_limit, s_words, &s_ready, 0ull)) compute_all(base + (size_t)i * row_bytes);
+    merge_words();
+    if (threadIdx.x == 0) {
         n_accepted[b] = i;
         next_token[b] = am;
         if (M) top2_margin[b] = v - s;
     }
-    depart(departed + b, slot_set(0), (i + 1) * G * W, G, waited_out);
+    clear_sequence(departed + b, slot_set(0), (i + 1) * G * W);
 }
 
 }  // namespace
