@@ -722,16 +722,19 @@ __global__ __launch_bounds__(kThreads) void accept_logits_kernel(const void* __r
 // memory: measured on MI355X at B = 512, K = 16, V = 256000 it runs about as
 // fast with its slice loads removed. Six vectors per lane (G = 21 slices of
 // 24 KB per row there) beat four by 4% and eight (which spills) by 30%.
-// The slice's statistics, the accept test, the weights of the draw and the
-// locate of the drawn id all come from those copies, so every byte the
-// method needs is fetched once. At each position the G workgroups publish
-// their slices' statistics (m, s) of both rows into slots of the caller's
-// workspace (filled with the empty marker before the launch) and each merges
-// all G in one fixed order, so every slice takes the same decision; for the
-// draw each publishes its slice's total weight, all find the slice holding
-// u * S, and that one locates the id. Every wait is bounded: a workgroup that
-// gives up loads the missing slices and computes their values itself with
-// the same code and lane mapping, so results are bitwise identical either way.
+// The slice's statistics, the accept test and the weights of the draw all
+// come from those copies, so every byte the method needs is fetched once;
+// the one exception is the slice the drawn id lies in, which the locating
+// workgroup loads again (two slices of 24 KB per sequence). At each position
+// the G workgroups publish their slices' statistics (m, s) of both rows into
+// slots of the caller's workspace (filled with the empty marker before the
+// launch) and each merges all G in one fixed order, so every slice takes the
+// same decision. For the draw each publishes its slice's total weight and
+// counts in; the others leave, and the last to arrive sums the totals,
+// finds the slice holding u * S and locates the id there. Every wait is
+// bounded: a workgroup that gives up loads the missing slices and computes
+// their values itself with the same code and lane mapping, so results are
+// bitwise identical either way.
 
 constexpr int kSliceWaves = 4;
 constexpr int kSliceThreads = kSliceWaves * kWave;
@@ -1052,37 +1055,30 @@ __device__ __forceinline__ double word_total(unsigned long long w) {
     return __longlong_as_double((long long)(w ^ 0x8000000000000000ull));
 }
 
-// Total draw weight of the row (pair) over the G slices: this slice's total
-// (its chunks left in chunk[]) is published into set[g], all G gathered into
-// s_tot and summed in slice order (uniform). If the wait runs out, every
-// slice is loaded and summed here alike; then this slice's chunks again.
-// Called by the whole workgroup.
-template <bool BF16, bool VEC, bool D>
-__device__ double exchange_totals(const SliceCtx& x, unsigned long long* set, const char* tr, const char* dr, float c,
-                                  const RowStats& st, const Shift& k, u32x4 (&rt)[kSliceVecs], double* chunk,
-                                  double* s_tot) {
-    auto own_draft = [&](int u) { return x.draft(u); };
-    const double Sg = slice_total<BF16, D>(rt, own_draft, c, st, k, chunk);
-    publish_word(set + x.g, total_word(Sg));
-    if (gather_words(set, x.G, x.wait_limit, x.s_words, x.s_ready)) {
-        if (threadIdx.x < x.G) s_tot[threadIdx.x] = word_total(x.s_words[threadIdx.x]);
-    } else {
-        for (int kk = 0; kk < x.G; ++kk) {
-            u32x4 vd[kSliceVecs];
-            load_slice<BF16, VEC>(tr, (int64_t)kk * x.Ls, x.len(kk), rt);
-            if (D) load_slice<BF16, VEC>(dr, (int64_t)kk * x.Ls, x.len(kk), vd);
-            auto other_draft = [&](int u) { return vd[u]; };
-            const double Sk = slice_total<BF16, D>(rt, other_draft, c, st, k, chunk);
-            if (threadIdx.x == 0) s_tot[kk] = Sk;
-        }
-        // this slice again (its draft share is in LDS), and its chunks
-        load_slice<BF16, VEC>(tr, (int64_t)x.g * x.Ls, x.len(x.g), rt);
-        slice_total<BF16, D>(rt, own_draft, c, st, k, chunk);
+// The slices of a sequence count in on `counter` (filled with kEmptySlot
+// before the launch, so the k-th arrival reads kEmptySlot + k); returns,
+// uniform over the workgroup, whether this one was the last of the G.
+__device__ __forceinline__ bool last_in(unsigned long long* counter, int G, int* s_flag) {
+    if (threadIdx.x == 0) {
+        const unsigned long long prev =
+            __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev + 1ull == (unsigned long long)(G - 1);
     }
     __syncthreads();
-    double S = 0.0;
-    for (int kk = 0; kk < x.G; ++kk) S += s_tot[kk];
-    return S;
+    return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+}
+
+// This workgroup's slice k of the draw rows: target slice into rt, and with
+// D the draft slice into s_draft (each lane its own entries).
+template <bool BF16, bool VEC, bool D>
+__device__ void load_draw_slice(const SliceCtx& x, int k, const char* tr, const char* dr, u32x4 (&rt)[kSliceVecs]) {
+    load_slice<BF16, VEC>(tr, (int64_t)k * x.Ls, x.len(k), rt);
+    if (D) {
+        u32x4 v[kSliceVecs];
+        load_slice<BF16, VEC>(dr, (int64_t)k * x.Ls, x.len(k), v);
+#pragma unroll
+        for (int u = 0; u < kSliceVecs; ++u) x.s_draft[u * kSliceThreads + threadIdx.x] = v[u];
+    }
 }
 
 // Element-level locate inside vector U of the calling wavefront's lanes:
@@ -1200,8 +1196,9 @@ __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
     const char* tbase = (const char*)zt + (size_t)b * (size_t)(K + 1) * row_bytes;
     const char* dbase = (const char*)zd + (size_t)b * (size_t)K * row_bytes;
     const SliceCtx x{s_words, &s_ready, s_draft, G, g, Ls, V, wait_limit};
-    // per sequence: 2G words of draw totals (the residual's or the bonus's,
-    // then the zero-residual fallback's), then 2G words per position
+    // per sequence: G words of draw totals (the residual's or the bonus's)
+    // and the draw's arrival counter (in G words kept for it), then 2G words
+    // per position
     unsigned long long* my = slots + (size_t)b * (size_t)(2 * G) * (size_t)(K + 2);
     unsigned long long* draw_sets = my;
     unsigned long long* pos_sets = my + 2 * G;
@@ -1246,25 +1243,58 @@ __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
         }
     }
 
-    // 2. total draw weight over the slices
+    if (g == 0 && threadIdx.x == 0) n_accepted[b] = n;
+
+    // 2. this slice's total draw weight (its chunk sums stay in chunk[]) is
+    // published and the slices count in; only the last to arrive goes on. It
+    // sums the G totals in slice order and locates the drawn id, in its own
+    // slice or in the one it loads again. The others have nothing left to do.
     const Shift k0 = residual ? residual_shift(st, sd) : Shift{0.f, 0.f};
+    auto own_draft = [&](int u) { return x.draft(u); };
+    const double Sg = residual ? slice_total<BF16, true>(rt, own_draft, c, st, k0, chunk)
+                               : slice_total<BF16, false>(rt, own_draft, c, st, k0, chunk);
+    publish_word(draw_sets + g, total_word(Sg));
+    if (!last_in(draw_sets + G, G, &s_ready)) return;
+    int held = g;  // the slice whose data (rt, s_draft) and chunk sums this workgroup holds
+    if (gather_words(draw_sets, G, wait_limit, s_words, &s_ready)) {
+        if (threadIdx.x < G) s_tot[threadIdx.x] = word_total(s_words[threadIdx.x]);
+    } else {  // bounded wait ran out: every slice's total computed here alike
+        for (int k = 0; k < G; ++k) {
+            if (residual)
+                load_draw_slice<BF16, VEC, true>(x, k, trow, drow, rt);
+            else
+                load_draw_slice<BF16, VEC, false>(x, k, trow, drow, rt);
+            const double Sk = residual ? slice_total<BF16, true>(rt, own_draft, c, st, k0, chunk)
+                                       : slice_total<BF16, false>(rt, own_draft, c, st, k0, chunk);
+            if (threadIdx.x == 0) s_tot[k] = Sk;
+        }
+        held = G - 1;
+    }
+    __syncthreads();
+    double S = 0.0;
+    for (int k = 0; k < G; ++k) S += s_tot[k];
     bool bonus = !residual;
-    double S = residual ? exchange_totals<BF16, VEC, true>(x, draw_sets, trow, drow, c, st, k0, rt, chunk, s_tot)
-                        : exchange_totals<BF16, VEC, false>(x, draw_sets, trow, nullptr, c, st, k0, rt, chunk, s_tot);
     if (residual && !(S > 0.0)) {
-        // p_n == q_n: no residual mass, draw from max(0, p_n)
+        // p_n == q_n: no residual mass, draw from max(0, p_n); every slice's
+        // total computed here
         bonus = true;
-        S = exchange_totals<BF16, VEC, false>(x, draw_sets + G, trow, nullptr, c, st, k0, rt, chunk, s_tot);
+        for (int k = 0; k < G; ++k) {
+            load_draw_slice<BF16, VEC, false>(x, k, trow, nullptr, rt);
+            const double Sk = slice_total<BF16, false>(rt, own_draft, c, st, k0, chunk);
+            if (threadIdx.x == 0) s_tot[k] = Sk;
+        }
+        held = G - 1;
+        __syncthreads();
+        S = 0.0;
+        for (int k = 0; k < G; ++k) S += s_tot[k];
     }
-    if (g == 0 && threadIdx.x == 0) {
-        n_accepted[b] = n;
-        if (!(S > 0.0)) next_token[b] = -1;
+    if (!(S > 0.0)) {
+        if (threadIdx.x == 0) next_token[b] = -1;
+        return;
     }
-    if (!(S > 0.0)) return;
 
     // 3. the slice holding u * S: the first with positive total whose running
     // sum exceeds it; if rounding leaves none, the last with positive total.
-    // That slice locates the id in its copies.
     const double thr = (double)uniforms[(int64_t)b * (K + 1) + kb] * S;
     int ks = -1, klast = -1;
     double pre = 0.0, pre_ks = 0.0;
@@ -1280,10 +1310,18 @@ __global__ __launch_bounds__(kSliceThreads) void accept_logits_sliced_kernel(
     }
     const double thr_local = ks < 0 ? INFINITY : thr - pre_ks;
     if (ks < 0) ks = klast;
-    if (g != ks) return;
+    if (ks != held) {  // that slice's data and chunk sums, again (the same values as its own workgroup's)
+        if (bonus) {
+            load_draw_slice<BF16, VEC, false>(x, ks, trow, nullptr, rt);
+            slice_total<BF16, false>(rt, own_draft, c, st, k0, chunk);
+        } else {
+            load_draw_slice<BF16, VEC, true>(x, ks, trow, drow, rt);
+            slice_total<BF16, true>(rt, own_draft, c, st, k0, chunk);
+        }
+    }
     const int xi = bonus ? locate_in_slice<BF16, false>(x, rt, c, st, k0, chunk, thr_local)
                          : locate_in_slice<BF16, true>(x, rt, c, st, k0, chunk, thr_local);
-    if (xi != -2 && (threadIdx.x & (kWave - 1)) == 0) next_token[b] = xi < 0 ? -1 : (int)((int64_t)g * Ls + xi);
+    if (xi != -2 && (threadIdx.x & (kWave - 1)) == 0) next_token[b] = xi < 0 ? -1 : (int)((int64_t)ks * Ls + xi);
 }
 
 __global__ void fill_empty(unsigned long long* __restrict__ p, int64_t n) {
