@@ -205,13 +205,16 @@ def test_accept_logits_k0_identical_rows_and_bonus(sv):
     assert (n == K).all()
 
 
-def test_accept_logits_zero_residual_row(sv):
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 777), (torch.float32, 20000), (torch.bfloat16, 40000)])
+def test_accept_logits_zero_residual_row(sv, dtype, V):
     """Target and draft identical at the rejected position: the residual is zero
     everywhere, so the correction falls back to the target row (the oracle does
-    the same and flags it)."""
+    the same and flags it). V = 777 takes the one-workgroup kernel; the larger
+    rows are split over 4 slices, where the last slice to arrive recomputes every
+    slice's total itself."""
     g = torch.Generator().manual_seed(13)
-    B, K, V = 8, 2, 777
-    zt = torch.randn(B, K + 1, V, generator=g)
+    B, K = 8, 2
+    zt = torch.randn(B, K + 1, V, generator=g).to(dtype)
     zd = zt[:, :K].clone()
     tok = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
     tok[:, 0] = V + 1  # rows identical, but an out-of-range token forces rejection at position 0
