@@ -205,15 +205,17 @@ def test_accept_logits_k0_identical_rows_and_bonus(sv):
     assert (n == K).all()
 
 
-@pytest.mark.parametrize("dtype,V", [(torch.float32, 777), (torch.float32, 20000), (torch.bfloat16, 40000)])
-def test_accept_logits_zero_residual_row(sv, dtype, V):
+@pytest.mark.parametrize("dtype,V,B", [(torch.float32, 777, 8), (torch.float32, 20000, 8), (torch.bfloat16, 40000, 8),
+                                       (torch.float32, 20000, 1024)])
+def test_accept_logits_zero_residual_row(sv, dtype, V, B):
     """Target and draft identical at the rejected position: the residual is zero
     everywhere, so the correction falls back to the target row (the oracle does
     the same and flags it). V = 777 takes the one-workgroup kernel; the larger
-    rows are split over 4 slices, where the last slice to arrive recomputes every
-    slice's total itself."""
+    rows are split over 4 slices, whose draw recomputes every slice's total. At
+    B = 1024 the launch is 4096 workgroups deep, which on a 256-CU device makes
+    the last slice to arrive locate the id."""
     g = torch.Generator().manual_seed(13)
-    B, K = 8, 2
+    K = 2
     zt = torch.randn(B, K + 1, V, generator=g).to(dtype)
     zd = zt[:, :K].clone()
     tok = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
@@ -233,11 +235,14 @@ def test_accept_logits_bitwise_determinism(sv):
         assert (r1[0] == r2[0]).all() and (r1[1] == r2[1]).all()
 
 
+@pytest.mark.parametrize("B", [96, 200])
 @pytest.mark.parametrize("name", ["logits-bf16-b512-k16-v256000-zipf", "logits-f32-b1024-ragged7-v152064"])
-def test_accept_logits_sliced_fallback_is_bitwise_identical(sv, name):
+def test_accept_logits_sliced_fallback_is_bitwise_identical(sv, name, B):
     """With the bounded wait forced to give up at once, every slice recomputes the
-    others' partial statistics and totals itself; the results must not change."""
-    b = synth.generate(name, "cuda", B=96)
+    others' partial statistics and totals itself; the results must not change.
+    B = 200 makes the launch deep enough (over 4096 workgroups) for the last slice
+    to arrive to locate the drawn id; B = 96 has the slice holding it locate it."""
+    b = synth.generate(name, "cuda", B=B)
     r1 = run(sv, b.target, b.draft, b.tokens, b.uniforms, b.lens, b.temperature)
     try:
         sv.sv_set_wait_limit(0)
