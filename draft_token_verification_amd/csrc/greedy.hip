@@ -9,10 +9,10 @@
 // owns one sequence and walks its rows in order, so the early exit at the
 // first miss is a plain loop exit: rows after the miss are never fetched and
 // no workgroup waits on another. With a workspace (greedy_sliced_kernel
-// below) the rows of a sequence are split over up to 8 workgroups that
-// exchange their partial argmaxes at every position, so a long chain of
-// matches is read by several compute units. Each row (or slice) is one
-// streaming argmax:
+// below) the rows of a sequence are split over up to 64 workgroups of 32 KB
+// slices that exchange their partial argmaxes at every position, so a long
+// chain of matches is read by several compute units. Each row (or slice) is
+// one streaming argmax:
 //   - 16-byte coalesced non-temporal loads (8 bf16 or 4 fp32 per load),
 //     UNROLL loads in flight per lane;
 //   - per lane, a strict '>' keeps the first of equal maxima (each lane sees
