@@ -14,6 +14,7 @@ raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -163,6 +164,14 @@ def _dtype_code(t: torch.Tensor, what: str) -> int:
     raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}")
 
 
+def _on(device):
+    """The device guard of a call: entered only when `device` is not already the
+    current device (switching costs a few microseconds per call)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -263,7 +272,7 @@ def sv_softmax_warp(logits: torch.Tensor, temperature: float = 1.0, draft_lens: 
     if lens is not None and tuple(lens.shape) != (B,):
         raise ValueError("draft_lens must be [B]")
     probs = _out((B, R, V), dev, out, torch.float32, "out")
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         if workspace is None:
             workspace = _workspace(sv_softmax_warp_workspace_bytes(B, R, V) if B > 0 else 0, dev, stream.value)
@@ -295,7 +304,7 @@ def sv_softmax_warp_noalloc(logits: torch.Tensor, temperature: float, draft_lens
         if draft_lens.dtype != torch.int32 or tuple(draft_lens.shape) != (B,) or draft_lens.device != dev:
             raise ValueError("draft_lens must be int32 [B] on the logits' device")
     probs = _out((B, R, V), dev, out, torch.float32, "out")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _lib.sv_softmax_warp_noalloc(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(draft_lens),
                                           int(extra_rows), float(temperature), _ptr(probs), _stream(dev))
     _check("sv_softmax_warp_noalloc", st)
@@ -324,7 +333,7 @@ def sv_verify_greedy_margin(target: torch.Tensor, draft_tokens: Optional[torch.T
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
     mg = _out((B,), dev, None if out is None else out[2], torch.float32, "top2_margin")
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
                                       stream.value, "target", "zero")
@@ -361,7 +370,7 @@ def sv_gate_update(hits: torch.Tensor, trials: torch.Tensor, K: int, draft_lens:
         raise ValueError("n_accepted and draft_lens must be [B]")
     if bk is not None and tuple(bk.shape) != (B, K):
         raise ValueError(f"buckets must be [B, K] = {(B, K)}")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _lib.sv_gate_update(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(lens), _ptr(na), _ptr(bk),
                                  float(decay), _stream(dev))
     _check("sv_gate_update", st)
@@ -388,7 +397,7 @@ def sv_gate_choose(hits: torch.Tensor, trials: torch.Tensor, K: int, buckets: Op
     nl = _out((B,), dev, out, torch.int32, "out")
     gp = GateParams(P["draft_ms"], P["verify_base_ms"], P["verify_slope_ms"], P["plain_ms"], P["margin"],
                     int(P["min_draft"]), P["margin_threshold"])
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _lib.sv_gate_choose(_ptr(hits), _ptr(trials), B, NB, int(K), _ptr(bk), _ptr(top2_margin),
                                  ctypes.byref(gp), _ptr(nl), _stream(dev))
     _check("sv_gate_choose", st)
@@ -471,7 +480,7 @@ def sv_apply_penalties(logits: torch.Tensor, draft_lens: Optional[torch.Tensor] 
     pen = Penalties(None if sq is None else sq.data_ptr(), None if sl is None else sl.data_ptr(),
                     0 if sq is None else sq.shape[1], None if tk is None else tk.data_ptr(),
                     0 if tk is None else tk.shape[1], *[None if t is None else t.data_ptr() for t in params])
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = sv_apply_penalties_workspace_bytes(B, sq.shape[1]) if (sq is not None and B > 0) else 0
         ws, ws_bytes = _workspace_arg(workspace, need, dev, stream.value, "logits", "penalty")
@@ -500,7 +509,7 @@ def sv_softmax_warp_filtered(logits: torch.Tensor, temperature: float = 1.0, dra
     tk = _per_sequence(top_k, B, torch.int32, dev, "top_k")
     tp = _per_sequence(top_p, B, torch.float32, dev, "top_p")
     probs = _out((B, R, V), dev, out, torch.float32, "out")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _lib.sv_softmax_warp_filtered(_ptr(logits), _dtype_code(logits, "logits"), B, R, V, _ptr(lens),
                                            int(extra_rows), float(temperature), _ptr(tk), _ptr(tp), _ptr(probs),
                                            _stream(dev))
@@ -533,7 +542,7 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: Optional[torch.Tensor],
         raise ValueError("draft_lens must be [B]")
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         ws, ws_bytes = _workspace_arg(workspace, sv_verify_greedy_workspace_bytes(B, K, V) if B > 0 else 0, dev,
                                       stream.value, "target", "zero")
@@ -572,7 +581,7 @@ def sv_accept(target_probs: torch.Tensor, draft_probs: Optional[torch.Tensor], d
         raise ValueError("draft_lens must be [B]")
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _lib.sv_accept(_ptr(target_probs), _ptr(draft_probs if K > 0 else None), B, K, V, _ptr(toks), _ptr(lens),
                             _ptr(uniforms), _ptr(n), _ptr(nx), _stream(dev))
     _check("sv_accept", st)
@@ -628,7 +637,7 @@ def sv_accept_logits(target_logits: torch.Tensor, draft_logits: Optional[torch.T
             raise ValueError(f"draft_lse must be fp32 {(B, K)} on {dev}")
     n = _out((B,), dev, None if out is None else out[0], torch.int32, "n_accepted")
     nx = _out((B,), dev, None if out is None else out[1], torch.int32, "next_token")
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         if workspace is None:
             need = _lib.sv_accept_logits_workspace_bytes(B, K, V) if B > 0 else 0
